@@ -1,0 +1,359 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test checks the oracle against one of: a library routine that reduces to the same
+definition (stable sort, dense float64 matmul), a closed form, an invariant of the
+method, hand-built edge cases, or an error bound of the quantization. Small shapes with
+d != f, several blocks and a ragged token count are used throughout.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+from oracle import oracle as O
+from quantized_routed_expert_router_amd import synth
+
+from refmath import bf16_to_f64, dequant, dequant_act, unpack_codes
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _layer(E, d, f, bits, seed=3, layer=0):
+    g = synth.fill_matrix_host(synth.empty_matrix(E, f, d, bits), seed, layer, synth.T_GATE)
+    u = synth.fill_matrix_host(synth.empty_matrix(E, f, d, bits), seed, layer, synth.T_UP)
+    dn = synth.fill_matrix_host(synth.empty_matrix(E, d, f, bits), seed, layer, synth.T_DOWN)
+    return g, u, dn
+
+
+def _M(h):
+    return O.Matrix(h.codes, h.scale_min, h.rows, h.cols, h.bits)
+
+
+# ------------------------------------------------------------------ route
+
+def test_route_matches_stable_sort():
+    rng = np.random.default_rng(1)
+    for n, E, k in [(7, 8, 2), (5, 64, 10), (3, 512, 10), (2, 9, 9), (4, 33, 1)]:
+        lg = rng.standard_normal((n, E)).astype(np.float32)
+        ids, w = O.route(lg, k)
+        ref = np.argsort(-lg, axis=1, kind="stable")[:, :k]
+        assert np.array_equal(ids, ref)
+        # weights: softmax over all E experts, then renormalised over the selected k
+        p = np.exp(lg.astype(np.float64) - lg.max(axis=1, keepdims=True))
+        p /= p.sum(axis=1, keepdims=True)
+        sel = np.take_along_axis(p, ref, axis=1)
+        ref_w = sel / sel.sum(axis=1, keepdims=True)
+        np.testing.assert_allclose(w, ref_w, rtol=2e-7, atol=0)
+        assert np.all(np.abs(w.astype(np.float64).sum(axis=1) - 1.0) <= k * 2.0 ** -24)
+        assert np.all(np.diff(w, axis=1) <= 0)  # slot 0 the largest
+
+
+def test_route_ties_and_signed_zero():
+    with open(os.path.join(GOLDEN, "route_ties.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        lg = np.array(c["logits"], np.float32)[None, :]
+        ids, w = O.route(lg, c["k"])
+        assert ids[0].tolist() == c["ids"], c["name"]
+        np.testing.assert_allclose(w[0], c["w"], rtol=1e-7, atol=0)
+
+
+def test_route_k1_and_k_equals_E():
+    rng = np.random.default_rng(2)
+    lg = rng.standard_normal((6, 16)).astype(np.float32)
+    ids, w = O.route(lg, 1)
+    assert np.array_equal(ids[:, 0], np.argmax(lg, axis=1))
+    assert np.all(w == 1.0)
+    ids, w = O.route(lg, 16)
+    assert np.array_equal(np.sort(ids, axis=1), np.tile(np.arange(16), (6, 1)))
+    with pytest.raises(ValueError):
+        O.route(lg, 17)
+
+
+# ------------------------------------------------------------------ group
+
+def test_group_is_stable_counting_sort():
+    rng = np.random.default_rng(4)
+    for n, k, E in [(5, 3, 7), (64, 10, 512), (1, 2, 8), (0, 2, 8)]:
+        ids = np.array([rng.permutation(E)[:k] for _ in range(n)], np.int32).reshape(n, k)
+        off, pidx = O.group(ids, E)
+        flat = ids.ravel()
+        assert np.array_equal(pidx, np.argsort(flat, kind="stable"))
+        assert np.array_equal(off, np.concatenate([[0], np.cumsum(np.bincount(flat, minlength=E))]))
+
+
+# ------------------------------------------------------------------ int8 activation quantization
+
+def test_quant_hand_cases():
+    with open(os.path.join(GOLDEN, "quant_cases.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        x = np.array(c["x"], np.float32)
+        q, s = O.quant_act(x)
+        assert q.tolist() == c["q"], c["name"]
+        assert float(s[0]) == np.float32(c["scale"]), c["name"]
+
+
+def test_quant_properties():
+    rng = np.random.default_rng(5)
+    x = (rng.standard_normal((50, 256)) * rng.uniform(0.01, 100, (50, 1))).astype(np.float32)
+    x[3, 32:64] = 0.0  # an all-zero block
+    q, s = O.quant_act(x)
+    assert q.dtype == np.int8 and np.all(np.abs(q.astype(int)) <= 127)
+    xb = x.reshape(50, 8, 32).astype(np.float64)
+    qb = q.reshape(50, 8, 32).astype(np.float64)
+    sb = s.astype(np.float64)[..., None]
+    nz = sb[..., 0] > 0
+    # the largest magnitude of every non-zero block maps to +-127
+    assert np.all(np.abs(qb).max(axis=2)[nz] == 127)
+    assert np.all((s == 0) == (np.abs(xb).max(axis=2) == 0))
+    # scale*127 is amax up to fp32 rounding of the division
+    np.testing.assert_allclose(sb[..., 0][nz] * 127, np.abs(xb).max(axis=2)[nz], rtol=2 ** -23)
+    # round to nearest: every code is within half a step of x/scale
+    err = np.abs(np.where(sb > 0, xb / np.where(sb > 0, sb, 1), 0) - qb)
+    assert err.max() <= 0.5 + 1e-5
+    # odd symmetry and exact power-of-two scale invariance
+    q2, s2 = O.quant_act(-x)
+    assert np.array_equal(q2, -q) and np.array_equal(s2, s)
+    q3, s3 = O.quant_act(x * np.float32(8.0))
+    assert np.array_equal(q3, q) and np.array_equal(s3, s * 8)
+
+
+# ------------------------------------------------------------------ fp16 decode and bf16 weights
+
+def test_weight_decode_all_fp16_mins():
+    # one expert whose every block has code 0 and a distinct fp16 min: w = min exactly
+    rows = 2048
+    sm = np.zeros((1, 1, rows, 2), np.uint16)
+    pats = np.arange(0, 65536, 32, dtype=np.uint16)[:rows]
+    sm[0, 0, :, 1] = pats
+    M = O.Matrix(np.zeros((1, 1, rows, 4), np.uint32), sm, rows, 32, 4)
+    ref = pats.view(np.float16).astype(np.float64)
+    for r in range(rows):
+        got = O.weight(M, 0, r, 5)
+        if np.isnan(ref[r]):
+            assert np.isnan(got)
+        else:
+            assert got == ref[r]
+
+
+def test_bf16_weight_rounding_hand_cases():
+    # scale 2^-8, min 1.0: w = 1 + q/256; bf16 has 7 fraction bits (step 2^-7 at 1.0)
+    sm = np.zeros((1, 1, 1, 2), np.uint16)
+    sm[0, 0, 0, 0] = np.array([2.0 ** -8], np.float16).view(np.uint16)[0]
+    sm[0, 0, 0, 1] = np.array([1.0], np.float16).view(np.uint16)[0]
+    codes = np.zeros((1, 1, 1, 4), np.uint32)
+    # q = 1 -> 1+2^-8 (tie, to even -> 1.0); q = 3 -> 1+3*2^-8 (tie, to even -> 1+2^-6)
+    # q = 2 -> exact 1+2^-7
+    codes[0, 0, 0, 0] = 1 | (3 << 4) | (2 << 8)
+    M = O.Matrix(codes, sm, 1, 32, 4)
+    got = [bf16_to_f64(np.array([O.weight_bf16(M, 0, 0, c)]))[0] for c in range(3)]
+    assert got == [1.0, 1.0 + 2.0 ** -6, 1.0 + 2.0 ** -7]
+
+
+# ------------------------------------------------------------------ decode layer vs dense fp64
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_decode_layer_vs_dense_bruteforce(bits):
+    E, d, f, k, n = 6, 128, 96, 3, 5
+    g, u, dn = _layer(E, d, f, bits)
+    rng = np.random.default_rng(6)
+    lg = rng.standard_normal((n, E)).astype(np.float32)
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    res = rng.standard_normal((n, d)).astype(np.float32)
+    ids, w = O.route(lg, k)
+    out, tr = O.ffn_decode(_M(g), _M(u), _M(dn), E, x, ids, w, res, trace=True)
+
+    Wg, Wu, Wd = (dequant(m.codes, m.scale_min, bits) for m in (g, u, dn))
+    Qg, Qu, Qd = (unpack_codes(m.codes, bits) for m in (g, u, dn))
+    # x codes are a valid quantization of x (pinned separately), use them as given
+    xa = dequant_act(tr["xq"], tr["xs"])
+    np.testing.assert_array_equal(tr["xq"], O.quant_act(x)[0])
+    for p in range(n * k):
+        t, j = divmod(p, k)
+        e = ids[t, j]
+        # exact integer block dots, brute force in int64
+        xb = tr["xq"][t].astype(np.int64).reshape(d // 32, 32)
+        ref_gd = np.einsum("rbi,bi->rb", Qg[e].reshape(f, d // 32, 32), xb)
+        ref_ud = np.einsum("rbi,bi->rb", Qu[e].reshape(f, d // 32, 32), xb)
+        assert np.array_equal(tr["gate_dots"][p], ref_gd)
+        assert np.array_equal(tr["up_dots"][p], ref_ud)
+        # gate/up rows: dense fp64 product of dequantized weight and dequantized x
+        np.testing.assert_allclose(tr["g"][p], Wg[e] @ xa[t], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(tr["u"][p], Wu[e] @ xa[t], rtol=1e-12, atol=1e-12)
+        # SwiGLU: silu(g) * u, silu(z) = z * logistic(z)
+        h_ref = (tr["g"][p] * expit(tr["g"][p]) * tr["u"][p]).astype(np.float32)
+        np.testing.assert_array_max_ulp(tr["h"][p], h_ref, maxulp=1)
+        hq, hs = O.quant_act(tr["h"][p])
+        assert np.array_equal(tr["hq"][p], hq) and np.array_equal(tr["hs"][p], hs)
+        hb = tr["hq"][p].astype(np.int64).reshape(f // 32, 32)
+        ref_dd = np.einsum("rbi,bi->rb", Qd[e].reshape(d, f // 32, 32), hb)
+        assert np.array_equal(tr["down_dots"][p], ref_dd)
+        ha = dequant_act(tr["hq"][p], tr["hs"][p])
+        np.testing.assert_allclose(tr["y"][p], Wd[e] @ ha, rtol=1e-12, atol=1e-12)
+    # combine: residual + routing-weighted sum over the k slots
+    y = tr["y"].reshape(n, k, d)
+    ref_out = (res.astype(np.float64) + np.einsum("tj,tjc->tc", w.astype(np.float64), y))
+    np.testing.assert_array_max_ulp(out, ref_out.astype(np.float32), maxulp=1)
+
+
+def test_int8_error_bound_against_unquantized_x():
+    # |W.x - W.(xs*xq)| <= sum_c |w_c| * xs_b(c) / 2 (round-to-nearest bound per element)
+    E, d, f, k, n = 4, 256, 64, 2, 3
+    g, u, dn = _layer(E, d, f, 4, seed=9)
+    rng = np.random.default_rng(7)
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    ids, w = O.route(rng.standard_normal((n, E)).astype(np.float32), k)
+    _, tr = O.ffn_decode(_M(g), _M(u), _M(dn), E, x, ids, w, x, trace=True)
+    Wg = dequant(g.codes, g.scale_min, 4)
+    for p in range(n * k):
+        t, j = divmod(p, k)
+        e = ids[t, j]
+        exact = Wg[e] @ x[t].astype(np.float64)
+        bound = np.abs(Wg[e]) @ np.repeat(tr["xs"][t].astype(np.float64), 32) / 2 * (1 + 1e-6)
+        assert np.all(np.abs(tr["g"][p] - exact) <= bound + 1e-12)
+        # and the quantized product is not trivially zero
+        assert np.abs(tr["g"][p]).max() > 0.1 * np.abs(exact).max()
+
+
+def test_closed_form_constant_codes_and_activations():
+    # every code c and every activation a = 127*2^-7: xq = 127, xs = 2^-7 exactly, so
+    # g_r = sum_b (s_b*c + m_b) * 2^-7 * 32*127
+    E, d, f, k = 2, 96, 64, 1
+    c = 11
+    word = 0
+    for i in range(8):
+        word |= c << (4 * i)
+    g = synth.fill_matrix_host(synth.empty_matrix(E, f, d, 4), 1, 0, synth.T_GATE)
+    u = synth.fill_matrix_host(synth.empty_matrix(E, f, d, 4), 1, 0, synth.T_UP)
+    dn = synth.fill_matrix_host(synth.empty_matrix(E, d, f, 4), 1, 0, synth.T_DOWN)
+    g.codes[:] = word
+    x = np.full((1, d), 127 * 2.0 ** -7, np.float32)
+    ids = np.array([[1]], np.int32)
+    w = np.ones((1, 1), np.float32)
+    _, tr = O.ffn_decode(_M(g), _M(u), _M(dn), E, x, ids, w, x, trace=True)
+    s = g.scale_min[1, :, :, 0].view(np.float16).astype(np.float64)  # [nb][rows]
+    m = g.scale_min[1, :, :, 1].view(np.float16).astype(np.float64)
+    closed = ((s * c + m) * 2.0 ** -7 * 32 * 127).sum(axis=0)
+    assert np.array_equal(tr["g"][0], closed)
+    assert np.all(tr["xs"] == 2.0 ** -7) and np.all(tr["xq"] == 127)
+
+
+# ------------------------------------------------------------------ invariants
+
+def test_zero_expert_contributes_exactly_zero():
+    E, d, f, k, n = 5, 64, 64, 3, 4
+    g, u, dn = _layer(E, d, f, 4, seed=11)
+    rng = np.random.default_rng(8)
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    res = rng.standard_normal((n, d)).astype(np.float32)
+    ids, w = O.route(rng.standard_normal((n, E)).astype(np.float32), k)
+    z = int(ids[0, 1])
+    for m in (g, u, dn):
+        m.codes[z] = 0
+        m.scale_min[z] = 0
+    out_zero, tr = O.ffn_decode(_M(g), _M(u), _M(dn), E, x, ids, w, res, trace=True)
+    assert np.all(tr["y"][(ids.ravel() == z)] == 0)
+    w_omit = np.where(ids == z, np.float32(0), w)
+    out_omit, _ = O.ffn_decode(_M(g), _M(u), _M(dn), E, x, ids, w_omit, res)
+    assert np.array_equal(out_zero, out_omit)
+
+
+def test_zero_input_returns_residual():
+    E, d, f, k, n = 4, 64, 32, 2, 3
+    g, u, dn = _layer(E, d, f, 2, seed=12)
+    rng = np.random.default_rng(9)
+    res = rng.standard_normal((n, d)).astype(np.float32)
+    ids, w = O.route(rng.standard_normal((n, E)).astype(np.float32), k)
+    out, _ = O.ffn_decode(_M(g), _M(u), _M(dn), E, np.zeros((n, d), np.float32), ids, w, res)
+    assert np.array_equal(out, res)
+
+
+def test_expert_permutation_changes_nothing():
+    E, d, f, k, n = 7, 64, 64, 3, 5
+    g, u, dn = _layer(E, d, f, 4, seed=13)
+    rng = np.random.default_rng(10)
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    lg = rng.standard_normal((n, E)).astype(np.float32)
+    ids, w = O.route(lg, k)
+    out, _ = O.ffn_decode(_M(g), _M(u), _M(dn), E, x, ids, w, x)
+    pi = rng.permutation(E)  # expert e moves to slot pi[e]
+    inv = np.argsort(pi)
+    lg2 = lg[:, inv]
+    g2, u2, dn2 = (synth.HostMatrix(m.codes[inv].copy(), m.scale_min[inv].copy(), m.rows, m.cols,
+                                    m.bits) for m in (g, u, dn))
+    ids2, w2 = O.route(lg2, k)
+    assert np.array_equal(ids2, pi[ids]) and np.array_equal(w2, w)
+    out2, _ = O.ffn_decode(_M(g2), _M(u2), _M(dn2), E, x, ids2, w2, x)
+    assert np.array_equal(out, out2)
+
+
+def test_token_subset_matches_full_run():
+    E, d, f, k, n = 6, 64, 32, 2, 7
+    g, u, dn = _layer(E, d, f, 4, seed=14)
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    ids, w = O.route(rng.standard_normal((n, E)).astype(np.float32), k)
+    full, _ = O.ffn_decode(_M(g), _M(u), _M(dn), E, x, ids, w, x)
+    sub, _ = O.ffn_decode(_M(g), _M(u), _M(dn), E, x, ids, w, x, tokens=np.array([6, 0, 3]))
+    assert np.array_equal(sub, full[[6, 0, 3]])
+    one, _ = O.ffn_decode(_M(g), _M(u), _M(dn), E, x, ids, w, x, nthreads=1)
+    assert np.array_equal(one, full)  # thread count does not change results
+
+
+# ------------------------------------------------------------------ prefill layer vs dense fp64
+
+def test_prefill_layer_vs_dense_bruteforce():
+    E, d, f, k, n = 5, 96, 64, 2, 6
+    g, u, dn = _layer(E, d, f, 4, seed=15)
+    rng = np.random.default_rng(12)
+    xb = synth.to_bf16_bits(rng.standard_normal((n, d)).astype(np.float32))
+    res = rng.standard_normal((n, d)).astype(np.float32)
+    ids, w = O.route(rng.standard_normal((n, E)).astype(np.float32), k)
+    out, tr = O.ffn_prefill(_M(g), _M(u), _M(dn), E, xb, ids, w, res, trace=True)
+
+    def wbf(m):  # bf16 of fp32(scale*q + min), through the oracle's per-weight accessor
+        M = _M(m)
+        return np.array([[[O.weight_bf16(M, e, r, c) for c in range(m.cols)]
+                          for r in range(m.rows)] for e in range(E)], np.uint16)
+
+    Wg, Wu, Wd = (bf16_to_f64(wbf(m)) for m in (g, u, dn))
+    # the bf16 weights are within one bf16 rounding of the exact dequantized weights
+    np.testing.assert_allclose(Wg, dequant(g.codes, g.scale_min, 4), rtol=2 ** -8, atol=1e-30)
+    xf = bf16_to_f64(xb)
+    for p in range(n * k):
+        t, j = divmod(p, k)
+        e = ids[t, j]
+        np.testing.assert_allclose(tr["g"][p], Wg[e] @ xf[t], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(tr["u"][p], Wu[e] @ xf[t], rtol=1e-12, atol=1e-12)
+        hf = bf16_to_f64(tr["hb"][p])
+        h_exact = tr["g"][p] * expit(tr["g"][p]) * tr["u"][p]
+        assert np.all(np.abs(hf - h_exact) <= np.abs(h_exact) * 2 ** -8 * 1.0001)
+        np.testing.assert_allclose(tr["y"][p], Wd[e] @ hf, rtol=1e-12, atol=1e-12)
+    y = tr["y"].reshape(n, k, d)
+    ref_out = res.astype(np.float64) + np.einsum("tj,tjc->tc", w.astype(np.float64), y)
+    np.testing.assert_array_max_ulp(out, ref_out.astype(np.float32), maxulp=1)
+
+
+# ------------------------------------------------------------------ byte accounting
+
+def test_expert_byte_formula_against_pages():
+    with open(os.path.join(GOLDEN, "byte_accounting.json")) as fh:
+        gold = json.load(fh)
+    # the pages' own identity: bytes per token = experts per token x bytes per expert
+    per_expert = gold["slot_bytes_mib"] * 2 ** 20 / gold["slots"]
+    assert abs(gold["experts_per_token"] * per_expert / 1e6 - gold["mb_per_token"]) < 0.5
+    assert gold["layers"] * gold["experts_per_layer"] == gold["experts_total"]
+    # our formula: 3 matrices * f*d weights * (bits + 1 bit of fp16 scale+min per weight)/8
+    assert synth.expert_bytes(2048, 768, 4) == 2_949_120
+    assert synth.expert_bytes(2048, 768, 2) == 1_769_472
+    E, d, f = 3, 64, 32
+    for bits in (2, 4):
+        m = [synth.empty_matrix(E, f, d, bits), synth.empty_matrix(E, f, d, bits),
+             synth.empty_matrix(E, d, f, bits)]
+        nbytes = sum(x.codes.nbytes + x.scale_min.nbytes for x in m)
+        assert nbytes == E * synth.expert_bytes(d, f, bits)
