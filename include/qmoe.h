@@ -1,0 +1,175 @@
+/*
+ * qmoe.h - C ABI of the routed-expert MoE FFN library for AMD MI355X (gfx950).
+ *
+ * The library computes one routed mixture-of-experts FFN layer of a top-k MoE decoder
+ * whose experts are stored as block-quantized low-bit weights:
+ *
+ *   moe_route              router top-k over expert logits, routing weights over the k
+ *                          selected experts, and the token-expert pairs grouped by
+ *                          expert. (Strata engine explainer, m.lqnn.cn/news/264700,
+ *                          sections "Architecture overview" - the router picks the 10
+ *                          active experts of 512 per token - and "Doorbell handshake" -
+ *                          expert ids travel together with routing weights; grouping
+ *                          by expert as in section "Expert cache", where cached experts
+ *                          run in a grouped kernel over the verify window.)
+ *   moe_expert_ffn_decode  the expert FFN for a small verify window (T <= 5 tokens per
+ *                          sequence, "Speculative decoding" section: 3 drafted tokens,
+ *                          up to 5 copied by prompt lookup): int8 block quantization of
+ *                          the activations, dequantized low-bit gate/up weights through
+ *                          exact per-block int8 dot products ("CPU expert pool" section:
+ *                          int8 dot products, activation quantized once and reused over
+ *                          many weight rows), SwiGLU, int8 quantization of the hidden
+ *                          vector, the down projection, and the routing-weighted combine
+ *                          written into the residual ("Doorbell handshake": combine,
+ *                          then residual write-back).
+ *   moe_expert_ffn_prefill the same layer for a prefill chunk of up to 8192 tokens
+ *                          ("Architecture overview": prompts are cut into chunks of at
+ *                          most 8192 tokens) with bf16 dequantized weights, bf16
+ *                          activations and fp32 accumulation on the matrix cores.
+ *
+ * Conventions for every entry point:
+ *   * Pointers named device are GPU memory of the current HIP device; the caller owns
+ *     all memory, including the workspace. The library allocates nothing.
+ *   * `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on it and the
+ *     call returns without waiting. Calls on one stream are ordered; calls that share
+ *     output or workspace buffers must not run concurrently on different streams.
+ *   * Arguments are validated before anything is enqueued; on any error nothing is
+ *     enqueued. MOE_ERR_HIP means a launch failed; faults during execution surface at
+ *     the caller's next synchronization with the stream.
+ *   * n_tokens == 0 is valid: the FFN entry points then enqueue nothing, and moe_route
+ *     only writes expert_offsets (all zero; the other routing pointers may be NULL).
+ *
+ * Packed weight layout (one moe_qmatrix holds all E experts of one projection):
+ *   codes      uint32 [E][cols/32][rows][bits]   32 unsigned codes of `bits` bits per
+ *              block of 32 consecutive columns; code i (0..31) of a block sits in word
+ *              i/(32/bits) at bit offset bits*(i % (32/bits)).
+ *   scale_min  uint16 [E][cols/32][rows][2]      fp16 scale and fp16 min per block.
+ *   weight     w[e][r][c] = scale * code + min    (block b = c/32)
+ *   The block axis is the reduction axis (cols); blocks are stored block-column-major
+ *   so that one block column of consecutive rows is contiguous (16 B per row at 4-bit,
+ *   8 B at 2-bit). codes must be 16-byte aligned, scale_min 4-byte aligned.
+ * Projections: gate and up are [rows = d_ff][cols = d_model], down is
+ *   [rows = d_model][cols = d_ff]; bits is 4 or 2, the same for all three.
+ */
+#ifndef QMOE_H
+#define QMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARGUMENT = 1,
+  MOE_ERR_UNSUPPORTED = 2,
+  MOE_ERR_WORKSPACE_TOO_SMALL = 3,
+  MOE_ERR_HIP = 4
+} moe_status;
+
+/* Limits checked by every entry point. */
+#define MOE_MAX_EXPERTS 1024       /* n_experts                                  */
+#define MOE_MAX_TOP_K 64           /* top_k                                      */
+#define MOE_MAX_DECODE_TOKENS 512  /* n_tokens of moe_expert_ffn_decode          */
+#define MOE_MAX_PREFILL_TOKENS 8192 /* n_tokens of moe_expert_ffn_prefill         */
+#define MOE_MAX_ROUTE_TOKENS 65536 /* n_tokens of moe_route                      */
+
+typedef struct {
+  const uint32_t* codes;     /* device, [E][cols/32][rows][bits]                    */
+  const uint16_t* scale_min; /* device, [E][cols/32][rows][2] fp16 (scale, min)      */
+  int32_t rows, cols, bits;
+} moe_qmatrix;
+
+typedef struct {
+  int32_t d_model;   /* d: multiple of 32, at most 8192                            */
+  int32_t d_ff;      /* f: multiple of 32, at most 8192                            */
+  int32_t n_experts; /* E: 1..MOE_MAX_EXPERTS                                      */
+  int32_t top_k;     /* k: 1..min(E, MOE_MAX_TOP_K)                                */
+  moe_qmatrix gate, up, down;
+} moe_layer;
+
+/* Routing record of n tokens (all device memory), written by moe_route and read by the
+ * FFN entry points:
+ *   topk_ids        int32 [n][k]  expert of slot j of token t; slot 0 has the largest
+ *                                 logit; equal logits (-0 equals +0) order by lower id
+ *   topk_w          fp32  [n][k]  w_j = exp(l_j - l_0) / sum_i exp(l_i - l_0) over the
+ *                                 k selected (= softmax, then renormalised over the k)
+ *   expert_offsets  int32 [E+1]   pairs of expert e are pair_index[off[e] .. off[e+1])
+ *   pair_index      int32 [n*k]   pair ids p = t*k + j, grouped by expert, ascending p
+ *                                 within an expert (stable counting sort) */
+typedef struct {
+  int32_t* topk_ids;
+  float* topk_w;
+  int32_t* expert_offsets;
+  int32_t* pair_index;
+} moe_routing;
+
+/* Optional intermediate outputs of moe_expert_ffn_decode, for checking (each may be
+ * NULL; passing a non-NULL moe_debug selects a slower instance of the same kernels).
+ * p = t*k + j is the pair id. Layouts:
+ *   xq int8 [n][d], xs fp32 [n][d/32]            activation codes and block scales
+ *   gate_dots, up_dots int32 [n*k][f][d/32]       exact per-block integer dots
+ *   g, u fp32 [n*k][f]                            gate/up projections (rounded to fp32)
+ *   h fp32 [n*k][f]                               SwiGLU output, the value quantized
+ *   hq int8 [n*k][f], hs fp32 [n*k][f/32]         hidden codes and block scales
+ *   down_dots int32 [n*k][d][f/32]                exact per-block integer dots
+ *   y fp32 [n*k][d]                               expert output of each pair */
+typedef struct {
+  int8_t* xq;
+  float* xs;
+  int32_t* gate_dots;
+  int32_t* up_dots;
+  float* g;
+  float* u;
+  float* h;
+  int8_t* hq;
+  float* hs;
+  int32_t* down_dots;
+  float* y;
+} moe_debug;
+
+/* Human-readable name of a status code (static storage). */
+const char* moe_status_string(moe_status s);
+
+/* Bytes of device workspace moe_route needs for these sizes (0 when none). */
+size_t moe_route_workspace_bytes(int n_tokens, int n_experts, int top_k);
+
+/* Router top-k, routing weights and grouping (see moe_routing for the outputs).
+ * logits: device fp32 [n_tokens][n_experts], finite values (NaN/Inf are a caller
+ * error with unspecified selection). Errors: MOE_ERR_INVALID_ARGUMENT for sizes out
+ * of range or NULL outputs; MOE_ERR_WORKSPACE_TOO_SMALL. */
+moe_status moe_route(const float* logits, int n_tokens, int n_experts, int top_k,
+                     const moe_routing* out, void* ws, size_t ws_bytes, void* stream);
+
+/* Bytes of device workspace the FFN entry points need (prefill != 0 for
+ * moe_expert_ffn_prefill). Returns 0 if the layer description is invalid. */
+size_t moe_ffn_workspace_bytes(const moe_layer* L, int n_tokens, int prefill);
+
+/* Decode-window expert FFN. x: device fp32 [n][d], the layer's MoE input; residual:
+ * device fp32 [n][d], updated in place: residual[t] += sum_j w[t][j] * y[t*k+j] (slot
+ * order). x may be the residual buffer itself (all of x is read before residual is
+ * written); any other overlap is rejected. r: routing from moe_route for the same n,
+ * E and k. ws: device workspace of at least moe_ffn_workspace_bytes(L, n, 0) bytes,
+ * 256-byte aligned; its contents need no initialisation. dbg: NULL, or debug outputs.
+ * Limits: n <= MOE_MAX_DECODE_TOKENS. */
+moe_status moe_expert_ffn_decode(const moe_layer* L, const float* x, int n_tokens,
+                                 const moe_routing* r, float* residual, void* ws,
+                                 size_t ws_bytes, const moe_debug* dbg, void* stream);
+
+/* Prefill-chunk expert FFN with bf16 arithmetic on the matrix cores: weights are
+ * dequantized to bf16 (bf16 of fp32 scale*q + min), x_bf16: device bf16 bits [n][d];
+ * gate/up accumulate in fp32; h = bf16(silu(g) * u); down accumulates in fp32;
+ * residual (fp32 [n][d]) += routing-weighted sum. Only 4-bit weights. ws: at least
+ * moe_ffn_workspace_bytes(L, n, 1) bytes, 256-byte aligned.
+ * Limits: n <= MOE_MAX_PREFILL_TOKENS. */
+moe_status moe_expert_ffn_prefill(const moe_layer* L, const uint16_t* x_bf16, int n_tokens,
+                                  const moe_routing* r, float* residual, void* ws,
+                                  size_t ws_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QMOE_H */

@@ -1,0 +1,161 @@
+// C ABI of libqmoe: argument validation, workspace sizing and kernel launches.
+// Every check runs on the host before anything is enqueued.
+#include <algorithm>
+#include <mutex>
+#include <vector>
+
+#include "qmoe_internal.h"
+
+namespace qmoe {
+
+int device_cu_count() {
+  static std::mutex mu;
+  static std::vector<int> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, 0);
+  if (cache[dev] == 0) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0)
+      cus = 256;
+    cache[dev] = cus;
+  }
+  return cache[dev];
+}
+
+namespace {
+
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool overlaps(const void* a, size_t an, const void* b, size_t bn) {
+  const uintptr_t a0 = (uintptr_t)a, b0 = (uintptr_t)b;
+  return a0 < b0 + bn && b0 < a0 + an;
+}
+
+moe_status check_matrix(const moe_qmatrix& m, int rows, int cols, int bits) {
+  if (!m.codes || !m.scale_min) return MOE_ERR_INVALID_ARGUMENT;
+  if (m.rows != rows || m.cols != cols || m.bits != bits) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(m.codes, bits == 4 ? 16 : 8) || !aligned(m.scale_min, 4))
+    return MOE_ERR_INVALID_ARGUMENT;
+  return MOE_OK;
+}
+
+moe_status check_layer(const moe_layer* L) {
+  if (!L) return MOE_ERR_INVALID_ARGUMENT;
+  const int d = L->d_model, f = L->d_ff, E = L->n_experts, k = L->top_k;
+  if (d <= 0 || f <= 0 || d % 32 || f % 32 || d > 8192 || f > 8192) return MOE_ERR_INVALID_ARGUMENT;
+  if (E < 1 || E > MOE_MAX_EXPERTS || k < 1 || k > E || k > MOE_MAX_TOP_K)
+    return MOE_ERR_INVALID_ARGUMENT;
+  const int bits = L->gate.bits;
+  if (bits != 2 && bits != 4) return MOE_ERR_UNSUPPORTED;
+  if (L->up.bits != bits || L->down.bits != bits) return MOE_ERR_UNSUPPORTED;
+  moe_status s = check_matrix(L->gate, f, d, bits);
+  if (s == MOE_OK) s = check_matrix(L->up, f, d, bits);
+  if (s == MOE_OK) s = check_matrix(L->down, d, f, bits);
+  return s;
+}
+
+moe_status check_routing(const moe_routing* r) {
+  if (!r || !r->topk_ids || !r->topk_w || !r->expert_offsets || !r->pair_index)
+    return MOE_ERR_INVALID_ARGUMENT;
+  return MOE_OK;
+}
+
+}  // namespace
+}  // namespace qmoe
+
+using namespace qmoe;
+
+extern "C" {
+
+const char* moe_status_string(moe_status s) {
+  switch (s) {
+    case MOE_OK:
+      return "MOE_OK";
+    case MOE_ERR_INVALID_ARGUMENT:
+      return "MOE_ERR_INVALID_ARGUMENT";
+    case MOE_ERR_UNSUPPORTED:
+      return "MOE_ERR_UNSUPPORTED";
+    case MOE_ERR_WORKSPACE_TOO_SMALL:
+      return "MOE_ERR_WORKSPACE_TOO_SMALL";
+    case MOE_ERR_HIP:
+      return "MOE_ERR_HIP";
+  }
+  return "MOE_ERR_UNKNOWN";
+}
+
+size_t moe_route_workspace_bytes(int n_tokens, int n_experts, int top_k) {
+  (void)n_tokens;
+  (void)n_experts;
+  (void)top_k;
+  return 0;
+}
+
+moe_status moe_route(const float* logits, int n_tokens, int n_experts, int top_k,
+                     const moe_routing* out, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  if (n_tokens < 0 || n_tokens > MOE_MAX_ROUTE_TOKENS) return MOE_ERR_INVALID_ARGUMENT;
+  if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARGUMENT;
+  if (top_k < 1 || top_k > n_experts || top_k > MOE_MAX_TOP_K) return MOE_ERR_INVALID_ARGUMENT;
+  if (!out || !out->expert_offsets) return MOE_ERR_INVALID_ARGUMENT;
+  if (n_tokens > 0 && (check_routing(out) != MOE_OK || !logits)) return MOE_ERR_INVALID_ARGUMENT;
+  const hipError_t err =
+      launch_route(logits, n_tokens, n_experts, top_k, out, (hipStream_t)stream);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+size_t moe_ffn_workspace_bytes(const moe_layer* L, int n_tokens, int prefill) {
+  if (!L || n_tokens < 0) return 0;
+  const int d = L->d_model, f = L->d_ff, k = L->top_k;
+  if (d <= 0 || f <= 0 || k <= 0) return 0;
+  if (prefill) return 0;
+  return decode_ws_layout(n_tokens, k, d, f).total;
+}
+
+moe_status moe_expert_ffn_decode(const moe_layer* L, const float* x, int n_tokens,
+                                 const moe_routing* r, float* residual, void* ws,
+                                 size_t ws_bytes, const moe_debug* dbg, void* stream) {
+  moe_status s = check_layer(L);
+  if (s != MOE_OK) return s;
+  if (n_tokens < 0 || n_tokens > MOE_MAX_DECODE_TOKENS) return MOE_ERR_INVALID_ARGUMENT;
+  if (n_tokens == 0) return MOE_OK;
+  if (check_routing(r) != MOE_OK) return MOE_ERR_INVALID_ARGUMENT;
+  if (!x || !residual || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(residual, 4) || !aligned(ws, 256))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const size_t act_bytes = (size_t)n_tokens * L->d_model * sizeof(float);
+  if (x != residual && overlaps(x, act_bytes, residual, act_bytes))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = moe_ffn_workspace_bytes(L, n_tokens, 0);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (overlaps(ws, need, residual, act_bytes) || overlaps(ws, need, x, act_bytes))
+    return MOE_ERR_INVALID_ARGUMENT;
+  DecodeDebug dd{};
+  if (dbg) {
+    dd = DecodeDebug{dbg->xq, dbg->xs, dbg->gate_dots, dbg->up_dots, dbg->g,
+                     dbg->u,  dbg->h,  dbg->hq,        dbg->hs,      dbg->down_dots, dbg->y};
+  }
+  DecodeArgs a{L, x, n_tokens, r, residual, (char*)ws, dbg ? &dd : nullptr,
+               (hipStream_t)stream, device_cu_count()};
+  const hipError_t err = launch_decode(a);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
+moe_status moe_expert_ffn_prefill(const moe_layer* L, const uint16_t* x_bf16, int n_tokens,
+                                  const moe_routing* r, float* residual, void* ws,
+                                  size_t ws_bytes, void* stream) {
+  (void)L;
+  (void)x_bf16;
+  (void)n_tokens;
+  (void)r;
+  (void)residual;
+  (void)ws;
+  (void)ws_bytes;
+  (void)stream;
+  return MOE_ERR_UNSUPPORTED;
+}
+
+}  // extern "C"

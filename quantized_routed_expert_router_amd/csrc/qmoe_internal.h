@@ -1,0 +1,144 @@
+// Internal declarations shared by the translation units of libqmoe.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <string.h>
+
+#include "qmoe.h"
+
+namespace qmoe {
+
+constexpr int kWave = 64;
+
+// ------------------------------------------------------------------ small device helpers
+
+__device__ __forceinline__ double half_bits_to_double(uint32_t bits16) {
+  const uint16_t b = (uint16_t)bits16;
+  _Float16 h;
+  __builtin_memcpy(&h, &b, 2);
+  return (double)(float)h;
+}
+
+__device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
+  const uint16_t b = (uint16_t)bits16;
+  _Float16 h;
+  __builtin_memcpy(&h, &b, 2);
+  return (float)h;
+}
+
+// Signed 8-bit dot product of 4 byte lanes, accumulated into c (v_dot4c_i32_i8).
+__device__ __forceinline__ int dot4_i8(int a, int b, int c) {
+  return __builtin_amdgcn_sdot4(a, b, c, false);
+}
+
+// Activation bytes are stored permuted so that a masked shift of one packed weight word
+// lines up with one 4-byte activation word. For `bits`-bit codes a weight word holds
+// per = 32/bits codes; (word >> (bits*s)) & mask leaves in byte m the code s + G*m,
+// with G = 8/bits shift groups. Activation word k*G + s therefore holds the codes
+// per*k + s + G*m, m = 0..3. Returns the byte position of natural index i (0..31).
+template <int BITS>
+__host__ __device__ __forceinline__ int act_byte_pos(int i) {
+  constexpr int per = 32 / BITS, G = 8 / BITS;
+  const int kw = i / per, rem = i % per;
+  const int s = rem % G, m = rem / G;
+  return 4 * (kw * G + s) + m;
+}
+
+template <int BITS>
+struct CodeMask;
+template <>
+struct CodeMask<4> {
+  static constexpr uint32_t v = 0x0F0F0F0Fu;
+};
+template <>
+struct CodeMask<2> {
+  static constexpr uint32_t v = 0x03030303u;
+};
+
+// Exact int32 dot of one packed 32-code block against 8 permuted activation words.
+template <int BITS>
+__device__ __forceinline__ int block_dot(const uint32_t (&w)[BITS], const int* a) {
+  constexpr int G = 8 / BITS;
+  int acc = 0;
+#pragma unroll
+  for (int kw = 0; kw < BITS; ++kw)
+#pragma unroll
+    for (int s = 0; s < G; ++s)
+      acc = dot4_i8((int)((w[kw] >> (BITS * s)) & CodeMask<BITS>::v), a[kw * G + s], acc);
+  return acc;
+}
+
+// ------------------------------------------------------------------ workspace layouts
+
+__host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct DecodeWs {
+  size_t chunks;   // int4 [n*k]   (expert, first pair, pair count, 0)
+  size_t nchunks;  // int  [1]
+  size_t xq;       // int8 [n][d]  permuted activation codes
+  size_t xsc;      // double2 [n][d/32]   (scale, scale*sum of codes)
+  size_t hq;       // int8 [n*k][f] permuted hidden codes
+  size_t hsc;      // double2 [n*k][f/32]
+  size_t y;        // double [n*k][d]
+  size_t total;
+};
+
+inline DecodeWs decode_ws_layout(int n, int k, int d, int f) {
+  DecodeWs L;
+  size_t o = 0;
+  const size_t P = (size_t)n * k;
+  L.chunks = o;
+  o = align256(o + 16 * (P + 1));
+  L.nchunks = o;
+  o = align256(o + 16);
+  L.xq = o;
+  o = align256(o + (size_t)n * d);
+  L.xsc = o;
+  o = align256(o + 16 * (size_t)n * (d / 32));
+  L.hq = o;
+  o = align256(o + P * f);
+  L.hsc = o;
+  o = align256(o + 16 * P * (f / 32));
+  L.y = o;
+  o = align256(o + 8 * P * d);
+  L.total = o;
+  return L;
+}
+
+struct DecodeDebug {
+  int8_t* xq;
+  float* xs;
+  int32_t* gate_dots;
+  int32_t* up_dots;
+  float* g;
+  float* u;
+  float* h;
+  int8_t* hq;
+  float* hs;
+  int32_t* down_dots;
+  float* y;
+};
+
+struct DecodeArgs {
+  const moe_layer* L;
+  const float* x;
+  int n;
+  const moe_routing* r;
+  float* residual;
+  char* ws;
+  const DecodeDebug* dbg;  // nullptr: fast instances
+  hipStream_t stream;
+  int num_cus;
+};
+
+// ------------------------------------------------------------------ launchers
+
+hipError_t launch_route(const float* logits, int n, int E, int k, const moe_routing* out,
+                        hipStream_t stream);
+hipError_t launch_decode(const DecodeArgs& a);
+
+int device_cu_count();
+
+}  // namespace qmoe

@@ -1,0 +1,214 @@
+// Router top-k, routing weights and the grouping of token-expert pairs by expert.
+//
+// Selection follows the router of the Strata engine explainer (m.lqnn.cn/news/264700,
+// "Architecture overview": each token keeps the 10 of 512 experts its router picks);
+// the expert ids and routing weights form the hand-over record of the "Doorbell
+// handshake" section, and grouping by expert feeds a grouped expert kernel ("Expert
+// cache" section).
+//
+// One wavefront selects for one token: lane l holds the logits of experts l, l+64, ...
+// as 64-bit keys (order-preserving bits of the logit, then the complement of the expert
+// id so that equal logits favour the lower id); k rounds of a wave max-reduction pick
+// the slots in order. Weights are computed in binary64 and summed in slot order.
+// Grouping is a stable counting sort done by one workgroup: per-wave histograms in LDS,
+// a scan, and an in-order scatter where lanes holding the same expert are ranked with
+// ballots over the bits of the expert id.
+#include "qmoe_internal.h"
+
+namespace qmoe {
+
+namespace {
+
+constexpr int kGroupWaves = 8;
+constexpr int kGroupThreads = kGroupWaves * kWave;
+
+__device__ __forceinline__ uint32_t order_bits(float f) {
+  f = f + 0.0f;  // -0 becomes +0, so the two compare equal
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float order_bits_to_float(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+__device__ __forceinline__ uint64_t make_key(float logit, int e) {
+  return ((uint64_t)order_bits(logit) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
+}
+
+// Top-k of one token by one full wavefront; lane j < k writes slot j.
+template <int KPL>
+__device__ void wave_topk(const float* __restrict__ lrow, int E, int k, int32_t* __restrict__ ids,
+                          float* __restrict__ w) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t key[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int e = lane + kWave * i;
+    key[i] = e < E ? make_key(lrow[e], e) : 0ull;
+  }
+  int my_id = 0;
+  float my_l = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < KPL; ++i) best = key[i] > best ? key[i] : best;
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) {
+      const uint64_t o = __shfl_xor(best, off);
+      best = o > best ? o : best;
+    }
+    const int e = (int)(0xffffffffu - (uint32_t)best);
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+      if (lane + kWave * i == e) key[i] = 0ull;
+    if (lane == j) {
+      my_id = e;
+      my_l = order_bits_to_float((uint32_t)(best >> 32));
+    }
+  }
+  const double l0 = (double)__shfl(my_l, 0);
+  const double ex = lane < k ? exp((double)my_l - l0) : 0.0;
+  double sum = 0.0;
+  for (int j = 0; j < k; ++j) sum += __shfl(ex, j);  // slot order
+  if (lane < k) {
+    ids[lane] = my_id;
+    w[lane] = (float)(ex / sum);
+  }
+}
+
+// Exclusive scan of v[0..n) (n <= 2*kGroupThreads) in LDS by a kGroupThreads block.
+__device__ void block_exclusive_scan(int* v, int n, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int a = 2 * tid < n ? v[2 * tid] : 0;
+  const int b = 2 * tid + 1 < n ? v[2 * tid + 1] : 0;
+  int s = a + b, incl = s;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int i = 0; i < wave; ++i) wbase += wsum[i];
+  const int excl = wbase + incl - s;
+  __syncthreads();
+  if (2 * tid < n) v[2 * tid] = excl;
+  if (2 * tid + 1 < n) v[2 * tid + 1] = excl + a;
+  __syncthreads();
+}
+
+// Stable counting sort of pair ids 0..P-1 by ids[p], by one block of kGroupThreads.
+__device__ void group_block(const int32_t* ids, int P, int E, int32_t* __restrict__ offsets,
+                            int32_t* __restrict__ pair_index) {
+  __shared__ int s_hist[kGroupWaves * MOE_MAX_EXPERTS];  // [wave][E] counts, then bases
+  __shared__ int s_off[MOE_MAX_EXPERTS];
+  __shared__ int s_wsum[kGroupWaves];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  for (int i = tid; i < kGroupWaves * E; i += kGroupThreads) s_hist[i] = 0;
+  __syncthreads();
+  const int chunk = (P + kGroupWaves - 1) / kGroupWaves;
+  const int beg = min(P, wave * chunk), end = min(P, beg + chunk);
+  for (int p = beg + lane; p < end; p += kWave) atomicAdd(&s_hist[wave * E + ids[p]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += kGroupThreads) {
+    int run = 0;
+    for (int w = 0; w < kGroupWaves; ++w) {
+      const int c = s_hist[w * E + e];
+      s_hist[w * E + e] = run;
+      run += c;
+    }
+    s_off[e] = run;
+  }
+  __syncthreads();
+  block_exclusive_scan(s_off, E, s_wsum);
+  for (int e = tid; e < E; e += kGroupThreads) {
+    offsets[e] = s_off[e];
+    for (int w = 0; w < kGroupWaves; ++w) s_hist[w * E + e] += s_off[e];
+  }
+  if (tid == 0) offsets[E] = P;
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int base = beg; base < end; base += kWave) {
+    const int p = base + lane;
+    const bool valid = p < end;
+    const int e = valid ? ids[p] : 0;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 10; ++bit) {  // experts < 1024
+      const bool set = (e >> bit) & 1;
+      const uint64_t bal = __ballot(set);
+      same &= set ? bal : ~bal;
+    }
+    const int rank = __popcll(same & below);
+    const int cnt = __popcll(same);
+    int slot = 0;
+    if (valid) slot = s_hist[wave * E + e];
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      pair_index[slot + rank] = p;
+      if (rank == cnt - 1) s_hist[wave * E + e] = slot + cnt;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+template <int KPL>
+__global__ __launch_bounds__(kGroupThreads) void k_route_fused(
+    const float* __restrict__ logits, int n, int E, int k, int32_t* ids, float* __restrict__ w,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ pair_index) {
+  const int wave = threadIdx.x / kWave;
+  for (int t = wave; t < n; t += kGroupWaves)
+    wave_topk<KPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+  __threadfence_block();
+  __syncthreads();
+  group_block(ids, n * k, E, offsets, pair_index);
+}
+
+template <int KPL>
+__global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int n, int E,
+                                                    int k, int32_t* __restrict__ ids,
+                                                    float* __restrict__ w) {
+  const int t = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
+  if (t >= n) return;
+  wave_topk<KPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+}
+
+__global__ __launch_bounds__(kGroupThreads) void k_route_group(const int32_t* __restrict__ ids,
+                                                               int P, int E,
+                                                               int32_t* __restrict__ offsets,
+                                                               int32_t* __restrict__ pair_index) {
+  group_block(ids, P, E, offsets, pair_index);
+}
+
+template <int KPL>
+hipError_t launch_route_kpl(const float* logits, int n, int E, int k, const moe_routing* out,
+                            hipStream_t stream) {
+  if (n <= 64) {
+    hipLaunchKernelGGL(k_route_fused<KPL>, dim3(1), dim3(kGroupThreads), 0, stream, logits, n, E,
+                       k, out->topk_ids, out->topk_w, out->expert_offsets, out->pair_index);
+    return hipGetLastError();
+  }
+  hipLaunchKernelGGL(k_route_topk<KPL>, dim3((n + 3) / 4), dim3(256), 0, stream, logits, n, E, k,
+                     out->topk_ids, out->topk_w);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_route_group, dim3(1), dim3(kGroupThreads), 0, stream, out->topk_ids, n * k,
+                     E, out->expert_offsets, out->pair_index);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_route(const float* logits, int n, int E, int k, const moe_routing* out,
+                        hipStream_t stream) {
+  const int kpl = (E + kWave - 1) / kWave;
+  if (kpl <= 1) return launch_route_kpl<1>(logits, n, E, k, out, stream);
+  if (kpl <= 2) return launch_route_kpl<2>(logits, n, E, k, out, stream);
+  if (kpl <= 4) return launch_route_kpl<4>(logits, n, E, k, out, stream);
+  if (kpl <= 8) return launch_route_kpl<8>(logits, n, E, k, out, stream);
+  return launch_route_kpl<16>(logits, n, E, k, out, stream);
+}
+
+}  // namespace qmoe

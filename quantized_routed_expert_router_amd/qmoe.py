@@ -1,0 +1,206 @@
+"""Python binding of libqmoe (C ABI in include/qmoe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP kernels.
+PyTorch provides device memory and the current stream. There is no CPU fallback: if the
+compiled library is missing, importing this module raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+PKG_DIR = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG_DIR, "libqmoe.so")
+
+MOE_OK = 0
+STATUS = {0: "MOE_OK", 1: "MOE_ERR_INVALID_ARGUMENT", 2: "MOE_ERR_UNSUPPORTED",
+          3: "MOE_ERR_WORKSPACE_TOO_SMALL", 4: "MOE_ERR_HIP"}
+
+MAX_EXPERTS = 1024
+MAX_TOP_K = 64
+MAX_DECODE_TOKENS = 512
+MAX_PREFILL_TOKENS = 8192
+
+EXPORTS = ("moe_status_string", "moe_route_workspace_bytes", "moe_route",
+           "moe_ffn_workspace_bytes", "moe_expert_ffn_decode", "moe_expert_ffn_prefill")
+
+
+class MoeError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} failed: {STATUS.get(status, status)}")
+        self.status = status
+
+
+class _QMatrix(ctypes.Structure):
+    _fields_ = [("codes", ctypes.c_void_p), ("scale_min", ctypes.c_void_p),
+                ("rows", ctypes.c_int32), ("cols", ctypes.c_int32), ("bits", ctypes.c_int32)]
+
+
+class _Layer(ctypes.Structure):
+    _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
+                ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
+                ("gate", _QMatrix), ("up", _QMatrix), ("down", _QMatrix)]
+
+
+class _Routing(ctypes.Structure):
+    _fields_ = [("topk_ids", ctypes.c_void_p), ("topk_w", ctypes.c_void_p),
+                ("expert_offsets", ctypes.c_void_p), ("pair_index", ctypes.c_void_p)]
+
+
+DEBUG_FIELDS = ("xq", "xs", "gate_dots", "up_dots", "g", "u", "h", "hq", "hs", "down_dots", "y")
+
+
+class _Debug(ctypes.Structure):
+    _fields_ = [(name, ctypes.c_void_p) for name in DEBUG_FIELDS]
+
+
+def _load():
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing: build it with "
+                          "`python -m quantized_routed_expert_router_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    L.moe_status_string.argtypes = [i32]
+    L.moe_status_string.restype = ctypes.c_char_p
+    L.moe_route_workspace_bytes.argtypes = [i32, i32, i32]
+    L.moe_route_workspace_bytes.restype = sz
+    L.moe_route.argtypes = [vp, i32, i32, i32, ctypes.POINTER(_Routing), vp, sz, vp]
+    L.moe_ffn_workspace_bytes.argtypes = [ctypes.POINTER(_Layer), i32, i32]
+    L.moe_ffn_workspace_bytes.restype = sz
+    L.moe_expert_ffn_decode.argtypes = [ctypes.POINTER(_Layer), vp, i32, ctypes.POINTER(_Routing),
+                                        vp, vp, sz, ctypes.POINTER(_Debug), vp]
+    L.moe_expert_ffn_prefill.argtypes = [ctypes.POINTER(_Layer), vp, i32, ctypes.POINTER(_Routing),
+                                         vp, vp, sz, vp]
+    return L
+
+
+lib = _load()
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def status_string(status: int) -> str:
+    return lib.moe_status_string(status).decode()
+
+
+@dataclass
+class QMatrix:
+    """Packed weights of one projection for all experts, in device memory.
+    codes: int32 storage of uint32 [E][cols/32][rows][bits]; scale_min: int16 storage of
+    fp16 pairs [E][cols/32][rows][2]."""
+    codes: torch.Tensor
+    scale_min: torch.Tensor
+    rows: int
+    cols: int
+    bits: int
+
+    def _struct(self) -> _QMatrix:
+        return _QMatrix(self.codes.data_ptr(), self.scale_min.data_ptr(), self.rows, self.cols,
+                        self.bits)
+
+
+@dataclass
+class Layer:
+    d_model: int
+    d_ff: int
+    n_experts: int
+    top_k: int
+    gate: QMatrix
+    up: QMatrix
+    down: QMatrix
+
+    def _struct(self) -> _Layer:
+        return _Layer(self.d_model, self.d_ff, self.n_experts, self.top_k, self.gate._struct(),
+                      self.up._struct(), self.down._struct())
+
+
+@dataclass
+class Routing:
+    topk_ids: torch.Tensor      # int32 [n, k]
+    topk_w: torch.Tensor        # fp32 [n, k]
+    expert_offsets: torch.Tensor  # int32 [E+1]
+    pair_index: torch.Tensor    # int32 [n*k]
+
+    @staticmethod
+    def empty(n: int, E: int, k: int, device="cuda") -> "Routing":
+        return Routing(torch.empty((n, k), dtype=torch.int32, device=device),
+                       torch.empty((n, k), dtype=torch.float32, device=device),
+                       torch.empty(E + 1, dtype=torch.int32, device=device),
+                       torch.empty(max(n * k, 1), dtype=torch.int32, device=device))
+
+    def _struct(self) -> _Routing:
+        return _Routing(self.topk_ids.data_ptr(), self.topk_w.data_ptr(),
+                        self.expert_offsets.data_ptr(), self.pair_index.data_ptr())
+
+
+def route(logits: torch.Tensor, top_k: int, out: Routing | None = None, stream=None) -> Routing:
+    """moe_route: top-k experts, routing weights and expert grouping of `logits` [n, E]."""
+    n, E = logits.shape
+    if out is None:
+        out = Routing.empty(n, E, top_k, logits.device)
+    st = out._struct()
+    rc = lib.moe_route(_ptr(logits), n, E, top_k, ctypes.byref(st), None, 0, _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError("moe_route", rc)
+    return out
+
+
+def ffn_workspace_bytes(layer: Layer, n_tokens: int, prefill: bool = False) -> int:
+    st = layer._struct()
+    return int(lib.moe_ffn_workspace_bytes(ctypes.byref(st), n_tokens, 1 if prefill else 0))
+
+
+def workspace(layer: Layer, n_tokens: int, prefill: bool = False, device="cuda") -> torch.Tensor:
+    nbytes = max(ffn_workspace_bytes(layer, n_tokens, prefill), 256)
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def debug_buffers(layer: Layer, n: int, device="cuda") -> dict:
+    d, f, k = layer.d_model, layer.d_ff, layer.top_k
+    P = n * k
+    z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)  # noqa: E731
+    return dict(xq=z((n, d), torch.int8), xs=z((n, d // 32), torch.float32),
+                gate_dots=z((P, f, d // 32), torch.int32), up_dots=z((P, f, d // 32), torch.int32),
+                g=z((P, f), torch.float32), u=z((P, f), torch.float32), h=z((P, f), torch.float32),
+                hq=z((P, f), torch.int8), hs=z((P, f // 32), torch.float32),
+                down_dots=z((P, d, f // 32), torch.int32), y=z((P, d), torch.float32))
+
+
+def ffn_decode(layer: Layer, x: torch.Tensor, routing: Routing, residual: torch.Tensor,
+               ws: torch.Tensor | None = None, debug: dict | None = None, stream=None) -> None:
+    """moe_expert_ffn_decode: residual += routing-weighted expert outputs (in place)."""
+    n = x.shape[0]
+    if ws is None:
+        ws = workspace(layer, n, device=x.device)
+    st, rs = layer._struct(), routing._struct()
+    dbg = None
+    if debug is not None:
+        dbg = ctypes.byref(_Debug(**{k_: _ptr(debug.get(k_)) for k_ in DEBUG_FIELDS}))
+    rc = lib.moe_expert_ffn_decode(ctypes.byref(st), _ptr(x), n, ctypes.byref(rs), _ptr(residual),
+                                   _ptr(ws), ws.numel(), dbg, _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError("moe_expert_ffn_decode", rc)
+
+
+def ffn_prefill(layer: Layer, x_bf16: torch.Tensor, routing: Routing, residual: torch.Tensor,
+                ws: torch.Tensor | None = None, stream=None) -> None:
+    """moe_expert_ffn_prefill: bf16 matrix-core layer; residual updated in place."""
+    n = x_bf16.shape[0]
+    if ws is None:
+        ws = workspace(layer, n, prefill=True, device=x_bf16.device)
+    st, rs = layer._struct(), routing._struct()
+    rc = lib.moe_expert_ffn_prefill(ctypes.byref(st), _ptr(x_bf16), n, ctypes.byref(rs),
+                                    _ptr(residual), _ptr(ws), ws.numel(), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError("moe_expert_ffn_prefill", rc)

@@ -1,0 +1,54 @@
+"""Synthetic layers and inputs in device memory, for the tests and the benchmark.
+
+Weights come from the seeded generator (`synth`), written either straight into device
+memory by its GPU fill (large layers) or copied from host arrays (small layers and
+hand-modified cases). Nothing here computes a step of the layer.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import qmoe, synth
+
+
+def _stream_handle() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def device_matrix(w: synth.Workload, layer: int, tensor: int, rows: int, cols: int,
+                  device="cuda") -> qmoe.QMatrix:
+    codes = torch.empty(synth.matrix_words(w.E, rows, cols, w.bits), dtype=torch.int32,
+                        device=device)
+    sm = torch.empty(synth.matrix_halves(w.E, rows, cols), dtype=torch.int16, device=device)
+    synth.fill_matrix_device(codes.data_ptr(), sm.data_ptr(), w.seed, layer, tensor, w.E, rows,
+                             cols, w.bits, stream=_stream_handle())
+    return qmoe.QMatrix(codes, sm, rows, cols, w.bits)
+
+
+def device_layer(w: synth.Workload, layer: int, device="cuda") -> qmoe.Layer:
+    """All E experts of one layer instance generated on the GPU."""
+    return qmoe.Layer(w.d, w.f, w.E, w.k,
+                      device_matrix(w, layer, synth.T_GATE, w.f, w.d, device),
+                      device_matrix(w, layer, synth.T_UP, w.f, w.d, device),
+                      device_matrix(w, layer, synth.T_DOWN, w.d, w.f, device))
+
+
+def matrix_from_host(m: synth.HostMatrix, device="cuda") -> qmoe.QMatrix:
+    codes = torch.from_numpy(m.codes.reshape(-1).view(np.int32)).to(device)
+    sm = torch.from_numpy(m.scale_min.reshape(-1).view(np.int16)).to(device)
+    return qmoe.QMatrix(codes, sm, m.rows, m.cols, m.bits)
+
+
+def layer_from_host(gate: synth.HostMatrix, up: synth.HostMatrix, down: synth.HostMatrix, k: int,
+                    device="cuda") -> qmoe.Layer:
+    E = gate.codes.shape[0]
+    return qmoe.Layer(gate.cols, gate.rows, E, k, matrix_from_host(gate, device),
+                      matrix_from_host(up, device), matrix_from_host(down, device))
+
+
+def matrix_to_host(m: qmoe.QMatrix, E: int) -> synth.HostMatrix:
+    nb = m.cols // 32
+    codes = m.codes.cpu().numpy().view(np.uint32).reshape(E, nb, m.rows, m.bits)
+    sm = m.scale_min.cpu().numpy().view(np.uint16).reshape(E, nb, m.rows, 2)
+    return synth.HostMatrix(codes, sm, m.rows, m.cols, m.bits)

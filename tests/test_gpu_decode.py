@@ -1,0 +1,250 @@
+"""GPU parity of moe_route and moe_expert_ffn_decode against the CPU oracle.
+
+Every test runs the library through its C ABI on seeded inputs and compares with the
+oracle on the same bytes: bit-exact on expert ids, pair lists, int8 codes and per-block
+int32 dots; rel-L2 <= 1e-4 and max-abs <= 2e-3*rms(ref) on the fp32 layer output.
+"""
+from __future__ import annotations
+
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from quantized_routed_expert_router_amd import qmoe, synth, workloads
+
+from gpu_common import (assert_output_tolerance, check_routing, compare_decode_traces,
+                        device_layer_matches_host, omat, run_decode, to_dev)
+
+pytestmark = pytest.mark.gpu
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _small(E, d, f, k, n, bits, seed=0, layer=0, logits="normal"):
+    w = synth.Workload("small", d, f, E, k, n, bits, logits, seed=seed)
+    host = synth.host_layer(w, layer)
+    lg, x = synth.layer_inputs(w, layer)
+    return w, host, lg, x
+
+
+def _decode_parity(w, host, lg, x, layer=None, debug=True, dots=True, residual=None):
+    if layer is None:
+        layer = workloads.layer_from_host(*host, w.k)
+    dbg_keys = None
+    routing = qmoe.route(to_dev(lg), w.k)
+    ids, wt = check_routing(lg, w.k, routing)
+    res = x.copy() if residual is None else residual
+    res_d = to_dev(res)
+    dbg = None
+    if debug:
+        dbg = qmoe.debug_buffers(layer, x.shape[0])
+        if not dots:
+            for key in ("gate_dots", "up_dots", "down_dots"):
+                dbg.pop(key)
+    qmoe.ffn_decode(layer, to_dev(x), routing, res_d, debug=dbg)
+    torch.cuda.synchronize()
+    out = res_d.cpu().numpy()
+    out_o, tr = O.ffn_decode(*(omat(h) for h in host), w.E, x, ids, wt, res, trace=debug)
+    if debug:
+        compare_decode_traces(dbg, tr, host, ids, w.bits)
+        np.testing.assert_allclose(dbg["y"].cpu().numpy(), tr["y"].astype(np.float32),
+                                   rtol=1e-6, atol=1e-7)
+    assert_output_tolerance(out, out_o, what="residual out")
+    assert_output_tolerance(out - res, out_o - res, what="moe delta")
+    del dbg_keys
+    return out, out_o, ids, wt
+
+
+# ------------------------------------------------------------------ routing
+
+def test_route_golden_ties():
+    with open(os.path.join(GOLDEN, "route_ties.json")) as fh:
+        cases = json.load(fh)["cases"]
+    for c in cases:
+        lg = np.array(c["logits"], np.float32)[None, :]
+        r = qmoe.route(to_dev(lg), c["k"])
+        torch.cuda.synchronize()
+        assert r.topk_ids.cpu().numpy()[0].tolist() == c["ids"], c["name"]
+        np.testing.assert_allclose(r.topk_w.cpu().numpy()[0], c["w"], rtol=1e-7, atol=0)
+
+
+@pytest.mark.parametrize("n,E,k,kind", [
+    (1, 8, 2, "normal"), (4, 512, 10, "zipf"), (5, 33, 7, "normal"), (3, 8, 8, "normal"),
+    (6, 100, 1, "normal"), (64, 512, 10, "uniform"), (65, 512, 10, "uniform"),
+    (256, 512, 10, "uniform"), (8192, 512, 10, "zipf"), (2, 1024, 64, "normal"),
+    (300, 1000, 3, "normal")])
+def test_route_matches_oracle(n, E, k, kind):
+    lg = synth.logits(0, 7, n, E, kind)
+    r = qmoe.route(to_dev(lg), k)
+    torch.cuda.synchronize()
+    check_routing(lg, k, r)
+
+
+def test_route_many_ties():
+    # logits on a coarse grid: many equal values, -0 and +0 mixed
+    rng = np.random.default_rng(3)
+    lg = (rng.integers(-3, 4, (40, 64)) * 0.5).astype(np.float32)
+    lg[lg == 0] = np.where(rng.random((lg == 0).sum()) < 0.5, -0.0, 0.0)
+    r = qmoe.route(to_dev(lg), 10)
+    torch.cuda.synchronize()
+    check_routing(lg, 10, r)
+
+
+def test_route_zero_tokens_writes_empty_offsets():
+    r = qmoe.Routing.empty(0, 16, 2)
+    r.expert_offsets.fill_(-1)
+    qmoe.route(torch.empty((0, 16), dtype=torch.float32, device="cuda"), 2, out=r)
+    torch.cuda.synchronize()
+    assert np.all(r.expert_offsets.cpu().numpy() == 0)
+
+
+# ------------------------------------------------------------------ decode, small shapes
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_decode_config1_tiny(bits):
+    w = synth.config(1)
+    w.bits = bits
+    host = synth.host_layer(w, 0)
+    lg, x = synth.layer_inputs(w, 0)
+    _decode_parity(w, host, lg, x)
+
+
+@pytest.mark.parametrize("E,d,f,k,n,bits", [
+    (8, 96, 160, 3, 5, 4),    # f not a multiple of 64: partial row tiles
+    (6, 160, 96, 2, 7, 2),    # ragged token count, NPC=8 path
+    (8, 64, 64, 8, 3, 4),     # k = E: every expert
+    (16, 128, 64, 1, 9, 4),   # k = 1: weights exactly 1
+    (5, 64, 32, 2, 40, 2),    # many pairs per expert: several chunks per expert
+])
+def test_decode_small_shapes(E, d, f, k, n, bits):
+    w, host, lg, x = _small(E, d, f, k, n, bits, seed=1)
+    res = synth.normal(1, 9, 0, (n, d))
+    _decode_parity(w, host, lg, x, residual=res)
+
+
+def test_decode_x_aliases_residual():
+    w, host, lg, x = _small(8, 128, 64, 2, 3, 4, seed=2)
+    layer = workloads.layer_from_host(*host, w.k)
+    routing = qmoe.route(to_dev(lg), w.k)
+    buf = to_dev(x)
+    qmoe.ffn_decode(layer, buf, routing, buf)
+    torch.cuda.synchronize()
+    ids, wt = O.route(lg, w.k)
+    out_o, _ = O.ffn_decode(*(omat(h) for h in host), w.E, x, ids, wt, x)
+    assert_output_tolerance(buf.cpu().numpy(), out_o)
+
+
+def test_decode_zero_expert_contributes_exactly_zero():
+    w, host, lg, x = _small(8, 128, 64, 3, 4, 4, seed=3)
+    ids, _ = O.route(lg, w.k)
+    z = int(ids[1, 0])
+    for m in host:
+        m.codes[z] = 0
+        m.scale_min[z] = 0
+    layer = workloads.layer_from_host(*host, w.k)
+    routing = qmoe.route(to_dev(lg), w.k)
+    res_a = to_dev(x)
+    dbg = qmoe.debug_buffers(layer, x.shape[0])
+    qmoe.ffn_decode(layer, to_dev(x), routing, res_a, debug=dbg)
+    # same call with that expert's slots weighted 0 must give bit-identical output
+    routing.topk_w[routing.topk_ids == z] = 0.0
+    res_b = to_dev(x)
+    qmoe.ffn_decode(layer, to_dev(x), routing, res_b)
+    torch.cuda.synchronize()
+    assert np.all(dbg["y"].cpu().numpy()[ids.ravel() == z] == 0.0)
+    assert torch.equal(res_a, res_b)
+
+
+def test_decode_zero_input_returns_residual():
+    w, host, lg, x = _small(8, 64, 64, 2, 3, 2, seed=4)
+    layer = workloads.layer_from_host(*host, w.k)
+    routing = qmoe.route(to_dev(lg), w.k)
+    res = to_dev(synth.normal(4, 9, 0, (3, 64)))
+    before = res.clone()
+    qmoe.ffn_decode(layer, torch.zeros((3, 64), dtype=torch.float32, device="cuda"), routing, res)
+    torch.cuda.synchronize()
+    assert torch.equal(res, before)
+
+
+def test_decode_zero_tokens_is_noop():
+    w, host, lg, x = _small(8, 64, 64, 2, 1, 4, seed=5)
+    layer = workloads.layer_from_host(*host, w.k)
+    r = qmoe.Routing.empty(0, 8, 2)
+    qmoe.route(torch.empty((0, 8), dtype=torch.float32, device="cuda"), 2, out=r)
+    res = torch.empty((0, 64), dtype=torch.float32, device="cuda")
+    qmoe.ffn_decode(layer, res, r, res, ws=torch.empty(256, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+
+
+def test_decode_deterministic():
+    w, host, lg, x = _small(16, 256, 128, 4, 5, 4, seed=6)
+    layer = workloads.layer_from_host(*host, w.k)
+    outs = []
+    for _ in range(3):
+        routing = qmoe.route(to_dev(lg), w.k)
+        res = to_dev(x)
+        qmoe.ffn_decode(layer, to_dev(x), routing, res)
+        outs.append(res)
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0], outs[1]) and torch.equal(outs[0], outs[2])
+
+
+# ------------------------------------------------------------------ decode, full layer shapes
+
+@pytest.fixture(scope="module")
+def cfg2_layer():
+    w = synth.config(2)
+    layer = workloads.device_layer(w, 0)
+    torch.cuda.synchronize()
+    return w, layer
+
+
+def test_decode_config2_t4_full_trace(cfg2_layer):
+    w, layer = cfg2_layer
+    lg, x = synth.layer_inputs(w, 0)
+    ids, _ = O.route(lg, w.k)
+    experts = np.unique(ids)
+    host = synth.host_layer(w, 0, experts=experts)
+    device_layer_matches_host(layer, host, experts, w.E)
+    _decode_parity(w, host, lg, x, layer=layer)
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 5])
+def test_decode_config2_window_sizes(cfg2_layer, T):
+    w, layer = cfg2_layer
+    w = synth.Workload(w.name, w.d, w.f, w.E, w.k, T, w.bits, w.logits)
+    lg, x = synth.layer_inputs(w, 10 + T)
+    ids, _ = O.route(lg, w.k)
+    host = synth.host_layer(synth.config(2), 0, experts=np.unique(ids))
+    _decode_parity(w, host, lg, x, layer=layer, dots=False)
+
+
+def test_decode_max_tokens_sampled(cfg2_layer):
+    # n = 512, the decode maximum; the oracle evaluates a sample of tokens
+    w, layer = cfg2_layer
+    n = qmoe.MAX_DECODE_TOKENS
+    lg = synth.logits(0, 21, n, w.E, "uniform")
+    x = synth.activations(0, 21, n, w.d)
+    routing, out, _ = run_decode(layer, lg, x, w.k)
+    ids, wt = check_routing(lg, w.k, routing)
+    tokens = np.array([0, 1, 77, 255, 256, 400, 510, 511], np.int32)
+    host = synth.host_layer(synth.config(2), 0, experts=np.unique(ids[tokens]))
+    out_o, _ = O.ffn_decode(*(omat(h) for h in host), w.E, x, ids, wt, x, tokens=tokens)
+    assert_output_tolerance(out[tokens], out_o)
+    assert_output_tolerance(out[tokens] - x[tokens], out_o - x[tokens], what="moe delta")
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_config3_2bit_batched(T):
+    w = synth.config(3, T)
+    layer = workloads.device_layer(w, 0)
+    lg, x = synth.layer_inputs(w, 0)
+    ids, _ = O.route(lg, w.k)
+    experts = np.unique(ids)
+    host = synth.host_layer(w, 0, experts=experts)
+    device_layer_matches_host(layer, host, experts[::37], w.E)
+    _decode_parity(w, host, lg, x, layer=layer, dots=False)
