@@ -1,0 +1,339 @@
+#!/usr/bin/env python3
+"""Benchmark of the routed-expert MoE layer on one MI355X.
+
+Default workload (the one the headline metric is quoted on): one layer of d=2048, f=768,
+E=512 experts, top-10, 4-bit block-32 weights with fp16 scale+min, a T=4 speculative
+verify window, Zipf(1.1)-biased router logits. One step = moe_route + the decode expert
+FFN (int8 activation quantization, gate/up, SwiGLU, h quantization, down, combine) for
+the window's 4 tokens. Steps rotate over several independently generated layer
+instances so that consecutive steps read different experts and the 256 MB Infinity
+Cache cannot serve the weights (each instance is 1.51 GB; the touched experts of one
+step are ~63 MB).
+
+Reported:
+  value         expert-weight bytes streamed per second over whole steps (GB/s), with
+                bytes counted from each step's actual routing: every distinct touched
+                expert once, 3*f*d*(bits+1)/8 bytes;
+  tokens_per_s  window tokens per second (4 per step);
+  roofline      the dominant kernel (gate/up projections: 2/3 of the bytes) against the
+                8 TB/s HBM peak, its duration taken from HIP events around that stage in
+                an instrumented timed region;
+  cpu_baseline  the CPU oracle on the host cores, on a bounded sample of the same steps.
+
+Supplementary workloads (--config): 3 = 2-bit, 64 sequences x T (T=1 or 4), uniform
+logits; 4 = 48 chained layers, one decode step; 5 = 8192-token prefill chunk.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = ("expert-weight HBM GB/s (% of peak) and MoE-layer tokens/s, T=4 decode window")
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, AMD published
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawTextHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=400)
+    ap.add_argument("--warmup", type=int, default=40)
+    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--T", type=int, default=4, help="window size for --config 3")
+    ap.add_argument("--instances", type=int, default=0,
+                    help="layer instances rotated over (default: 10 for config 2, 3 for 3)")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="target CPU time of the oracle baseline sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+class Step:
+    """Pre-built C structs of one layer instance, so the timed loop only makes C calls."""
+
+    def __init__(self, q, layer, lg, x, res, routing, ws):
+        self.q = q
+        self.layer_s = layer._struct()
+        self.rout_s = routing._struct()
+        self.routing = routing
+        self.lg, self.x, self.res, self.ws = lg, x, res, ws
+        self.n, self.E = lg.shape
+        self.k = layer.top_k
+
+    def route(self, stream):
+        rc = self.q.lib.moe_route(self.lg.data_ptr(), self.n, self.E, self.k,
+                                  ctypes.byref(self.rout_s), None, 0, stream)
+        assert rc == 0, rc
+
+    def decode(self, stream, stages):
+        rc = self.q.lib.moe_expert_ffn_decode_stages(
+            ctypes.byref(self.layer_s), self.x.data_ptr(), self.n, ctypes.byref(self.rout_s),
+            self.res.data_ptr(), self.ws.data_ptr(), self.ws.numel(), None, stages, stream)
+        assert rc == 0, rc
+
+
+def sleep_cycles_for(torch, seconds):
+    """Spin-kernel length covering `seconds` of host enqueue time (calibrated)."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    n = 2_000_000
+    torch.cuda.synchronize()
+    s.record()
+    torch.cuda._sleep(n)
+    e.record()
+    torch.cuda.synchronize()
+    per_cycle = max(s.elapsed_time(e) * 1e-3 / n, 1e-12)
+    return int(seconds / per_cycle)
+
+
+def timed_region(torch, q, steps, order, instrument, enqueue_estimate):
+    """Run the steps back to back on the GPU: a spin kernel holds the queue while the host
+    enqueues every step, so host launch cost does not open gaps between kernels.
+    Returns (total_ms, per-step stage ms list or None)."""
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = None
+    if instrument:
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in order]
+    cycles = sleep_cycles_for(torch, max(0.02, 2.0 * enqueue_estimate))
+    torch.cuda.synchronize()
+    torch.cuda._sleep(cycles)
+    start.record()
+    t0 = time.perf_counter()
+    for s_idx, i in enumerate(order):
+        st = steps[i]
+        if instrument:
+            ev = evs[s_idx]
+            ev[0].record()
+            st.route(sh)
+            ev[1].record()
+            st.decode(sh, q.DECODE_PREP)
+            ev[2].record()
+            st.decode(sh, q.DECODE_GATE_UP)
+            ev[3].record()
+            st.decode(sh, q.DECODE_DOWN | q.DECODE_COMBINE)
+            ev[4].record()
+        else:
+            st.route(sh)
+            st.decode(sh, q.DECODE_ALL)
+    end.record()
+    host_s = time.perf_counter() - t0
+    covered = not start.query()  # the spin kernel still ran when the last step was queued
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(end)
+    stages = None
+    if instrument:
+        stages = [[ev[j].elapsed_time(ev[j + 1]) for j in range(4)] for ev in evs]
+    return total_ms, stages, host_s, covered
+
+
+def touched_experts(routing) -> int:
+    off = routing.expert_offsets.cpu()
+    return int(((off[1:] - off[:-1]) > 0).sum())
+
+
+def cpu_baseline(w, instances_inputs, seconds):
+    """The oracle (as it stands) on host cores, over config steps until ~`seconds`."""
+    import numpy as np
+
+    from oracle import oracle as O
+    from quantized_routed_expert_router_amd import synth
+
+    cores = O.threads(0)
+    total_t, total_b, steps = 0.0, 0, 0
+    host_layers = {}
+    i = 0
+    while total_t < seconds and steps < 10_000:
+        idx = i % len(instances_inputs)
+        lg, x = instances_inputs[idx]
+        ids_pre = np.argsort(-lg, axis=1, kind="stable")[:, :w.k]
+        if idx not in host_layers:
+            host_layers[idx] = synth.host_layer(w, idx, experts=np.unique(ids_pre))
+        g, u, dn = host_layers[idx]
+        om = lambda h: O.Matrix(h.codes, h.scale_min, h.rows, h.cols, h.bits)  # noqa: E731
+        t0 = time.perf_counter()
+        ids, wt = O.route(lg, w.k)
+        O.group(ids, w.E)
+        O.ffn_decode(om(g), om(u), om(dn), w.E, x, ids, wt, x)
+        total_t += time.perf_counter() - t0
+        total_b += len(np.unique(ids)) * synth.expert_bytes(w.d, w.f, w.bits)
+        steps += 1
+        i += 1
+    return dict(value=round(total_b / total_t / 1e9, 4), unit="GB/s", cores=cores, kind="oracle",
+                sample=f"{steps} steps of the same workload (route + decode layer, {w.n} tokens "
+                       f"each) over {min(steps, len(instances_inputs))} layer instances, "
+                       f"{total_t:.1f} s of oracle time on {cores} threads",
+                tokens_per_s=round(steps * w.n / total_t, 3))
+
+
+def bench_decode(args, torch, q, synth, workloads):
+    import numpy as np
+
+    w = synth.config(args.config, args.T)
+    L = args.instances or (10 if args.config == 2 else 3)
+    log(f"workload {w.name}: generating {L} layer instances on the GPU")
+    t0 = time.perf_counter()
+    steps, inputs = [], []
+    ws = q.workspace(_shape_layer(q, w), w.n)
+    for i in range(L):
+        layer = workloads.device_layer(w, i)
+        lg, x = synth.layer_inputs(w, i)
+        inputs.append((lg, x))
+        lg_d = torch.from_numpy(lg).cuda()
+        x_d = torch.from_numpy(x).cuda()
+        routing = q.Routing.empty(w.n, w.E, w.k)
+        steps.append(Step(q, layer, lg_d, x_d, x_d.clone(), routing, ws))
+    torch.cuda.synchronize()
+    log(f"generated {L} x {3 * w.E * synth.expert_bytes(w.d, w.f, w.bits) // 3 / 1e9:.2f} GB "
+        f"in {time.perf_counter() - t0:.1f} s")
+
+    # routing of each instance (fixed per instance): bytes per step
+    sh = torch.cuda.current_stream().cuda_stream
+    for st in steps:
+        st.route(sh)
+    torch.cuda.synchronize()
+    ebytes = synth.expert_bytes(w.d, w.f, w.bits)
+    touched = [touched_experts(st.routing) for st in steps]
+    step_bytes = [t * ebytes for t in touched]
+    gu_bytes = [t * ebytes * 2 // 3 for t in touched]
+
+    warm = [s % L for s in range(args.warmup)]
+    order = [s % L for s in range(args.steps)]
+    # warmup (also estimates the host enqueue time per step)
+    _, _, host_s, _ = timed_region(torch, q, steps, warm or [0], False, 0.05)
+    est = host_s / max(1, len(warm)) * len(order)
+    total_ms, _, host_s, covered = timed_region(torch, q, steps, order, False, est)
+    inst_ms, stage_ms, _, covered_i = timed_region(torch, q, steps, order, True, est * 2)
+    if not (covered and covered_i):
+        log("warning: the host enqueue outlasted the spin kernel; gaps may be included")
+
+    sec = total_ms * 1e-3
+    tot_bytes = sum(step_bytes[i] for i in order)
+    value = tot_bytes / sec / 1e9
+    tok_s = len(order) * w.n / sec
+    st_ms = np.array(stage_ms)  # [K, 4]: route, prep, gate_up, down+combine
+    gu_sec = st_ms[:, 2].sum() * 1e-3
+    gu_ach = sum(gu_bytes[i] for i in order) / gu_sec / 1e9
+    mean_us = st_ms.mean(axis=0) * 1e3
+    mean_touched = float(np.mean([touched[i] for i in order]))
+    rec = {
+        "metric": METRIC if args.config == 2 else f"{METRIC} [supplementary: {w.name}]",
+        "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(total_ms / len(order), 5),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "d_model": w.d, "d_ff": w.f, "experts": w.E,
+                   "top_k": w.k, "tokens_per_step": w.n, "weight_bits": w.bits,
+                   "layer_instances": L, "step": "moe_route + moe_expert_ffn_decode"},
+        "tokens_per_s": round(tok_s, 1),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "expert_bytes_per_step": round(float(np.mean([step_bytes[i] for i in order])), 1),
+        "touched_experts_per_step": round(mean_touched, 2),
+        "stage_us": {"route": round(mean_us[0], 2), "prep": round(mean_us[1], 2),
+                     "gate_up": round(mean_us[2], 2), "down_combine": round(mean_us[3], 2),
+                     "instrumented_step": round(inst_ms / len(order) * 1e3, 2)},
+        "roofline": {"bound": "hbm", "kernel": "k_gateup (gate/up + SwiGLU + h quant)",
+                     "achieved": round(gu_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(gu_ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": round(float(np.mean([gu_bytes[i] for i in order])), 1)},
+    }
+    if args.config == 2 and not args.no_cpu_baseline:
+        log("CPU oracle baseline ...")
+        rec["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)
+    return rec
+
+
+def _shape_layer(q, w):
+    """A layer description with the right sizes for workspace queries (no weights)."""
+    import torch
+
+    dummy = torch.empty(16, dtype=torch.int32, device="cuda")
+    dummy16 = torch.empty(16, dtype=torch.int16, device="cuda")
+    mk = lambda r, c: q.QMatrix(dummy, dummy16, r, c, w.bits)  # noqa: E731
+    return q.Layer(w.d, w.f, w.E, w.k, mk(w.f, w.d), mk(w.f, w.d), mk(w.d, w.f))
+
+
+def bench_chain(args, torch, q, synth, workloads):
+    import numpy as np
+
+    w = synth.config(4)
+    log(f"workload {w.name}: generating {w.layers} layers on the GPU")
+    t0 = time.perf_counter()
+    ws = q.workspace(_shape_layer(q, w), w.n)
+    x0 = torch.from_numpy(synth.activations(w.seed, 0, w.n, w.d)).cuda()
+    res = x0.clone()
+    steps = []
+    for l_ in range(w.layers):
+        layer = workloads.device_layer(w, l_)
+        lg = torch.from_numpy(synth.logits(w.seed, l_, w.n, w.E, w.logits)).cuda()
+        routing = q.Routing.empty(w.n, w.E, w.k)
+        steps.append(Step(q, layer, lg, res, res, routing, ws))  # x is the residual stream
+    torch.cuda.synchronize()
+    log(f"generated in {time.perf_counter() - t0:.1f} s")
+    sh = torch.cuda.current_stream().cuda_stream
+    for st in steps:
+        st.route(sh)
+    torch.cuda.synchronize()
+    ebytes = synth.expert_bytes(w.d, w.f, w.bits)
+    touched = [touched_experts(st.routing) for st in steps]
+    chain_bytes = sum(touched) * ebytes
+    order = list(range(w.layers)) * max(1, args.steps // w.layers)
+    _, _, host_s, _ = timed_region(torch, q, steps, list(range(w.layers)), False, 0.1)
+    est = host_s * len(order) / w.layers
+    total_ms, _, _, covered = timed_region(torch, q, steps, order, False, est)
+    n_chain = len(order) // w.layers
+    sec = total_ms * 1e-3
+    value = chain_bytes * n_chain / sec / 1e9
+    return {
+        "metric": f"{METRIC} [supplementary: {w.name}]", "value": round(value, 2), "unit": "GB/s",
+        "n_gpus": 1, "steps": n_chain, "warmup": 1, "ms_per_step": round(total_ms / n_chain, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
+        "data": "synthetic",
+        "config": {"workload": w.name, "layers": w.layers, "tokens_per_step": w.n,
+                   "step": "48 x (moe_route + moe_expert_ffn_decode), residual chained"},
+        "tokens_per_s": round(n_chain * w.n / sec, 1),
+        "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
+        "expert_bytes_per_step": chain_bytes,
+        "expert_bytes_per_token": chain_bytes / w.n,
+        "pages_bytes_per_token": 663.6e6,
+        "touched_experts_per_layer": round(float(np.mean(touched)), 2),
+        "enqueue_covered": covered,
+    }
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: this build measures the routed-expert layer on "
+              "one MI355X (how the layer would shard over several GPUs is described in "
+              "DESIGN.md); rerun with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from quantized_routed_expert_router_amd import qmoe as q
+    from quantized_routed_expert_router_amd import synth, workloads
+
+    torch.cuda.set_device(0)
+    if args.config in (2, 3):
+        rec = bench_decode(args, torch, q, synth, workloads)
+    elif args.config == 4:
+        rec = bench_chain(args, torch, q, synth, workloads)
+    else:
+        raise SystemExit("prefill benchmark not built yet")
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

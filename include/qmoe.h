@@ -158,6 +158,24 @@ moe_status moe_expert_ffn_decode(const moe_layer* L, const float* x, int n_token
                                  const moe_routing* r, float* residual, void* ws,
                                  size_t ws_bytes, const moe_debug* dbg, void* stream);
 
+/* Stages of moe_expert_ffn_decode, as bits of `stages` below. */
+#define MOE_DECODE_PREP 1u     /* int8 quantization of x and the per-expert work list     */
+#define MOE_DECODE_GATE_UP 2u  /* gate/up projections, SwiGLU, int8 quantization of h      */
+#define MOE_DECODE_DOWN 4u     /* down projection of every token-expert pair               */
+#define MOE_DECODE_COMBINE 8u  /* routing-weighted combine into the residual              */
+#define MOE_DECODE_ALL 15u
+
+/* moe_expert_ffn_decode split into its stages, for callers that interleave other work
+ * (or timing events) between them. The selected stages are enqueued in the order above;
+ * a stage reads what the earlier stages wrote into `ws`, so every stage of one layer
+ * call must be issued, in order, with the same arguments and workspace. Arguments and
+ * errors as moe_expert_ffn_decode; stages == MOE_DECODE_ALL is moe_expert_ffn_decode.
+ * MOE_ERR_INVALID_ARGUMENT if stages is 0 or has bits outside MOE_DECODE_ALL. */
+moe_status moe_expert_ffn_decode_stages(const moe_layer* L, const float* x, int n_tokens,
+                                        const moe_routing* r, float* residual, void* ws,
+                                        size_t ws_bytes, const moe_debug* dbg, unsigned stages,
+                                        void* stream);
+
 /* Prefill-chunk expert FFN with bf16 arithmetic on the matrix cores: weights are
  * dequantized to bf16 (bf16 of fp32 scale*q + min), x_bf16: device bf16 bits [n][d];
  * gate/up accumulate in fp32; h = bf16(silu(g) * u); down accumulates in fp32;

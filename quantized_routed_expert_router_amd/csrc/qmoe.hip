@@ -118,6 +118,15 @@ size_t moe_ffn_workspace_bytes(const moe_layer* L, int n_tokens, int prefill) {
 moe_status moe_expert_ffn_decode(const moe_layer* L, const float* x, int n_tokens,
                                  const moe_routing* r, float* residual, void* ws,
                                  size_t ws_bytes, const moe_debug* dbg, void* stream) {
+  return moe_expert_ffn_decode_stages(L, x, n_tokens, r, residual, ws, ws_bytes, dbg,
+                                      MOE_DECODE_ALL, stream);
+}
+
+moe_status moe_expert_ffn_decode_stages(const moe_layer* L, const float* x, int n_tokens,
+                                        const moe_routing* r, float* residual, void* ws,
+                                        size_t ws_bytes, const moe_debug* dbg, unsigned stages,
+                                        void* stream) {
+  if (stages == 0 || (stages & ~MOE_DECODE_ALL)) return MOE_ERR_INVALID_ARGUMENT;
   moe_status s = check_layer(L);
   if (s != MOE_OK) return s;
   if (n_tokens < 0 || n_tokens > MOE_MAX_DECODE_TOKENS) return MOE_ERR_INVALID_ARGUMENT;
@@ -139,7 +148,7 @@ moe_status moe_expert_ffn_decode(const moe_layer* L, const float* x, int n_token
                      dbg->u,  dbg->h,  dbg->hq,        dbg->hs,      dbg->down_dots, dbg->y};
   }
   DecodeArgs a{L, x, n_tokens, r, residual, (char*)ws, dbg ? &dd : nullptr,
-               (hipStream_t)stream, device_cu_count()};
+               (hipStream_t)stream, device_cu_count(), stages};
   const hipError_t err = launch_decode(a);
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }

@@ -390,37 +390,45 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   if (DBG) dbg = *a.dbg;
 
   const int nbd = d / 32;
-  const int prep_blocks = 1 + (n * nbd + kThreads - 1) / kThreads;
-  hipLaunchKernelGGL(k_prep<BITS>, dim3(prep_blocks), dim3(kThreads), 0, a.stream, a.x, n, d,
-                     a.r->expert_offsets, E, NPC, chunks, nchunks, xq, xsc,
-                     DBG ? dbg.xq : nullptr, DBG ? dbg.xs : nullptr);
-  hipError_t err = hipGetLastError();
-  if (err != hipSuccess) return err;
+  hipError_t err = hipSuccess;
+  if (a.stages & MOE_DECODE_PREP) {
+    const int prep_blocks = 1 + (n * nbd + kThreads - 1) / kThreads;
+    hipLaunchKernelGGL(k_prep<BITS>, dim3(prep_blocks), dim3(kThreads), 0, a.stream, a.x, n, d,
+                       a.r->expert_offsets, E, NPC, chunks, nchunks, xq, xsc,
+                       DBG ? dbg.xq : nullptr, DBG ? dbg.xs : nullptr);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
 
   // upper bound of chunks: every chunk holds >= 1 pair, and an expert holds <= n pairs
   const long long max_chunks =
       std::min<long long>((long long)n * k, (long long)E * ((n + NPC - 1) / NPC));
   const int cap = a.num_cus * 8;
-  const long long gu_items = max_chunks * ((f + kWave - 1) / kWave);
-  const int gu_grid = (int)std::max<long long>(1, std::min<long long>(gu_items, cap));
-  hipLaunchKernelGGL((k_gateup<BITS, NPC, DBG>), dim3(gu_grid), dim3(kThreads), 0, a.stream,
-                     L.gate.codes, reinterpret_cast<const uint32_t*>(L.gate.scale_min),
-                     L.up.codes, reinterpret_cast<const uint32_t*>(L.up.scale_min), d, f, k,
-                     chunks, nchunks, a.r->pair_index, xq, xsc, hq, hsc, dbg);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
-  const long long dn_items = max_chunks * ((d + kWave - 1) / kWave);
-  const int dn_grid = (int)std::max<long long>(1, std::min<long long>(dn_items, cap));
-  hipLaunchKernelGGL((k_down<BITS, NPC, DBG>), dim3(dn_grid), dim3(kThreads), 0, a.stream,
-                     L.down.codes, reinterpret_cast<const uint32_t*>(L.down.scale_min), d, f,
-                     chunks, nchunks, a.r->pair_index, hq, hsc, y, dbg);
-  err = hipGetLastError();
-  if (err != hipSuccess) return err;
-
-  hipLaunchKernelGGL(k_combine, dim3((n * d + kThreads - 1) / kThreads), dim3(kThreads), 0,
-                     a.stream, y, a.r->topk_w, n, d, k, a.residual);
-  return hipGetLastError();
+  if (a.stages & MOE_DECODE_GATE_UP) {
+    const long long gu_items = max_chunks * ((f + kWave - 1) / kWave);
+    const int gu_grid = (int)std::max<long long>(1, std::min<long long>(gu_items, cap));
+    hipLaunchKernelGGL((k_gateup<BITS, NPC, DBG>), dim3(gu_grid), dim3(kThreads), 0, a.stream,
+                       L.gate.codes, reinterpret_cast<const uint32_t*>(L.gate.scale_min),
+                       L.up.codes, reinterpret_cast<const uint32_t*>(L.up.scale_min), d, f, k,
+                       chunks, nchunks, a.r->pair_index, xq, xsc, hq, hsc, dbg);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (a.stages & MOE_DECODE_DOWN) {
+    const long long dn_items = max_chunks * ((d + kWave - 1) / kWave);
+    const int dn_grid = (int)std::max<long long>(1, std::min<long long>(dn_items, cap));
+    hipLaunchKernelGGL((k_down<BITS, NPC, DBG>), dim3(dn_grid), dim3(kThreads), 0, a.stream,
+                       L.down.codes, reinterpret_cast<const uint32_t*>(L.down.scale_min), d, f,
+                       chunks, nchunks, a.r->pair_index, hq, hsc, y, dbg);
+    err = hipGetLastError();
+    if (err != hipSuccess) return err;
+  }
+  if (a.stages & MOE_DECODE_COMBINE) {
+    hipLaunchKernelGGL(k_combine, dim3((n * d + kThreads - 1) / kThreads), dim3(kThreads), 0,
+                       a.stream, y, a.r->topk_w, n, d, k, a.residual);
+    err = hipGetLastError();
+  }
+  return err;
 }
 
 template <int BITS, bool DBG>

@@ -131,6 +131,7 @@ struct DecodeArgs {
   const DecodeDebug* dbg;  // nullptr: fast instances
   hipStream_t stream;
   int num_cus;
+  unsigned stages;  // MOE_DECODE_* bits
 };
 
 // ------------------------------------------------------------------ launchers

@@ -25,7 +25,10 @@ MAX_DECODE_TOKENS = 512
 MAX_PREFILL_TOKENS = 8192
 
 EXPORTS = ("moe_status_string", "moe_route_workspace_bytes", "moe_route",
-           "moe_ffn_workspace_bytes", "moe_expert_ffn_decode", "moe_expert_ffn_prefill")
+           "moe_ffn_workspace_bytes", "moe_expert_ffn_decode", "moe_expert_ffn_decode_stages",
+           "moe_expert_ffn_prefill")
+
+DECODE_PREP, DECODE_GATE_UP, DECODE_DOWN, DECODE_COMBINE, DECODE_ALL = 1, 2, 4, 8, 15
 
 
 class MoeError(RuntimeError):
@@ -72,6 +75,9 @@ def _load():
     L.moe_ffn_workspace_bytes.restype = sz
     L.moe_expert_ffn_decode.argtypes = [ctypes.POINTER(_Layer), vp, i32, ctypes.POINTER(_Routing),
                                         vp, vp, sz, ctypes.POINTER(_Debug), vp]
+    L.moe_expert_ffn_decode_stages.argtypes = [
+        ctypes.POINTER(_Layer), vp, i32, ctypes.POINTER(_Routing), vp, vp, sz,
+        ctypes.POINTER(_Debug), ctypes.c_uint, vp]
     L.moe_expert_ffn_prefill.argtypes = [ctypes.POINTER(_Layer), vp, i32, ctypes.POINTER(_Routing),
                                          vp, vp, sz, vp]
     return L
@@ -178,8 +184,10 @@ def debug_buffers(layer: Layer, n: int, device="cuda") -> dict:
 
 
 def ffn_decode(layer: Layer, x: torch.Tensor, routing: Routing, residual: torch.Tensor,
-               ws: torch.Tensor | None = None, debug: dict | None = None, stream=None) -> None:
-    """moe_expert_ffn_decode: residual += routing-weighted expert outputs (in place)."""
+               ws: torch.Tensor | None = None, debug: dict | None = None, stream=None,
+               stages: int | None = None) -> None:
+    """moe_expert_ffn_decode: residual += routing-weighted expert outputs (in place).
+    With `stages` (DECODE_* bits) the call goes through moe_expert_ffn_decode_stages."""
     n = x.shape[0]
     if ws is None:
         ws = workspace(layer, n, device=x.device)
@@ -187,10 +195,17 @@ def ffn_decode(layer: Layer, x: torch.Tensor, routing: Routing, residual: torch.
     dbg = None
     if debug is not None:
         dbg = ctypes.byref(_Debug(**{k_: _ptr(debug.get(k_)) for k_ in DEBUG_FIELDS}))
-    rc = lib.moe_expert_ffn_decode(ctypes.byref(st), _ptr(x), n, ctypes.byref(rs), _ptr(residual),
-                                   _ptr(ws), ws.numel(), dbg, _stream(stream))
+    if stages is None:
+        rc = lib.moe_expert_ffn_decode(ctypes.byref(st), _ptr(x), n, ctypes.byref(rs),
+                                       _ptr(residual), _ptr(ws), ws.numel(), dbg, _stream(stream))
+        fn = "moe_expert_ffn_decode"
+    else:
+        rc = lib.moe_expert_ffn_decode_stages(ctypes.byref(st), _ptr(x), n, ctypes.byref(rs),
+                                              _ptr(residual), _ptr(ws), ws.numel(), dbg, stages,
+                                              _stream(stream))
+        fn = "moe_expert_ffn_decode_stages"
     if rc != MOE_OK:
-        raise MoeError("moe_expert_ffn_decode", rc)
+        raise MoeError(fn, rc)
 
 
 def ffn_prefill(layer: Layer, x_bf16: torch.Tensor, routing: Routing, residual: torch.Tensor,
