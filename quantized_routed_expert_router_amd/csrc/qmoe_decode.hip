@@ -63,9 +63,10 @@ __device__ __forceinline__ float quant_block32(const float (&v)[32], int (&q)[32
 
 template <int BITS>
 __global__ __launch_bounds__(kThreads) void k_prep(
-    const float* __restrict__ x, int n, int d, const int32_t* __restrict__ offsets, int E, int npc,
-    int4* __restrict__ chunks, int* __restrict__ nchunks, int8_t* __restrict__ xq,
-    double2* __restrict__ xsc, int8_t* __restrict__ dbg_xq, float* __restrict__ dbg_xs) {
+    const float* __restrict__ x, int n, int d, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ pair_index, int E, int k, int npc, int* __restrict__ chunks,
+    int* __restrict__ nchunks, int8_t* __restrict__ xq, double2* __restrict__ xsc,
+    int8_t* __restrict__ dbg_xq, float* __restrict__ dbg_xs) {
   if (blockIdx.x == 0) {
     // work list: expert e with c pairs contributes ceil(c/npc) chunks, in expert order
     __shared__ int s_wsum[kWaves];
@@ -95,8 +96,19 @@ __global__ __launch_bounds__(kThreads) void k_prep(
       const int e = tid * per + i;
       if (e < E) {
         const int beg = offsets[e], c = offsets[e + 1] - beg;
-        for (int j = 0; j < cnt[i]; ++j)
-          chunks[base + j] = make_int4(e, beg + j * npc, min(npc, c - j * npc), 0);
+        for (int j = 0; j < cnt[i]; ++j) {
+          int* rec = chunks + (size_t)(base + j) * kChunkInts;
+          const int first = beg + j * npc, np = min(npc, c - j * npc);
+          rec[0] = e;
+          rec[1] = first;
+          rec[2] = np;
+          rec[3] = 0;
+          for (int q = 0; q < kMaxChunkPairs; ++q) {
+            const int p = pair_index[first + min(q, np - 1)];
+            rec[4 + q] = p;
+            rec[4 + kMaxChunkPairs + q] = p / k;
+          }
+        }
       }
       base += cnt[i];
     }
@@ -141,33 +153,36 @@ __global__ __launch_bounds__(kThreads) void k_prep(
 
 // ---------------------------------------------------------------- streaming block loads
 
+// One packed block (16 B at 4 bits, 8 B at 2 bits) through a buffer resource.
 template <int BITS>
 struct BlockLoad;
 template <>
 struct BlockLoad<4> {
-  __device__ static __forceinline__ void load(const uint32_t* p, uint32_t (&w)[4]) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    w[0] = v.x;
-    w[1] = v.y;
-    w[2] = v.z;
-    w[3] = v.w;
+  __device__ static __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int voff, int soff,
+                                              uint32_t (&w)[4]) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+    w[0] = v[0];
+    w[1] = v[1];
+    w[2] = v[2];
+    w[3] = v[3];
   }
 };
 template <>
 struct BlockLoad<2> {
-  __device__ static __forceinline__ void load(const uint32_t* p, uint32_t (&w)[2]) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    w[0] = v.x;
-    w[1] = v.y;
+  __device__ static __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int voff, int soff,
+                                              uint32_t (&w)[2]) {
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+    w[0] = v[0];
+    w[1] = v[1];
   }
 };
 
-// Sum the four waves' partial row sums in wave order (deterministic).
-template <int NPC>
+// Sum the waves' partial row sums in wave order (deterministic).
+template <int NPC, int NW>
 __device__ __forceinline__ double reduce_waves(double (*red)[NPC][kWave], int j, int lane) {
   double s = red[0][j][lane];
 #pragma unroll
-  for (int w = 1; w < kWaves; ++w) s += red[w][j][lane];
+  for (int w = 1; w < NW; ++w) s += red[w][j][lane];
   return s;
 }
 
@@ -198,77 +213,199 @@ __device__ __forceinline__ int quant_half_wave(float h, float& scale, int& sum) 
 
 // ---------------------------------------------------------------- gate/up + SwiGLU + h quant
 
+// A workgroup of kGuWaves waves takes one item = (chunk of pairs of one expert, 64 rows).
+// Waves 0..3 stream the gate matrix and waves 4..7 the up matrix; wave w covers the
+// reduction blocks w%4, w%4+4, ... in groups of kUnroll and issues all loads of a group
+// (codes and scale/min) as soon as the item's expert is known. The chunk's activation
+// codes and scales are staged in LDS and read back with wave-uniform addresses.
+constexpr int kGuWaves = 8;
+constexpr int kGuThreads = kGuWaves * kWave;
+constexpr int kGuKWaves = kGuWaves / 2;  // waves per matrix
+// blocks in flight per wave: fewer when the chunk holds more pairs (more accumulators)
+template <int NPC>
+struct Unroll {
+  static constexpr int value = 8;
+};
+
+// Activation staging straight into LDS with global_load_lds_dwordx4: each wave-level load
+// writes 64 consecutive 16-byte entries of s_act[j][bb][part] (part 0/1: the two halves of
+// a block's 32 codes, part 2: (scale, scale*sum)), without passing through registers. The
+// loads are issued before the weight loads; since vector loads complete in order, a wave
+// then waits for them with vmcnt(number of weight loads issued after them), which leaves
+// the weight loads in flight, and a workgroup barrier publishes the staged data.
+template <int NPC, int G, int NT>
+struct ActLds {
+  static constexpr int kTotal = NPC * G * 3;               // 16-byte entries used
+  static constexpr int kIter = (kTotal + NT - 1) / NT;     // wave-level loads per wave
+  static constexpr int kPadded = kIter * NT;               // entries allocated
+};
+
+template <int NPC, int G, int NT>
+__device__ __forceinline__ void act_load_lds(int4* s_act, const int8_t* __restrict__ act,
+                                             const double2* __restrict__ sc,
+                                             const int* __restrict__ rows, int np, int g0, int nb,
+                                             int rowlen, int wave, int lane) {
+  constexpr int kTotal = ActLds<NPC, G, NT>::kTotal;
+  static_assert((G * 3) % kWave == 0, "a wave-level load stays within one pair's entries");
+  // Every wave issues kIter loads with no branch (a branch would make the compiler wait for
+  // the first load before issuing the next); loads past kTotal fill the padding.
+#pragma unroll
+  for (int it = 0; it < ActLds<NPC, G, NT>::kIter; ++it) {
+    const int wbase = it * NT + wave * kWave;  // wave-uniform
+    const int src_base = min(wbase, kTotal - kWave);
+    // the pair is uniform across the wave: its activation row is a scalar load from the
+    // chunk's work record (rows[0..np))
+    const int jc = min(src_base / (G * 3), np - 1);
+    const int rj = load_uniform(rows + jc);
+    const int rem = src_base % (G * 3) + lane;
+    const int bb = rem / 3, part = rem % 3;
+    const int b = min(g0 + bb, nb - 1);
+    const uintptr_t a_codes =
+        reinterpret_cast<uintptr_t>(act + (size_t)rj * rowlen + 32 * b) + 16 * (part & 1);
+    const uintptr_t a_scale = reinterpret_cast<uintptr_t>(sc + (size_t)rj * nb + b);
+    typedef const __attribute__((address_space(1))) void* gptr_t;
+    typedef __attribute__((address_space(3))) void* lptr_t;
+    __builtin_amdgcn_global_load_lds((gptr_t)(part < 2 ? a_codes : a_scale),
+                                     (lptr_t)(s_act + wbase), 16, 0, 0);
+  }
+}
+
+// Workgroup barrier that publishes LDS written by global_load_lds: the caller has already
+// waited (wait_vmcnt) for its own staging loads, so no release fence (which would also wait
+// for the weight loads still in flight) is placed before the barrier.
+__device__ __forceinline__ void barrier_after_lds_dma() {
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt with only the vector-memory count limited to `vm` (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 template <int BITS, int NPC, bool DBG>
-__global__ __launch_bounds__(kThreads) void k_gateup(
+__global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gateup(
     const uint32_t* __restrict__ gcodes, const uint32_t* __restrict__ gsm,
-    const uint32_t* __restrict__ ucodes, const uint32_t* __restrict__ usm, int d, int f, int k,
-    const int4* __restrict__ chunks, const int* __restrict__ nchunks,
-    const int32_t* __restrict__ pair_index, const int8_t* __restrict__ xq,
+    const uint32_t* __restrict__ ucodes, const uint32_t* __restrict__ usm, int d, int f,
+    const int* __restrict__ chunks, const int* __restrict__ nchunks, const int8_t* __restrict__ xq,
     const double2* __restrict__ xsc, int8_t* __restrict__ hq, double2* __restrict__ hsc,
     DecodeDebug dbg) {
-  __shared__ double red_g[kWaves][NPC][kWave];
-  __shared__ double red_u[kWaves][NPC][kWave];
+  constexpr int kUnroll = Unroll<NPC>::value;
+  constexpr int kGroup = kGuKWaves * kUnroll;  // blocks per weight-load group
+  constexpr int kStage = 2 * kGroup;           // blocks per activation staging
+  __shared__ double red[kGuWaves][NPC][kWave];
+  __shared__ int4 s_act_raw[ActLds<NPC, kStage, kGuThreads>::kPadded];
+  int4 (*s_act)[kStage][3] = reinterpret_cast<int4 (*)[kStage][3]>(s_act_raw);
   const int nbd = d / 32, nbf = f / 32;
   const int ntiles = (f + kWave - 1) / kWave;
-  const int nitems = *nchunks * ntiles;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int4 ch = chunks[item / ntiles];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int mat = wave / kGuKWaves;  // 0: gate, 1: up
+  const int kw = wave % kGuKWaves;
+  const uint32_t* __restrict__ codes = mat ? ucodes : gcodes;
+  const uint32_t* __restrict__ smp = mat ? usm : gsm;
+  // One scalar load of a chunk's work record gives expert, pair and token ids. The grid
+  // never exceeds max_chunks * ntiles, so the first record is inside the work-list buffer.
+  int item = blockIdx.x;
+  const int nitems = load_uniform(nchunks) * ntiles;
+  int e, np, pid[NPC], tok[NPC];
+  const int* rec_rows;  // token ids of the chunk's pairs (activation rows)
+  auto read_record = [&](int it) {
+    const int* rec = chunks + (size_t)(it / ntiles) * kChunkInts;
+    rec_rows = rec + 4 + kMaxChunkPairs;
+    e = load_uniform(rec);
+    np = load_uniform(rec + 2);
+#pragma unroll
+    for (int j = 0; j < NPC; ++j) {
+      pid[j] = load_uniform(rec + 4 + j);
+      tok[j] = load_uniform(rec + 4 + kMaxChunkPairs + j);
+    }
+  };
+  read_record(item);
+  for (; item < nitems; item += gridDim.x) {
+    if (item != (int)blockIdx.x) read_record(item);
     const int tile = item % ntiles;
-    const int e = ch.x, pbeg = ch.y, np = ch.z;
     const int r = tile * kWave + lane;
     const bool rvalid = r < f;
     const int rr = rvalid ? r : 0;
-    int pid[NPC], tok[NPC];
+    double acc[NPC];
 #pragma unroll
-    for (int j = 0; j < NPC; ++j) {
-      pid[j] = j < np ? pair_index[pbeg + j] : 0;
-      tok[j] = pid[j] / k;
-    }
-    double ag[NPC], au[NPC];
+    for (int j = 0; j < NPC; ++j) acc[j] = 0.0;
+    // this expert's codes and scale/min of this matrix
+    const __amdgpu_buffer_rsrc_t rs_c =
+        buffer_rsrc(codes + (size_t)e * nbd * f * BITS, (uint32_t)(nbd * f * BITS * 4));
+    const __amdgpu_buffer_rsrc_t rs_s = buffer_rsrc(smp + (size_t)e * nbd * f, (uint32_t)(nbd * f * 4));
+    // activations are staged per super-group of kStage blocks, weights per group of kGroup
+    uint32_t w[kUnroll][BITS], smw[kUnroll];
+    auto load_weights = [&](int g0) {
 #pragma unroll
-    for (int j = 0; j < NPC; ++j) ag[j] = au[j] = 0.0;
-    for (int b = wave; b < nbd; b += kWaves) {
-      const size_t blk = ((size_t)e * nbd + b) * f + rr;
-      uint32_t gw[BITS], uw[BITS];
-      BlockLoad<BITS>::load(gcodes + blk * BITS, gw);
-      BlockLoad<BITS>::load(ucodes + blk * BITS, uw);
-      const uint32_t gsmw = gsm[blk], usmw = usm[blk];
-      const double gs = half_bits_to_double(gsmw & 0xffffu), gm = half_bits_to_double(gsmw >> 16);
-      const double us = half_bits_to_double(usmw & 0xffffu), um = half_bits_to_double(usmw >> 16);
+      for (int u = 0; u < kUnroll; ++u) {
+        // blocks past the end (partial last group) re-read the last block; never used
+        const int b = min(g0 + kw + kGuKWaves * u, nbd - 1);
+        BlockLoad<BITS>::load(rs_c, rr * BITS * 4, b * f * BITS * 4, w[u]);
+        smw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, rr * 4, b * f * 4, 0);
+      }
+    };
+    auto compute = [&](int g0, int s0) {
 #pragma unroll
-      for (int j = 0; j < NPC; ++j) {
-        if (j < np) {
-          const int* a = reinterpret_cast<const int*>(xq + (size_t)tok[j] * d + 32 * b);
-          const double2 sc = xsc[(size_t)tok[j] * nbd + b];
-          const int dg = block_dot<BITS>(gw, a);
-          const int du = block_dot<BITS>(uw, a);
-          ag[j] += (gs * sc.x) * (double)dg;
-          ag[j] += gm * sc.y;
-          au[j] += (us * sc.x) * (double)du;
-          au[j] += um * sc.y;
-          if (DBG && rvalid) {
-            if (dbg.gate_dots) dbg.gate_dots[((size_t)pid[j] * f + r) * nbd + b] = dg;
-            if (dbg.up_dots) dbg.up_dots[((size_t)pid[j] * f + r) * nbd + b] = du;
+      for (int u = 0; u < kUnroll; ++u) {
+        const int b = g0 + kw + kGuKWaves * u;
+        const int bb = b - s0;
+        if (b < nbd) {
+          const double sc_w = half_bits_to_double(smw[u] & 0xffffu);
+          const double mn_w = half_bits_to_double(smw[u] >> 16);
+#pragma unroll
+          for (int j = 0; j < NPC; ++j) {
+            if (j < np) {
+              const int4 a0 = s_act[j][bb][0], a1 = s_act[j][bb][1], scv = s_act[j][bb][2];
+              const int a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+              double2 sc;
+              __builtin_memcpy(&sc, &scv, 16);
+              const int dt = block_dot<BITS>(w[u], a);
+              acc[j] += (sc_w * sc.x) * (double)dt;
+              acc[j] += mn_w * sc.y;
+              if (DBG && rvalid) {
+                int32_t* dots = mat ? dbg.up_dots : dbg.gate_dots;
+                if (dots) dots[((size_t)pid[j] * f + r) * nbd + b] = dt;
+              }
+            }
           }
         }
       }
-    }
-#pragma unroll
-    for (int j = 0; j < NPC; ++j) {
-      if (j < np) {
-        red_g[wave][j][lane] = ag[j];
-        red_u[wave][j][lane] = au[j];
+    };
+    for (int s0 = 0; s0 < nbd; s0 += kStage) {
+      __syncthreads();  // earlier readers of s_act are done
+      act_load_lds<NPC, kStage, kGuThreads>(s_act_raw, xq, xsc, rec_rows, np, s0, nbd, d, wave, lane);
+      __builtin_amdgcn_sched_barrier(0);
+      load_weights(s0);  // issues exactly 2 * kUnroll vector loads
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<2 * kUnroll>();  // this wave's staging loads have landed
+      barrier_after_lds_dma();
+      compute(s0, s0);
+      for (int g0 = s0 + kGroup; g0 < min(nbd, s0 + kStage); g0 += kGroup) {
+        load_weights(g0);
+        compute(g0, s0);
       }
     }
+#pragma unroll
+    for (int j = 0; j < NPC; ++j)
+      if (j < np) red[wave][j][lane] = acc[j];
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
       for (int j = 0; j < NPC; ++j) {
         if (j < np) {
-          const double g = reduce_waves<NPC>(red_g, j, lane);
-          const double u = reduce_waves<NPC>(red_u, j, lane);
+          // sums over the four waves of each matrix, in wave order
+          double g = red[0][j][lane], u = red[kGuKWaves][j][lane];
+#pragma unroll
+          for (int w2 = 1; w2 < kGuKWaves; ++w2) {
+            g += red[w2][j][lane];
+            u += red[kGuKWaves + w2][j][lane];
+          }
           const double silu = g / (1.0 + exp(-g));
           const float h = rvalid ? (float)(silu * u) : 0.0f;
           float scale;
@@ -290,56 +427,104 @@ __global__ __launch_bounds__(kThreads) void k_gateup(
         }
       }
     }
-    __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------- down projection
 
+constexpr int kDnWaves = 4;
+constexpr int kDnThreads = kDnWaves * kWave;
+
 template <int BITS, int NPC, bool DBG>
-__global__ __launch_bounds__(kThreads) void k_down(
+__global__ __launch_bounds__(kDnThreads) void k_down(
     const uint32_t* __restrict__ dcodes, const uint32_t* __restrict__ dsm, int d, int f,
-    const int4* __restrict__ chunks, const int* __restrict__ nchunks,
-    const int32_t* __restrict__ pair_index, const int8_t* __restrict__ hq,
+    const int* __restrict__ chunks, const int* __restrict__ nchunks, const int8_t* __restrict__ hq,
     const double2* __restrict__ hsc, double* __restrict__ y, DecodeDebug dbg) {
-  __shared__ double red[kWaves][NPC][kWave];
+  constexpr int kUnroll = 8;
+  constexpr int kDnGroup = kDnWaves * kUnroll;  // blocks per weight-load group
+  constexpr int kDnStage = 2 * kDnGroup;        // blocks per activation staging
+  __shared__ double red[kDnWaves][NPC][kWave];
+  __shared__ int4 s_act_raw[ActLds<NPC, kDnStage, kDnThreads>::kPadded];
+  int4 (*s_act)[kDnStage][3] = reinterpret_cast<int4 (*)[kDnStage][3]>(s_act_raw);
   const int nbf = f / 32;
   const int ntiles = (d + kWave - 1) / kWave;
-  const int nitems = *nchunks * ntiles;
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  for (int item = blockIdx.x; item < nitems; item += gridDim.x) {
-    const int4 ch = chunks[item / ntiles];
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  int item = blockIdx.x;  // first record read with the count: see k_gateup
+  const int nitems = load_uniform(nchunks) * ntiles;
+  int e, np, pid[NPC];
+  const int* rec_rows;  // pair ids of the chunk (rows of hq)
+  auto read_record = [&](int it) {
+    const int* rec = chunks + (size_t)(it / ntiles) * kChunkInts;
+    rec_rows = rec + 4;
+    e = load_uniform(rec);
+    np = load_uniform(rec + 2);
+#pragma unroll
+    for (int j = 0; j < NPC; ++j) pid[j] = load_uniform(rec + 4 + j);
+  };
+  read_record(item);
+  for (; item < nitems; item += gridDim.x) {
+    if (item != (int)blockIdx.x) read_record(item);
     const int tile = item % ntiles;
-    const int e = ch.x, pbeg = ch.y, np = ch.z;
     const int r = tile * kWave + lane;
     const bool rvalid = r < d;
     const int rr = rvalid ? r : 0;
-    int pid[NPC];
-#pragma unroll
-    for (int j = 0; j < NPC; ++j) pid[j] = j < np ? pair_index[pbeg + j] : 0;
     double ay[NPC];
 #pragma unroll
     for (int j = 0; j < NPC; ++j) ay[j] = 0.0;
-    for (int b = wave; b < nbf; b += kWaves) {
-      const size_t blk = ((size_t)e * nbf + b) * d + rr;
-      uint32_t dw[BITS];
-      BlockLoad<BITS>::load(dcodes + blk * BITS, dw);
-      const uint32_t smw = dsm[blk];
-      const double s = half_bits_to_double(smw & 0xffffu), m = half_bits_to_double(smw >> 16);
+    const __amdgpu_buffer_rsrc_t rs_c =
+        buffer_rsrc(dcodes + (size_t)e * nbf * d * BITS, (uint32_t)(nbf * d * BITS * 4));
+    const __amdgpu_buffer_rsrc_t rs_s = buffer_rsrc(dsm + (size_t)e * nbf * d, (uint32_t)(nbf * d * 4));
+    uint32_t dw[kUnroll][BITS], smw[kUnroll];
+    auto load_weights = [&](int g0) {
 #pragma unroll
-      for (int j = 0; j < NPC; ++j) {
-        if (j < np) {
-          const int* a = reinterpret_cast<const int*>(hq + (size_t)pid[j] * f + 32 * b);
-          const double2 sc = hsc[(size_t)pid[j] * nbf + b];
-          const int dd = block_dot<BITS>(dw, a);
-          ay[j] += (s * sc.x) * (double)dd;
-          ay[j] += m * sc.y;
-          if (DBG && rvalid && dbg.down_dots)
-            dbg.down_dots[((size_t)pid[j] * d + r) * nbf + b] = dd;
+      for (int u = 0; u < kUnroll; ++u) {
+        const int b = min(g0 + wave + kDnWaves * u, nbf - 1);  // see k_gateup
+        BlockLoad<BITS>::load(rs_c, rr * BITS * 4, b * d * BITS * 4, dw[u]);
+        smw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, rr * 4, b * d * 4, 0);
+      }
+    };
+    auto compute = [&](int g0, int s0) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int b = g0 + wave + kDnWaves * u;
+        const int bb = b - s0;
+        if (b < nbf) {
+          const double s = half_bits_to_double(smw[u] & 0xffffu);
+          const double m = half_bits_to_double(smw[u] >> 16);
+#pragma unroll
+          for (int j = 0; j < NPC; ++j) {
+            if (j < np) {
+              const int4 a0 = s_act[j][bb][0], a1 = s_act[j][bb][1], scv = s_act[j][bb][2];
+              const int a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+              double2 sc;
+              __builtin_memcpy(&sc, &scv, 16);
+              const int dd = block_dot<BITS>(dw[u], a);
+              ay[j] += (s * sc.x) * (double)dd;
+              ay[j] += m * sc.y;
+              if (DBG && rvalid && dbg.down_dots)
+                dbg.down_dots[((size_t)pid[j] * d + r) * nbf + b] = dd;
+            }
+          }
         }
       }
+    };
+    for (int s0 = 0; s0 < nbf; s0 += kDnStage) {
+      __syncthreads();  // earlier readers of s_act are done
+      act_load_lds<NPC, kDnStage, kDnThreads>(s_act_raw, hq, hsc, rec_rows, np, s0, nbf, f, wave, lane);
+      __builtin_amdgcn_sched_barrier(0);  // see k_gateup
+      load_weights(s0);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<2 * kUnroll>();
+      barrier_after_lds_dma();
+      compute(s0, s0);
+      for (int g0 = s0 + kDnGroup; g0 < min(nbf, s0 + kDnStage); g0 += kDnGroup) {
+        load_weights(g0);
+        compute(g0, s0);
+      }
     }
+    __syncthreads();
 #pragma unroll
     for (int j = 0; j < NPC; ++j)
       if (j < np) red[wave][j][lane] = ay[j];
@@ -348,13 +533,12 @@ __global__ __launch_bounds__(kThreads) void k_down(
 #pragma unroll
       for (int j = 0; j < NPC; ++j) {
         if (j < np && rvalid) {
-          const double v = reduce_waves<NPC>(red, j, lane);
+          const double v = reduce_waves<NPC, kDnWaves>(red, j, lane);
           y[(size_t)pid[j] * d + r] = v;
           if (DBG && dbg.y) dbg.y[(size_t)pid[j] * d + r] = (float)v;
         }
       }
     }
-    __syncthreads();
   }
 }
 
@@ -379,7 +563,7 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   const moe_layer& L = *a.L;
   const int n = a.n, d = L.d_model, f = L.d_ff, k = L.top_k, E = L.n_experts;
   const DecodeWs W = decode_ws_layout(n, k, d, f);
-  int4* chunks = reinterpret_cast<int4*>(a.ws + W.chunks);
+  int* chunks = reinterpret_cast<int*>(a.ws + W.chunks);
   int* nchunks = reinterpret_cast<int*>(a.ws + W.nchunks);
   int8_t* xq = reinterpret_cast<int8_t*>(a.ws + W.xq);
   double2* xsc = reinterpret_cast<double2*>(a.ws + W.xsc);
@@ -394,8 +578,8 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   if (a.stages & MOE_DECODE_PREP) {
     const int prep_blocks = 1 + (n * nbd + kThreads - 1) / kThreads;
     hipLaunchKernelGGL(k_prep<BITS>, dim3(prep_blocks), dim3(kThreads), 0, a.stream, a.x, n, d,
-                       a.r->expert_offsets, E, NPC, chunks, nchunks, xq, xsc,
-                       DBG ? dbg.xq : nullptr, DBG ? dbg.xs : nullptr);
+                       a.r->expert_offsets, a.r->pair_index, E, k, NPC, chunks, nchunks, xq,
+                       xsc, DBG ? dbg.xq : nullptr, DBG ? dbg.xs : nullptr);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -407,19 +591,19 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   if (a.stages & MOE_DECODE_GATE_UP) {
     const long long gu_items = max_chunks * ((f + kWave - 1) / kWave);
     const int gu_grid = (int)std::max<long long>(1, std::min<long long>(gu_items, cap));
-    hipLaunchKernelGGL((k_gateup<BITS, NPC, DBG>), dim3(gu_grid), dim3(kThreads), 0, a.stream,
+    hipLaunchKernelGGL((k_gateup<BITS, NPC, DBG>), dim3(gu_grid), dim3(kGuThreads), 0, a.stream,
                        L.gate.codes, reinterpret_cast<const uint32_t*>(L.gate.scale_min),
-                       L.up.codes, reinterpret_cast<const uint32_t*>(L.up.scale_min), d, f, k,
-                       chunks, nchunks, a.r->pair_index, xq, xsc, hq, hsc, dbg);
+                       L.up.codes, reinterpret_cast<const uint32_t*>(L.up.scale_min), d, f,
+                       chunks, nchunks, xq, xsc, hq, hsc, dbg);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (a.stages & MOE_DECODE_DOWN) {
     const long long dn_items = max_chunks * ((d + kWave - 1) / kWave);
     const int dn_grid = (int)std::max<long long>(1, std::min<long long>(dn_items, cap));
-    hipLaunchKernelGGL((k_down<BITS, NPC, DBG>), dim3(dn_grid), dim3(kThreads), 0, a.stream,
+    hipLaunchKernelGGL((k_down<BITS, NPC, DBG>), dim3(dn_grid), dim3(kDnThreads), 0, a.stream,
                        L.down.codes, reinterpret_cast<const uint32_t*>(L.down.scale_min), d, f,
-                       chunks, nchunks, a.r->pair_index, hq, hsc, y, dbg);
+                       chunks, nchunks, hq, hsc, y, dbg);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

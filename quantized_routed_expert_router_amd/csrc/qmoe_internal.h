@@ -28,6 +28,31 @@ __device__ __forceinline__ float half_bits_to_float(uint32_t bits16) {
   return (float)h;
 }
 
+// Load through the constant address space: a wave-uniform address then becomes a scalar
+// load (SGPR result, its own wait counter), used for work-list and pair-list reads of data
+// written by an earlier kernel launch.
+__device__ __forceinline__ int load_uniform(const int* p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  return *reinterpret_cast<const __attribute__((address_space(4))) int*>(
+      reinterpret_cast<uintptr_t>(p));
+#else
+  return *p;
+#endif
+}
+
+__device__ __forceinline__ int4 load_uniform(const int4* p) {
+  const int* q = reinterpret_cast<const int*>(p);
+  return make_int4(load_uniform(q), load_uniform(q + 1), load_uniform(q + 2), load_uniform(q + 3));
+}
+
+// Raw buffer resource over `bytes` bytes at `base` (gfx9 descriptor word 3). Loads through
+// it take one VGPR offset per lane plus a wave-uniform SGPR offset, so the many loads a
+// wave keeps in flight share one address register; reads past `bytes` return zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
 // Signed 8-bit dot product of 4 byte lanes, accumulated into c (v_dot4c_i32_i8).
 __device__ __forceinline__ int dot4_i8(int a, int b, int c) {
   return __builtin_amdgcn_sdot4(a, b, c, false);
@@ -74,8 +99,14 @@ __device__ __forceinline__ int block_dot(const uint32_t (&w)[BITS], const int* a
 
 __host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
+// Work record of one chunk (up to kMaxChunkPairs pairs of one expert), 128 bytes:
+// [0] expert, [1] first pair position in pair_index, [2] pair count np, [3] unused,
+// [4..12) pair ids p, [12..20) token ids p / k (entries >= np repeat entry np-1).
+constexpr int kMaxChunkPairs = 8;
+constexpr int kChunkInts = 32;
+
 struct DecodeWs {
-  size_t chunks;   // int4 [n*k]   (expert, first pair, pair count, 0)
+  size_t chunks;   // int [n*k][kChunkInts] work records
   size_t nchunks;  // int  [1]
   size_t xq;       // int8 [n][d]  permuted activation codes
   size_t xsc;      // double2 [n][d/32]   (scale, scale*sum of codes)
@@ -90,7 +121,7 @@ inline DecodeWs decode_ws_layout(int n, int k, int d, int f) {
   size_t o = 0;
   const size_t P = (size_t)n * k;
   L.chunks = o;
-  o = align256(o + 16 * (P + 1));
+  o = align256(o + sizeof(int) * kChunkInts * (P + 1));
   L.nchunks = o;
   o = align256(o + 16);
   L.xq = o;
