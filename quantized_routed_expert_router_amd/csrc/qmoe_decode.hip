@@ -17,7 +17,9 @@
 //               row sums round only in the additions. The workgroup then applies SwiGLU
 //               and quantizes h per 32 rows (two halves of a wave) to int8.
 //   k_down      the same streaming scheme over the down projection's d rows.
-//   k_combine   residual[t] += sum_j w[t][j] * y[t*k+j] in slot order, binary64.
+//   k_combine   residual[t] += sum_j w[t][j] * y[t*k+j] in slot order, binary64. (Folding
+//               it into k_down with a last-arriver counter needs device-scope fences, which
+//               write back the XCD's L2 and cost far more than this small launch.)
 //
 // Every expert's weights are read once per chunk of up to NPC pairs; at n <= NPC tokens
 // (the T = 4 window) every touched expert is read exactly once per call.
@@ -61,26 +63,26 @@ __device__ __forceinline__ float quant_block32(const float (&v)[32], int (&q)[32
 
 // ---------------------------------------------------------------- prep: x quant + work list
 
+constexpr int kPrepThreads = 1024;  // block 0: one thread per expert (E <= 1024)
+constexpr int kPrepWaves = kPrepThreads / kWave;
+
 template <int BITS>
-__global__ __launch_bounds__(kThreads) void k_prep(
+__global__ __launch_bounds__(kPrepThreads) void k_prep(
     const float* __restrict__ x, int n, int d, const int32_t* __restrict__ offsets,
     const int32_t* __restrict__ pair_index, int E, int k, int npc, int* __restrict__ chunks,
-    int* __restrict__ nchunks, int8_t* __restrict__ xq, double2* __restrict__ xsc,
-    int8_t* __restrict__ dbg_xq, float* __restrict__ dbg_xs) {
+    int* __restrict__ nchunks, int8_t* __restrict__ xq,
+    double2* __restrict__ xsc, int8_t* __restrict__ dbg_xq, float* __restrict__ dbg_xs) {
+  const int tid = threadIdx.x;
   if (blockIdx.x == 0) {
-    // work list: expert e with c pairs contributes ceil(c/npc) chunks, in expert order
-    __shared__ int s_wsum[kWaves];
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
-    constexpr int per = MOE_MAX_EXPERTS / kThreads;  // experts per thread (4)
-    int cnt[per], sum = 0;
-#pragma unroll
-    for (int i = 0; i < per; ++i) {
-      const int e = tid * per + i;
-      const int c = e < E ? offsets[e + 1] - offsets[e] : 0;
-      cnt[i] = (c + npc - 1) / npc;
-      sum += cnt[i];
-    }
-    int incl = sum;
+    // work list: expert e with c pairs contributes ceil(c/npc) chunk records, in expert
+    // order
+    __shared__ int s_wsum[kPrepWaves];
+    const int lane = tid & (kWave - 1), wave = tid / kWave;
+    const int e = tid;
+    const int beg = e < E ? offsets[e] : 0;
+    const int c = e < E ? offsets[e + 1] - beg : 0;
+    const int cnt = (c + npc - 1) / npc;
+    int incl = cnt;
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
       const int o = __shfl_up(incl, off);
@@ -88,35 +90,29 @@ __global__ __launch_bounds__(kThreads) void k_prep(
     }
     if (lane == kWave - 1) s_wsum[wave] = incl;
     __syncthreads();
-    int base = 0;
+    int base = incl - cnt;
     for (int w = 0; w < wave; ++w) base += s_wsum[w];
-    base += incl - sum;
+    for (int j = 0; j < cnt; ++j) {
+      int* rec = chunks + (size_t)(base + j) * kChunkInts;
+      const int first = beg + j * npc, np = min(npc, c - j * npc);
+      int p[kMaxChunkPairs];
 #pragma unroll
-    for (int i = 0; i < per; ++i) {
-      const int e = tid * per + i;
-      if (e < E) {
-        const int beg = offsets[e], c = offsets[e + 1] - beg;
-        for (int j = 0; j < cnt[i]; ++j) {
-          int* rec = chunks + (size_t)(base + j) * kChunkInts;
-          const int first = beg + j * npc, np = min(npc, c - j * npc);
-          rec[0] = e;
-          rec[1] = first;
-          rec[2] = np;
-          rec[3] = 0;
-          for (int q = 0; q < kMaxChunkPairs; ++q) {
-            const int p = pair_index[first + min(q, np - 1)];
-            rec[4 + q] = p;
-            rec[4 + kMaxChunkPairs + q] = p / k;
-          }
-        }
+      for (int q = 0; q < kMaxChunkPairs; ++q) p[q] = pair_index[first + min(q, np - 1)];
+      rec[0] = e;
+      rec[1] = first;
+      rec[2] = np;
+      rec[3] = 0;
+#pragma unroll
+      for (int q = 0; q < kMaxChunkPairs; ++q) {
+        rec[4 + q] = p[q];
+        rec[4 + kMaxChunkPairs + q] = p[q] / k;
       }
-      base += cnt[i];
     }
-    if (tid == kThreads - 1) *nchunks = base;
+    if (tid == kPrepThreads - 1) *nchunks = base + cnt;
     return;
   }
   const int nbd = d / 32;
-  const int gid = (blockIdx.x - 1) * kThreads + threadIdx.x;
+  const int gid = (blockIdx.x - 1) * kPrepThreads + tid;
   if (gid >= n * nbd) return;
   const int t = gid / nbd, b = gid % nbd;
   float v[32];
@@ -576,9 +572,9 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   const int nbd = d / 32;
   hipError_t err = hipSuccess;
   if (a.stages & MOE_DECODE_PREP) {
-    const int prep_blocks = 1 + (n * nbd + kThreads - 1) / kThreads;
-    hipLaunchKernelGGL(k_prep<BITS>, dim3(prep_blocks), dim3(kThreads), 0, a.stream, a.x, n, d,
-                       a.r->expert_offsets, a.r->pair_index, E, k, NPC, chunks, nchunks, xq,
+    const int prep_blocks = 1 + (n * nbd + kPrepThreads - 1) / kPrepThreads;
+    hipLaunchKernelGGL(k_prep<BITS>, dim3(prep_blocks), dim3(kPrepThreads), 0, a.stream, a.x, n,
+                       d, a.r->expert_offsets, a.r->pair_index, E, k, NPC, chunks, nchunks, xq,
                        xsc, DBG ? dbg.xq : nullptr, DBG ? dbg.xs : nullptr);
     err = hipGetLastError();
     if (err != hipSuccess) return err;

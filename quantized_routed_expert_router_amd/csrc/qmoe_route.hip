@@ -36,10 +36,47 @@ __device__ __forceinline__ uint64_t make_key(float logit, int e) {
   return ((uint64_t)order_bits(logit) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e);
 }
 
+// 64-bit DPP move within a wavefront; lanes whose source is invalid or masked off by
+// row_mask keep their own value.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+  const uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+  const uint32_t lo2 = __builtin_amdgcn_update_dpp(lo, lo, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t hi2 = __builtin_amdgcn_update_dpp(hi, hi, CTRL, ROW_MASK, 0xF, false);
+  return ((uint64_t)hi2 << 32) | lo2;
+}
+
+__device__ __forceinline__ uint64_t max_u64(uint64_t a, uint64_t b) { return a > b ? a : b; }
+
+// Maximum of a 64-bit value over the wavefront, returned wave-uniform: DPP steps reduce
+// within quads, 8- and 16-lane rows, then across rows (row_bcast15/31) into lane 63.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+  v = max_u64(v, dpp_u64<0xB1, 0xF>(v));   // quad_perm [1,0,3,2]
+  v = max_u64(v, dpp_u64<0x4E, 0xF>(v));   // quad_perm [2,3,0,1]
+  v = max_u64(v, dpp_u64<0x141, 0xF>(v));  // row_half_mirror
+  v = max_u64(v, dpp_u64<0x140, 0xF>(v));  // row_mirror
+  v = max_u64(v, dpp_u64<0x142, 0xA>(v));  // row_bcast:15
+  v = max_u64(v, dpp_u64<0x143, 0xC>(v));  // row_bcast:31
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)v, kWave - 1);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(v >> 32), kWave - 1);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  uint64_t u;
+  __builtin_memcpy(&u, &v, 8);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), lane);
+  u = ((uint64_t)hi << 32) | lo;
+  double r;
+  __builtin_memcpy(&r, &u, 8);
+  return r;
+}
+
 // Top-k of one token by one full wavefront; lane j < k writes slot j.
 template <int KPL>
-__device__ void wave_topk(const float* __restrict__ lrow, int E, int k, int32_t* __restrict__ ids,
-                          float* __restrict__ w) {
+__device__ int wave_topk(const float* __restrict__ lrow, int E, int k, int32_t* __restrict__ ids,
+                         float* __restrict__ w) {
   const int lane = threadIdx.x & (kWave - 1);
   uint64_t key[KPL];
 #pragma unroll
@@ -52,12 +89,8 @@ __device__ void wave_topk(const float* __restrict__ lrow, int E, int k, int32_t*
   for (int j = 0; j < k; ++j) {
     uint64_t best = key[0];
 #pragma unroll
-    for (int i = 1; i < KPL; ++i) best = key[i] > best ? key[i] : best;
-#pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) {
-      const uint64_t o = __shfl_xor(best, off);
-      best = o > best ? o : best;
-    }
+    for (int i = 1; i < KPL; ++i) best = max_u64(best, key[i]);
+    best = wave_max_u64(best);
     const int e = (int)(0xffffffffu - (uint32_t)best);
 #pragma unroll
     for (int i = 0; i < KPL; ++i)
@@ -67,14 +100,15 @@ __device__ void wave_topk(const float* __restrict__ lrow, int E, int k, int32_t*
       my_l = order_bits_to_float((uint32_t)(best >> 32));
     }
   }
-  const double l0 = (double)__shfl(my_l, 0);
-  const double ex = lane < k ? exp((double)my_l - l0) : 0.0;
+  const float l0f = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(my_l)));
+  const double ex = lane < k ? exp((double)my_l - (double)l0f) : 0.0;
   double sum = 0.0;
-  for (int j = 0; j < k; ++j) sum += __shfl(ex, j);  // slot order
+  for (int j = 0; j < k; ++j) sum += readlane_f64(ex, j);  // slot order
   if (lane < k) {
     ids[lane] = my_id;
     w[lane] = (float)(ex / sum);
   }
+  return my_id;  // lane j < k: the expert of slot j
 }
 
 // Exclusive scan of v[0..n) (n <= 2*kGroupThreads) in LDS by a kGroupThreads block.
@@ -154,16 +188,51 @@ __device__ void group_block(const int32_t* ids, int P, int E, int32_t* __restric
   }
 }
 
+// Grouping for small batches (P = n*k <= kSmallPairs): with the pair ids in LDS, thread e
+// computes offsets[e] = #{q : ids[q] < e} and pair p lands at
+// #{q : ids[q] < ids[p]} + #{q < p : ids[q] == ids[p]}, the position a stable counting sort
+// gives it. O(P) LDS broadcasts per thread, no atomics and no scans.
+constexpr int kSmallPairs = 256;
+
+__device__ void group_small(const int* s_ids, int P, int E, int32_t* __restrict__ offsets,
+                            int32_t* __restrict__ pair_index) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e <= E; e += kGroupThreads) {
+    int c = 0;
+#pragma unroll 8
+    for (int q = 0; q < P; ++q) c += s_ids[q] < e;
+    offsets[e] = c;
+  }
+  for (int p = tid; p < P; p += kGroupThreads) {
+    const int ep = s_ids[p];
+    int pos = 0;
+#pragma unroll 8
+    for (int q = 0; q < P; ++q) {
+      const int eq = s_ids[q];
+      pos += (eq < ep) | ((eq == ep) & (q < p));
+    }
+    pair_index[pos] = p;
+  }
+}
+
 template <int KPL>
 __global__ __launch_bounds__(kGroupThreads) void k_route_fused(
     const float* __restrict__ logits, int n, int E, int k, int32_t* ids, float* __restrict__ w,
     int32_t* __restrict__ offsets, int32_t* __restrict__ pair_index) {
-  const int wave = threadIdx.x / kWave;
-  for (int t = wave; t < n; t += kGroupWaves)
-    wave_topk<KPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+  __shared__ int s_ids[kSmallPairs];
+  const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
+  const int P = n * k;
+  for (int t = wave; t < n; t += kGroupWaves) {
+    const int id = wave_topk<KPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k,
+                                  w + (size_t)t * k);
+    if (P <= kSmallPairs && lane < k) s_ids[t * k + lane] = id;
+  }
   __threadfence_block();
   __syncthreads();
-  group_block(ids, n * k, E, offsets, pair_index);
+  if (P <= kSmallPairs)
+    group_small(s_ids, P, E, offsets, pair_index);
+  else
+    group_block(ids, P, E, offsets, pair_index);
 }
 
 template <int KPL>
