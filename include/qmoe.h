@@ -179,12 +179,32 @@ moe_status moe_expert_ffn_decode_stages(const moe_layer* L, const float* x, int 
 /* Prefill-chunk expert FFN with bf16 arithmetic on the matrix cores: weights are
  * dequantized to bf16 (bf16 of fp32 scale*q + min), x_bf16: device bf16 bits [n][d];
  * gate/up accumulate in fp32; h = bf16(silu(g) * u); down accumulates in fp32;
- * residual (fp32 [n][d]) += routing-weighted sum. Only 4-bit weights. ws: at least
- * moe_ffn_workspace_bytes(L, n, 1) bytes, 256-byte aligned.
- * Limits: n <= MOE_MAX_PREFILL_TOKENS. */
+ * residual (fp32 [n][d]) += routing-weighted sum of the pair outputs (binary64 sum in
+ * slot order, rounded once). 4-bit and 2-bit weights. x_bf16 must be 16-byte aligned and
+ * must not overlap residual. r: routing from moe_route for the same n, E and k. ws: at
+ * least moe_ffn_workspace_bytes(L, n, 1) bytes, 256-byte aligned, no initialisation
+ * needed; it holds h (bf16 [n*k][f]) and the pair outputs (fp32 [n*k][d]).
+ * Limits: n <= MOE_MAX_PREFILL_TOKENS; n == 0 enqueues nothing. */
 moe_status moe_expert_ffn_prefill(const moe_layer* L, const uint16_t* x_bf16, int n_tokens,
                                   const moe_routing* r, float* residual, void* ws,
                                   size_t ws_bytes, void* stream);
+
+/* Stages of moe_expert_ffn_prefill, as bits of `stages` below. */
+#define MOE_PREFILL_PREP 1u     /* M-tile work list and token / grouped-position maps     */
+#define MOE_PREFILL_GATE_UP 2u  /* gate/up grouped GEMM with SwiGLU, h in bf16            */
+#define MOE_PREFILL_DOWN 4u     /* down grouped GEMM, fp32 pair outputs                   */
+#define MOE_PREFILL_COMBINE 8u  /* routing-weighted combine into the residual            */
+#define MOE_PREFILL_ALL 15u
+
+/* moe_expert_ffn_prefill split into its stages, with the same contract as
+ * moe_expert_ffn_decode_stages: the selected stages are enqueued in the order above and
+ * every stage of one layer call must be issued, in order, with the same arguments and
+ * workspace. stages == MOE_PREFILL_ALL is moe_expert_ffn_prefill.
+ * MOE_ERR_INVALID_ARGUMENT if stages is 0 or has bits outside MOE_PREFILL_ALL. */
+moe_status moe_expert_ffn_prefill_stages(const moe_layer* L, const uint16_t* x_bf16,
+                                         int n_tokens, const moe_routing* r, float* residual,
+                                         void* ws, size_t ws_bytes, unsigned stages,
+                                         void* stream);
 
 #ifdef __cplusplus
 }

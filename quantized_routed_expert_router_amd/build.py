@@ -34,7 +34,7 @@ COMMON_FLAGS = [
 ]
 
 LIBS = {
-    "libqmoe.so": ["qmoe.hip", "qmoe_route.hip", "qmoe_decode.hip"],
+    "libqmoe.so": ["qmoe.hip", "qmoe_route.hip", "qmoe_decode.hip", "qmoe_prefill.hip"],
     "libqmoe_synth.so": ["synth.hip"],
 }
 

@@ -111,7 +111,12 @@ size_t moe_ffn_workspace_bytes(const moe_layer* L, int n_tokens, int prefill) {
   if (!L || n_tokens < 0) return 0;
   const int d = L->d_model, f = L->d_ff, k = L->top_k;
   if (d <= 0 || f <= 0 || k <= 0) return 0;
-  if (prefill) return 0;
+  if (prefill) {
+    if (n_tokens > MOE_MAX_PREFILL_TOKENS) return 0;
+    const int E = L->n_experts;
+    if (E < 1 || E > MOE_MAX_EXPERTS) return 0;
+    return prefill_ws_layout(n_tokens, k, d, f, E).total;
+  }
   return decode_ws_layout(n_tokens, k, d, f).total;
 }
 
@@ -156,15 +161,33 @@ moe_status moe_expert_ffn_decode_stages(const moe_layer* L, const float* x, int 
 moe_status moe_expert_ffn_prefill(const moe_layer* L, const uint16_t* x_bf16, int n_tokens,
                                   const moe_routing* r, float* residual, void* ws,
                                   size_t ws_bytes, void* stream) {
-  (void)L;
-  (void)x_bf16;
-  (void)n_tokens;
-  (void)r;
-  (void)residual;
-  (void)ws;
-  (void)ws_bytes;
-  (void)stream;
-  return MOE_ERR_UNSUPPORTED;
+  return moe_expert_ffn_prefill_stages(L, x_bf16, n_tokens, r, residual, ws, ws_bytes,
+                                       MOE_PREFILL_ALL, stream);
+}
+
+moe_status moe_expert_ffn_prefill_stages(const moe_layer* L, const uint16_t* x_bf16,
+                                         int n_tokens, const moe_routing* r, float* residual,
+                                         void* ws, size_t ws_bytes, unsigned stages,
+                                         void* stream) {
+  if (stages == 0 || (stages & ~MOE_PREFILL_ALL)) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status s = check_layer(L);
+  if (s != MOE_OK) return s;
+  if (n_tokens < 0 || n_tokens > MOE_MAX_PREFILL_TOKENS) return MOE_ERR_INVALID_ARGUMENT;
+  if (n_tokens == 0) return MOE_OK;
+  if (check_routing(r) != MOE_OK) return MOE_ERR_INVALID_ARGUMENT;
+  if (!x_bf16 || !residual || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x_bf16, 16) || !aligned(residual, 4) || !aligned(ws, 256))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const size_t x_bytes = (size_t)n_tokens * L->d_model * sizeof(uint16_t);
+  const size_t res_bytes = (size_t)n_tokens * L->d_model * sizeof(float);
+  if (overlaps(x_bf16, x_bytes, residual, res_bytes)) return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = moe_ffn_workspace_bytes(L, n_tokens, 1);
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (overlaps(ws, need, residual, res_bytes) || overlaps(ws, need, x_bf16, x_bytes))
+    return MOE_ERR_INVALID_ARGUMENT;
+  PrefillArgs a{L, x_bf16, n_tokens, r, residual, (char*)ws, (hipStream_t)stream, stages};
+  const hipError_t err = launch_prefill(a);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
 }  // extern "C"

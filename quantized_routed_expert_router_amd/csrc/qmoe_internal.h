@@ -2,6 +2,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 #include <stddef.h>
 #include <stdint.h>
 #include <string.h>
@@ -138,6 +140,58 @@ inline DecodeWs decode_ws_layout(int n, int k, int d, int f) {
   return L;
 }
 
+// Prefill workspace. M-tiles hold up to kPrefillBM consecutive grouped pairs of one
+// expert; h and y are kept in grouped pair order.
+constexpr int kPrefillBM = 128;
+
+struct PrefillWs {
+  size_t tiles;     // int4 [max M-tiles] (expert, first grouped position, rows, 0)
+  size_t ntiles;    // int  [1]
+  size_t tok_of_g;  // int  [n*k] token of grouped position g
+  size_t g_of_p;    // int  [n*k] grouped position of pair p = t*k + j
+  size_t h;         // bf16 [n*k][f]
+  size_t y;         // fp32 [n*k][d]
+  size_t total;
+};
+
+// Upper bound of the number of M-tiles: sum over experts of ceil(m_e / BM) with
+// sum m_e = P and at most min(E, P) non-empty experts.
+inline int prefill_max_mtiles(int P, int E) {
+  const long long busy = std::min<long long>(E, P);
+  return (int)(((long long)P + busy * (kPrefillBM - 1)) / kPrefillBM);
+}
+
+inline PrefillWs prefill_ws_layout(int n, int k, int d, int f, int E) {
+  PrefillWs L;
+  size_t o = 0;
+  const size_t P = (size_t)n * k;
+  L.tiles = o;
+  o = align256(o + 16 * (size_t)(prefill_max_mtiles((int)P, E) + 1));
+  L.ntiles = o;
+  o = align256(o + 16);
+  L.tok_of_g = o;
+  o = align256(o + 4 * P);
+  L.g_of_p = o;
+  o = align256(o + 4 * P);
+  L.h = o;
+  o = align256(o + 2 * P * f);
+  L.y = o;
+  o = align256(o + 4 * P * d);
+  L.total = o;
+  return L;
+}
+
+struct PrefillArgs {
+  const moe_layer* L;
+  const uint16_t* x;
+  int n;
+  const moe_routing* r;
+  float* residual;
+  char* ws;
+  hipStream_t stream;
+  unsigned stages;  // MOE_PREFILL_* bits
+};
+
 struct DecodeDebug {
   int8_t* xq;
   float* xs;
@@ -170,6 +224,7 @@ struct DecodeArgs {
 hipError_t launch_route(const float* logits, int n, int E, int k, const moe_routing* out,
                         hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a);
+hipError_t launch_prefill(const PrefillArgs& a);
 
 int device_cu_count();
 

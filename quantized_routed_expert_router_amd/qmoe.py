@@ -26,9 +26,10 @@ MAX_PREFILL_TOKENS = 8192
 
 EXPORTS = ("moe_status_string", "moe_route_workspace_bytes", "moe_route",
            "moe_ffn_workspace_bytes", "moe_expert_ffn_decode", "moe_expert_ffn_decode_stages",
-           "moe_expert_ffn_prefill")
+           "moe_expert_ffn_prefill", "moe_expert_ffn_prefill_stages")
 
 DECODE_PREP, DECODE_GATE_UP, DECODE_DOWN, DECODE_COMBINE, DECODE_ALL = 1, 2, 4, 8, 15
+PREFILL_PREP, PREFILL_GATE_UP, PREFILL_DOWN, PREFILL_COMBINE, PREFILL_ALL = 1, 2, 4, 8, 15
 
 
 class MoeError(RuntimeError):
@@ -80,6 +81,8 @@ def _load():
         ctypes.POINTER(_Debug), ctypes.c_uint, vp]
     L.moe_expert_ffn_prefill.argtypes = [ctypes.POINTER(_Layer), vp, i32, ctypes.POINTER(_Routing),
                                          vp, vp, sz, vp]
+    L.moe_expert_ffn_prefill_stages.argtypes = [
+        ctypes.POINTER(_Layer), vp, i32, ctypes.POINTER(_Routing), vp, vp, sz, ctypes.c_uint, vp]
     return L
 
 
@@ -209,13 +212,22 @@ def ffn_decode(layer: Layer, x: torch.Tensor, routing: Routing, residual: torch.
 
 
 def ffn_prefill(layer: Layer, x_bf16: torch.Tensor, routing: Routing, residual: torch.Tensor,
-                ws: torch.Tensor | None = None, stream=None) -> None:
-    """moe_expert_ffn_prefill: bf16 matrix-core layer; residual updated in place."""
+                ws: torch.Tensor | None = None, stream=None, stages: int | None = None) -> None:
+    """moe_expert_ffn_prefill: bf16 matrix-core layer; residual updated in place.
+    x_bf16 holds bf16 bit patterns (any 2-byte dtype). With `stages` (PREFILL_* bits) the
+    call goes through moe_expert_ffn_prefill_stages."""
     n = x_bf16.shape[0]
     if ws is None:
         ws = workspace(layer, n, prefill=True, device=x_bf16.device)
     st, rs = layer._struct(), routing._struct()
-    rc = lib.moe_expert_ffn_prefill(ctypes.byref(st), _ptr(x_bf16), n, ctypes.byref(rs),
-                                    _ptr(residual), _ptr(ws), ws.numel(), _stream(stream))
+    if stages is None:
+        rc = lib.moe_expert_ffn_prefill(ctypes.byref(st), _ptr(x_bf16), n, ctypes.byref(rs),
+                                        _ptr(residual), _ptr(ws), ws.numel(), _stream(stream))
+        fn = "moe_expert_ffn_prefill"
+    else:
+        rc = lib.moe_expert_ffn_prefill_stages(ctypes.byref(st), _ptr(x_bf16), n,
+                                               ctypes.byref(rs), _ptr(residual), _ptr(ws),
+                                               ws.numel(), stages, _stream(stream))
+        fn = "moe_expert_ffn_prefill_stages"
     if rc != MOE_OK:
-        raise MoeError("moe_expert_ffn_prefill", rc)
+        raise MoeError(fn, rc)

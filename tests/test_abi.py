@@ -111,14 +111,47 @@ def test_workspace_bytes_grow_with_tokens():
     assert qmoe.lib.moe_route_workspace_bytes(4, 512, 10) == 0
 
 
+def _prefill(L, n=300, x=FAKE + 0x600000, res=FAKE + 0x700000, ws=FAKE + 0x10000000,
+             ws_bytes=1 << 34, routing=None):
+    r = routing if routing is not None else _routing()
+    return qmoe.lib.moe_expert_ffn_prefill(ctypes.byref(L) if L is not None else None, x, n,
+                                           ctypes.byref(r), res, ws, ws_bytes, None)
+
+
 def test_prefill_argument_checks():
+    # every call is rejected before launch: each one breaks exactly one rule
+    assert _prefill(None) == INVALID
+    assert _prefill(_layer(d=100)) == INVALID
+    assert _prefill(_layer(bits=3)) == UNSUPPORTED
     L = _layer()
-    r = _routing()
-    call = lambda L_, n: qmoe.lib.moe_expert_ffn_prefill(  # noqa: E731
-        ctypes.byref(L_), FAKE + 0x600000, n, ctypes.byref(r), FAKE + 0x700000, FAKE + 0x800000,
-        1 << 34, None)
-    assert call(_layer(bits=2), 16) in (INVALID, UNSUPPORTED)
-    assert call(L, 8193) in (INVALID, UNSUPPORTED)
+    L.down = _mat(256, 128, 2)
+    assert _prefill(L) == UNSUPPORTED                           # mixed bit widths
+    assert _prefill(_layer(), n=8193) == INVALID                # beyond the prefill limit
+    assert _prefill(_layer(), n=-1) == INVALID
+    assert _prefill(_layer(), x=FAKE + 0x600008) == INVALID     # x not 16-byte aligned
+    assert _prefill(_layer(), res=FAKE + 0x600000 + 4) == INVALID  # residual overlaps x
+    assert _prefill(_layer(), ws=FAKE + 0x10000010) == INVALID  # ws not 256-byte aligned
+    assert _prefill(_layer(), routing=qmoe._Routing(FAKE, 0, FAKE, FAKE)) == INVALID
+    need = qmoe.lib.moe_ffn_workspace_bytes(ctypes.byref(_layer()), 300, 1)
+    assert need > 0
+    assert _prefill(_layer(), ws_bytes=need - 1) == WS_SMALL
+    assert _prefill(_layer(), ws=FAKE + 0x700000 - 256) == INVALID  # ws overlaps residual
+    assert _prefill(_layer(), n=0, x=0, res=0, ws=0, ws_bytes=0) == OK
+    stages = lambda st: qmoe.lib.moe_expert_ffn_prefill_stages(  # noqa: E731
+        ctypes.byref(_layer()), FAKE + 0x600000, 300, ctypes.byref(_routing()), FAKE + 0x700000,
+        FAKE + 0x10000000, 1 << 34, st, None)
+    assert stages(0) == INVALID
+    assert stages(16) == INVALID
+
+
+def test_prefill_workspace_bytes():
+    L = _layer(d=2048, f=768, E=512, k=10)
+    sizes = [qmoe.lib.moe_ffn_workspace_bytes(ctypes.byref(L), n, 1) for n in (1, 64, 8192)]
+    assert sizes == sorted(sizes) and sizes[0] > 0 and all(s % 256 == 0 for s in sizes)
+    # h (bf16) and the pair outputs (fp32) dominate: (2 f + 4 d) bytes per pair
+    P = 8192 * 10
+    assert P * (2 * 768 + 4 * 2048) <= sizes[-1] < P * (2 * 768 + 4 * 2048 + 64) + (1 << 20)
+    assert qmoe.lib.moe_ffn_workspace_bytes(ctypes.byref(L), 8193, 1) == 0
 
 
 @pytest.mark.parametrize("name", ["libqmoe.so", "libqmoe_synth.so"])
