@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="target CPU time of the oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="first run one plain device-to-device copy of MIB MiB (the reference "
+                         "dispatch that scales hardware byte counters)")
     return ap.parse_args()
 
 
@@ -177,6 +180,31 @@ def cpu_baseline(w, instances_inputs, seconds):
                 tokens_per_s=round(steps * w.n / total_t, 3))
 
 
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_t4_k_gateup_traffic.md")
+
+
+def measured_traffic(profile_path):
+    """Calibrated HBM bytes per launch from a committed counter summary, or None when the
+    kernel source has changed since the counters were taken."""
+    import hashlib
+    import re
+
+    if not os.path.exists(profile_path):
+        return None
+    text = open(profile_path).read()
+    src = re.search(r"^kernel_source: (\S+)$", text, re.M)
+    sha = re.search(r"^kernel_source_sha256: ([0-9a-f]{64})$", text, re.M)
+    val = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
+    if not (src and sha and val):
+        return None
+    path = os.path.join(ROOT, src.group(1))
+    if not os.path.exists(path):
+        return None
+    if hashlib.sha256(open(path, "rb").read()).hexdigest() != sha.group(1):
+        return None
+    return int(val.group(1))
+
+
 def bench_decode(args, torch, q, synth, workloads):
     import numpy as np
 
@@ -245,7 +273,8 @@ def bench_decode(args, torch, q, synth, workloads):
                      "instrumented_step": round(inst_ms / len(order) * 1e3, 2)},
         "roofline": {"bound": "hbm", "kernel": "k_gateup (gate/up + SwiGLU + h quant)",
                      "achieved": round(gu_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(gu_ach / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(gu_ach / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic(TRAFFIC_PROFILE) if args.config == 2 else None,
                      "bytes_per_launch": round(float(np.mean([gu_bytes[i] for i in order])), 1)},
     }
     if args.config == 2 and not args.no_cpu_baseline:
@@ -408,6 +437,15 @@ def main():
     from quantized_routed_expert_router_amd import synth, workloads
 
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        nbytes = args.copy_calibration << 20
+        src = torch.ones(nbytes, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"calibration copy: {nbytes} bytes read, {nbytes} bytes written")
+        del src, dst
     if args.config in (2, 3):
         rec = bench_decode(args, torch, q, synth, workloads)
     elif args.config == 4:
