@@ -63,7 +63,8 @@ def log(msg):
 
 
 class Step:
-    """Pre-built C structs of one layer instance, so the timed loop only makes C calls."""
+    """Pre-built C structs of one layer instance, so the timed loop only makes C calls.
+    One step is moe_layer_decode: routing fused into the first kernel, then the expert FFN."""
 
     def __init__(self, q, layer, lg, x, res, routing, ws):
         self.q = q
@@ -74,16 +75,21 @@ class Step:
         self.n, self.E = lg.shape
         self.k = layer.top_k
 
-    def route(self, stream):
-        rc = self.q.lib.moe_route(self.lg.data_ptr(), self.n, self.E, self.k,
-                                  ctypes.byref(self.rout_s), None, 0, stream)
+    def layer(self, stream, stages):
+        rc = self.q.lib.moe_layer_decode_stages(
+            ctypes.byref(self.layer_s), self.lg.data_ptr(), self.x.data_ptr(), self.n,
+            ctypes.byref(self.rout_s), self.res.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
+            None, stages, stream)
         assert rc == 0, rc
 
-    def decode(self, stream, stages):
-        rc = self.q.lib.moe_expert_ffn_decode_stages(
-            ctypes.byref(self.layer_s), self.x.data_ptr(), self.n, ctypes.byref(self.rout_s),
-            self.res.data_ptr(), self.ws.data_ptr(), self.ws.numel(), None, stages, stream)
-        assert rc == 0, rc
+    def full(self, stream):
+        self.layer(stream, self.q.DECODE_ALL)
+
+    def stages(self):
+        q = self.q
+        return [("route_prep", lambda sh: self.layer(sh, q.DECODE_PREP)),
+                ("gate_up", lambda sh: self.layer(sh, q.DECODE_GATE_UP)),
+                ("down_combine", lambda sh: self.layer(sh, q.DECODE_DOWN | q.DECODE_COMBINE))]
 
 
 def sleep_cycles_for(torch, seconds):
@@ -99,37 +105,32 @@ def sleep_cycles_for(torch, seconds):
     return int(seconds / per_cycle)
 
 
-def timed_region(torch, q, steps, order, instrument, enqueue_estimate):
+def timed_region(torch, steps, order, instrument, enqueue_estimate):
     """Run the steps back to back on the GPU: a spin kernel holds the queue while the host
-    enqueues every step, so host launch cost does not open gaps between kernels.
-    Returns (total_ms, per-step stage ms list or None)."""
+    enqueues every step, so host launch cost does not open gaps between kernels. With
+    `instrument`, HIP events on the launch stream bracket each stage of every step.
+    Returns (total_ms, {stage label: per-step ms list} or None, host seconds, covered)."""
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    plans = [steps[i].stages() for i in order] if instrument else None
     evs = None
     if instrument:
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in order]
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(p) + 1)] for p in plans]
     cycles = sleep_cycles_for(torch, max(0.02, 2.0 * enqueue_estimate))
     torch.cuda.synchronize()
     torch.cuda._sleep(cycles)
     start.record()
     t0 = time.perf_counter()
     for s_idx, i in enumerate(order):
-        st = steps[i]
         if instrument:
             ev = evs[s_idx]
             ev[0].record()
-            st.route(sh)
-            ev[1].record()
-            st.decode(sh, q.DECODE_PREP)
-            ev[2].record()
-            st.decode(sh, q.DECODE_GATE_UP)
-            ev[3].record()
-            st.decode(sh, q.DECODE_DOWN | q.DECODE_COMBINE)
-            ev[4].record()
+            for j, (_, fn) in enumerate(plans[s_idx]):
+                fn(sh)
+                ev[j + 1].record()
         else:
-            st.route(sh)
-            st.decode(sh, q.DECODE_ALL)
+            steps[i].full(sh)
     end.record()
     host_s = time.perf_counter() - t0
     covered = not start.query()  # the spin kernel still ran when the last step was queued
@@ -137,7 +138,9 @@ def timed_region(torch, q, steps, order, instrument, enqueue_estimate):
     total_ms = start.elapsed_time(end)
     stages = None
     if instrument:
-        stages = [[ev[j].elapsed_time(ev[j + 1]) for j in range(4)] for ev in evs]
+        labels = [lab for lab, _ in plans[0]]
+        stages = {lab: [ev[j].elapsed_time(ev[j + 1]) for ev in evs]
+                  for j, lab in enumerate(labels)}
     return total_ms, stages, host_s, covered
 
 
@@ -229,7 +232,7 @@ def bench_decode(args, torch, q, synth, workloads):
     # routing of each instance (fixed per instance): bytes per step
     sh = torch.cuda.current_stream().cuda_stream
     for st in steps:
-        st.route(sh)
+        st.full(sh)  # routing of each instance is fixed: bytes per step
     torch.cuda.synchronize()
     ebytes = synth.expert_bytes(w.d, w.f, w.bits)
     touched = [touched_experts(st.routing) for st in steps]
@@ -239,10 +242,10 @@ def bench_decode(args, torch, q, synth, workloads):
     warm = [s % L for s in range(args.warmup)]
     order = [s % L for s in range(args.steps)]
     # warmup (also estimates the host enqueue time per step)
-    _, _, host_s, _ = timed_region(torch, q, steps, warm or [0], False, 0.05)
+    _, _, host_s, _ = timed_region(torch, steps, warm or [0], False, 0.05)
     est = host_s / max(1, len(warm)) * len(order)
-    total_ms, _, host_s, covered = timed_region(torch, q, steps, order, False, est)
-    inst_ms, stage_ms, _, covered_i = timed_region(torch, q, steps, order, True, est * 2)
+    total_ms, _, host_s, covered = timed_region(torch, steps, order, False, est)
+    inst_ms, stage_ms, _, covered_i = timed_region(torch, steps, order, True, est * 2)
     if not (covered and covered_i):
         log("warning: the host enqueue outlasted the spin kernel; gaps may be included")
 
@@ -250,10 +253,10 @@ def bench_decode(args, torch, q, synth, workloads):
     tot_bytes = sum(step_bytes[i] for i in order)
     value = tot_bytes / sec / 1e9
     tok_s = len(order) * w.n / sec
-    st_ms = np.array(stage_ms)  # [K, 4]: route, prep, gate_up, down+combine
-    gu_sec = st_ms[:, 2].sum() * 1e-3
+    gu_sec = float(np.sum(stage_ms["gate_up"])) * 1e-3
     gu_ach = sum(gu_bytes[i] for i in order) / gu_sec / 1e9
-    mean_us = st_ms.mean(axis=0) * 1e3
+    stage_us = {lab: round(float(np.mean(v)) * 1e3, 2) for lab, v in stage_ms.items()}
+    stage_us["instrumented_step"] = round(inst_ms / len(order) * 1e3, 2)
     mean_touched = float(np.mean([touched[i] for i in order]))
     rec = {
         "metric": METRIC if args.config == 2 else f"{METRIC} [supplementary: {w.name}]",
@@ -263,14 +266,14 @@ def bench_decode(args, torch, q, synth, workloads):
         "data": "synthetic",
         "config": {"workload": w.name, "d_model": w.d, "d_ff": w.f, "experts": w.E,
                    "top_k": w.k, "tokens_per_step": w.n, "weight_bits": w.bits,
-                   "layer_instances": L, "step": "moe_route + moe_expert_ffn_decode"},
+                   "layer_instances": L,
+                   "step": "moe_layer_decode (routing + expert FFN: x quant, gate/up, SwiGLU, "
+                           "h quant, down, combine)"},
         "tokens_per_s": round(tok_s, 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "expert_bytes_per_step": round(float(np.mean([step_bytes[i] for i in order])), 1),
         "touched_experts_per_step": round(mean_touched, 2),
-        "stage_us": {"route": round(mean_us[0], 2), "prep": round(mean_us[1], 2),
-                     "gate_up": round(mean_us[2], 2), "down_combine": round(mean_us[3], 2),
-                     "instrumented_step": round(inst_ms / len(order) * 1e3, 2)},
+        "stage_us": stage_us,
         "roofline": {"bound": "hbm", "kernel": "k_gateup (gate/up + SwiGLU + h quant)",
                      "achieved": round(gu_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_ach / HBM_PEAK_GBS, 4),
@@ -312,15 +315,15 @@ def bench_chain(args, torch, q, synth, workloads):
     log(f"generated in {time.perf_counter() - t0:.1f} s")
     sh = torch.cuda.current_stream().cuda_stream
     for st in steps:
-        st.route(sh)
+        st.full(sh)
     torch.cuda.synchronize()
     ebytes = synth.expert_bytes(w.d, w.f, w.bits)
     touched = [touched_experts(st.routing) for st in steps]
     chain_bytes = sum(touched) * ebytes
     order = list(range(w.layers)) * max(1, args.steps // w.layers)
-    _, _, host_s, _ = timed_region(torch, q, steps, list(range(w.layers)), False, 0.1)
+    _, _, host_s, _ = timed_region(torch, steps, list(range(w.layers)), False, 0.1)
     est = host_s * len(order) / w.layers
-    total_ms, _, _, covered = timed_region(torch, q, steps, order, False, est)
+    total_ms, _, _, covered = timed_region(torch, steps, order, False, est)
     n_chain = len(order) // w.layers
     sec = total_ms * 1e-3
     value = chain_bytes * n_chain / sec / 1e9
@@ -330,7 +333,7 @@ def bench_chain(args, torch, q, synth, workloads):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
         "data": "synthetic",
         "config": {"workload": w.name, "layers": w.layers, "tokens_per_step": w.n,
-                   "step": "48 x (moe_route + moe_expert_ffn_decode), residual chained"},
+                   "step": "48 x moe_layer_decode, residual chained"},
         "tokens_per_s": round(n_chain * w.n / sec, 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "expert_bytes_per_step": chain_bytes,
@@ -358,11 +361,23 @@ class PrefillStep:
                                   ctypes.byref(self.rout_s), None, 0, stream)
         assert rc == 0, rc
 
-    def decode(self, stream, stages):  # the prefill layer, under the name timed_region uses
+    def prefill(self, stream, stages):
         rc = self.q.lib.moe_expert_ffn_prefill_stages(
             ctypes.byref(self.layer_s), self.xb.data_ptr(), self.n, ctypes.byref(self.rout_s),
             self.res.data_ptr(), self.ws.data_ptr(), self.ws.numel(), stages, stream)
         assert rc == 0, rc
+
+    def full(self, stream):
+        self.route(stream)
+        self.prefill(stream, self.q.PREFILL_ALL)
+
+    def stages(self):
+        q = self.q
+        return [("route", self.route),
+                ("prep", lambda sh: self.prefill(sh, q.PREFILL_PREP)),
+                ("gate_up", lambda sh: self.prefill(sh, q.PREFILL_GATE_UP)),
+                ("down", lambda sh: self.prefill(sh, q.PREFILL_DOWN)),
+                ("combine", lambda sh: self.prefill(sh, q.PREFILL_COMBINE))]
 
 
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix-core peak, AMD published
@@ -390,14 +405,18 @@ def bench_prefill(args, torch, q, synth, workloads):
     flop_dn = 2.0 * P * w.d * w.f
     warm = [s % L for s in range(args.warmup)]
     order = [s % L for s in range(args.steps)]
-    _, _, host_s, _ = timed_region(torch, q, steps, warm or [0], False, 0.05)
+    for st in steps:
+        st.route(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    _, _, host_s, _ = timed_region(torch, steps, warm or [0], False, 0.05)
     est = host_s / max(1, len(warm)) * len(order)
-    total_ms, _, _, covered = timed_region(torch, q, steps, order, False, est)
-    inst_ms, stage_ms, _, covered_i = timed_region(torch, q, steps, order, True, est * 2)
-    st_ms = np.array(stage_ms)  # [K, 4]: route, prep, gate_up, down+combine
-    mean_us = st_ms.mean(axis=0) * 1e3
+    total_ms, _, _, covered = timed_region(torch, steps, order, False, est)
+    inst_ms, stage_ms, _, covered_i = timed_region(torch, steps, order, True, est * 2)
+    stage_us = {lab: round(float(np.mean(v)) * 1e3, 2) for lab, v in stage_ms.items()}
+    stage_us["instrumented_step"] = round(inst_ms / len(order) * 1e3, 2)
     sec = total_ms * 1e-3
-    gu_tflops = flop_gu / (mean_us[2] * 1e-6) / 1e12
+    gu_tflops = flop_gu / (stage_us["gate_up"] * 1e-6) / 1e12
+    dn_tflops = flop_dn / (stage_us["down"] * 1e-6) / 1e12
     layer_tflops = (flop_gu + flop_dn) * len(order) / sec / 1e12
     touched = [touched_experts(st.routing) for st in steps]
     ebytes = synth.expert_bytes(w.d, w.f, w.bits)
@@ -412,9 +431,8 @@ def bench_prefill(args, torch, q, synth, workloads):
                    "layer_instances": L, "step": "moe_route + moe_expert_ffn_prefill"},
         "layer_tflops": round(layer_tflops, 1),
         "expert_gbs": round(float(np.mean(touched)) * ebytes * len(order) / sec / 1e9, 1),
-        "stage_us": {"route": round(mean_us[0], 2), "prep": round(mean_us[1], 2),
-                     "gate_up": round(mean_us[2], 2), "down_combine": round(mean_us[3], 2),
-                     "instrumented_step": round(inst_ms / len(order) * 1e3, 2)},
+        "stage_us": stage_us,
+        "down_tflops": round(dn_tflops, 1),
         "roofline": {"bound": "mfma", "kernel": "k_pf_gateup (gate/up GEMM + SwiGLU)",
                      "achieved": round(gu_tflops, 1), "peak": MFMA_BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(gu_tflops / MFMA_BF16_PEAK_TFLOPS, 4),

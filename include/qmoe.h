@@ -176,6 +176,25 @@ moe_status moe_expert_ffn_decode_stages(const moe_layer* L, const float* x, int 
                                         size_t ws_bytes, const moe_debug* dbg, unsigned stages,
                                         void* stream);
 
+/* The whole routed-expert layer for a decode window: moe_route followed by
+ * moe_expert_ffn_decode on the same arguments, with the routing done inside the first
+ * kernel of the layer. The router hands expert ids and weights to the expert pass
+ * (Strata engine explainer, m.lqnn.cn/news/264700, "Doorbell handshake": routing ends
+ * the first half of a layer, combine and residual write-back end the second). logits:
+ * device fp32 [n][E]; r receives the routing exactly as moe_route writes it; all other
+ * arguments, limits and errors as moe_expert_ffn_decode, plus MOE_ERR_INVALID_ARGUMENT
+ * for NULL logits when n > 0. n == 0 only writes zero expert offsets. */
+moe_status moe_layer_decode(const moe_layer* L, const float* logits, const float* x,
+                            int n_tokens, const moe_routing* r, float* residual, void* ws,
+                            size_t ws_bytes, const moe_debug* dbg, void* stream);
+
+/* moe_layer_decode split into stages like moe_expert_ffn_decode_stages; here
+ * MOE_DECODE_PREP also performs the routing. */
+moe_status moe_layer_decode_stages(const moe_layer* L, const float* logits, const float* x,
+                                   int n_tokens, const moe_routing* r, float* residual, void* ws,
+                                   size_t ws_bytes, const moe_debug* dbg, unsigned stages,
+                                   void* stream);
+
 /* Prefill-chunk expert FFN with bf16 arithmetic on the matrix cores: weights are
  * dequantized to bf16 (bf16 of fp32 scale*q + min), x_bf16: device bf16 bits [n][d];
  * gate/up accumulate in fp32; h = bf16(silu(g) * u); down accumulates in fp32;

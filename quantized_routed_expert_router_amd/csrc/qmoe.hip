@@ -63,6 +63,37 @@ moe_status check_routing(const moe_routing* r) {
   return MOE_OK;
 }
 
+moe_status decode_entry(const moe_layer* L, const float* logits, const float* x, int n_tokens,
+                        const moe_routing* r, float* residual, void* ws, size_t ws_bytes,
+                        const moe_debug* dbg, unsigned stages, void* stream) {
+  if (stages == 0 || (stages & ~MOE_DECODE_ALL)) return MOE_ERR_INVALID_ARGUMENT;
+  moe_status s = check_layer(L);
+  if (s != MOE_OK) return s;
+  if (n_tokens < 0 || n_tokens > MOE_MAX_DECODE_TOKENS) return MOE_ERR_INVALID_ARGUMENT;
+  if (n_tokens == 0) return MOE_OK;
+  if (check_routing(r) != MOE_OK) return MOE_ERR_INVALID_ARGUMENT;
+  if (!x || !residual || !ws) return MOE_ERR_INVALID_ARGUMENT;
+  if (!aligned(x, 16) || !aligned(residual, 4) || !aligned(ws, 256))
+    return MOE_ERR_INVALID_ARGUMENT;
+  if (logits && !aligned(logits, 4)) return MOE_ERR_INVALID_ARGUMENT;
+  const size_t act_bytes = (size_t)n_tokens * L->d_model * sizeof(float);
+  if (x != residual && overlaps(x, act_bytes, residual, act_bytes))
+    return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = decode_ws_layout(n_tokens, L->top_k, L->d_model, L->d_ff).total;
+  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  if (overlaps(ws, need, residual, act_bytes) || overlaps(ws, need, x, act_bytes))
+    return MOE_ERR_INVALID_ARGUMENT;
+  DecodeDebug dd{};
+  if (dbg) {
+    dd = DecodeDebug{dbg->xq, dbg->xs, dbg->gate_dots, dbg->up_dots, dbg->g,
+                     dbg->u,  dbg->h,  dbg->hq,        dbg->hs,      dbg->down_dots, dbg->y};
+  }
+  DecodeArgs a{L, logits, x, n_tokens, r, residual, (char*)ws, dbg ? &dd : nullptr,
+               (hipStream_t)stream, device_cu_count(), stages};
+  const hipError_t err = launch_decode(a);
+  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+}
+
 }  // namespace
 }  // namespace qmoe
 
@@ -131,31 +162,30 @@ moe_status moe_expert_ffn_decode_stages(const moe_layer* L, const float* x, int 
                                         const moe_routing* r, float* residual, void* ws,
                                         size_t ws_bytes, const moe_debug* dbg, unsigned stages,
                                         void* stream) {
-  if (stages == 0 || (stages & ~MOE_DECODE_ALL)) return MOE_ERR_INVALID_ARGUMENT;
-  moe_status s = check_layer(L);
-  if (s != MOE_OK) return s;
-  if (n_tokens < 0 || n_tokens > MOE_MAX_DECODE_TOKENS) return MOE_ERR_INVALID_ARGUMENT;
-  if (n_tokens == 0) return MOE_OK;
-  if (check_routing(r) != MOE_OK) return MOE_ERR_INVALID_ARGUMENT;
-  if (!x || !residual || !ws) return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned(x, 16) || !aligned(residual, 4) || !aligned(ws, 256))
-    return MOE_ERR_INVALID_ARGUMENT;
-  const size_t act_bytes = (size_t)n_tokens * L->d_model * sizeof(float);
-  if (x != residual && overlaps(x, act_bytes, residual, act_bytes))
-    return MOE_ERR_INVALID_ARGUMENT;
-  const size_t need = moe_ffn_workspace_bytes(L, n_tokens, 0);
-  if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
-  if (overlaps(ws, need, residual, act_bytes) || overlaps(ws, need, x, act_bytes))
-    return MOE_ERR_INVALID_ARGUMENT;
-  DecodeDebug dd{};
-  if (dbg) {
-    dd = DecodeDebug{dbg->xq, dbg->xs, dbg->gate_dots, dbg->up_dots, dbg->g,
-                     dbg->u,  dbg->h,  dbg->hq,        dbg->hs,      dbg->down_dots, dbg->y};
+  return decode_entry(L, nullptr, x, n_tokens, r, residual, ws, ws_bytes, dbg, stages, stream);
+}
+
+moe_status moe_layer_decode(const moe_layer* L, const float* logits, const float* x,
+                            int n_tokens, const moe_routing* r, float* residual, void* ws,
+                            size_t ws_bytes, const moe_debug* dbg, void* stream) {
+  return moe_layer_decode_stages(L, logits, x, n_tokens, r, residual, ws, ws_bytes, dbg,
+                                 MOE_DECODE_ALL, stream);
+}
+
+moe_status moe_layer_decode_stages(const moe_layer* L, const float* logits, const float* x,
+                                   int n_tokens, const moe_routing* r, float* residual, void* ws,
+                                   size_t ws_bytes, const moe_debug* dbg, unsigned stages,
+                                   void* stream) {
+  if (n_tokens > 0 && !logits) return MOE_ERR_INVALID_ARGUMENT;
+  if (n_tokens == 0) {
+    // no tokens: the routing still reports empty expert groups
+    moe_status s = check_layer(L);
+    if (s != MOE_OK) return s;
+    if (stages == 0 || (stages & ~MOE_DECODE_ALL)) return MOE_ERR_INVALID_ARGUMENT;
+    if (!(stages & MOE_DECODE_PREP)) return MOE_OK;
+    return moe_route(logits, 0, L->n_experts, L->top_k, r, nullptr, 0, stream);
   }
-  DecodeArgs a{L, x, n_tokens, r, residual, (char*)ws, dbg ? &dd : nullptr,
-               (hipStream_t)stream, device_cu_count(), stages};
-  const hipError_t err = launch_decode(a);
-  return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
+  return decode_entry(L, logits, x, n_tokens, r, residual, ws, ws_bytes, dbg, stages, stream);
 }
 
 moe_status moe_expert_ffn_prefill(const moe_layer* L, const uint16_t* x_bf16, int n_tokens,

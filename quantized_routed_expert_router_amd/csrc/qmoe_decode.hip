@@ -25,7 +25,7 @@
 // (the T = 4 window) every touched expert is read exactly once per call.
 #include <algorithm>
 
-#include "qmoe_internal.h"
+#include "qmoe_route_dev.h"
 
 namespace qmoe {
 
@@ -66,55 +66,13 @@ __device__ __forceinline__ float quant_block32(const float (&v)[32], int (&q)[32
 constexpr int kPrepThreads = 1024;  // block 0: one thread per expert (E <= 1024)
 constexpr int kPrepWaves = kPrepThreads / kWave;
 
+// One (token, 32-block) of x -> permuted int8 codes, (scale, scale*sum of codes).
 template <int BITS>
-__global__ __launch_bounds__(kPrepThreads) void k_prep(
-    const float* __restrict__ x, int n, int d, const int32_t* __restrict__ offsets,
-    const int32_t* __restrict__ pair_index, int E, int k, int npc, int* __restrict__ chunks,
-    int* __restrict__ nchunks, int8_t* __restrict__ xq,
-    double2* __restrict__ xsc, int8_t* __restrict__ dbg_xq, float* __restrict__ dbg_xs) {
-  const int tid = threadIdx.x;
-  if (blockIdx.x == 0) {
-    // work list: expert e with c pairs contributes ceil(c/npc) chunk records, in expert
-    // order
-    __shared__ int s_wsum[kPrepWaves];
-    const int lane = tid & (kWave - 1), wave = tid / kWave;
-    const int e = tid;
-    const int beg = e < E ? offsets[e] : 0;
-    const int c = e < E ? offsets[e + 1] - beg : 0;
-    const int cnt = (c + npc - 1) / npc;
-    int incl = cnt;
-#pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
-    }
-    if (lane == kWave - 1) s_wsum[wave] = incl;
-    __syncthreads();
-    int base = incl - cnt;
-    for (int w = 0; w < wave; ++w) base += s_wsum[w];
-    for (int j = 0; j < cnt; ++j) {
-      int* rec = chunks + (size_t)(base + j) * kChunkInts;
-      const int first = beg + j * npc, np = min(npc, c - j * npc);
-      int p[kMaxChunkPairs];
-#pragma unroll
-      for (int q = 0; q < kMaxChunkPairs; ++q) p[q] = pair_index[first + min(q, np - 1)];
-      rec[0] = e;
-      rec[1] = first;
-      rec[2] = np;
-      rec[3] = 0;
-#pragma unroll
-      for (int q = 0; q < kMaxChunkPairs; ++q) {
-        rec[4 + q] = p[q];
-        rec[4 + kMaxChunkPairs + q] = p[q] / k;
-      }
-    }
-    if (tid == kPrepThreads - 1) *nchunks = base + cnt;
-    return;
-  }
+__device__ __forceinline__ void quant_x_block(const float* __restrict__ x, int d, int t, int b,
+                                              int8_t* __restrict__ xq, double2* __restrict__ xsc,
+                                              int8_t* __restrict__ dbg_xq,
+                                              float* __restrict__ dbg_xs) {
   const int nbd = d / 32;
-  const int gid = (blockIdx.x - 1) * kPrepThreads + tid;
-  if (gid >= n * nbd) return;
-  const int t = gid / nbd, b = gid % nbd;
   float v[32];
   const float4* src = reinterpret_cast<const float4*>(x + (size_t)t * d + 32 * b);
 #pragma unroll
@@ -145,6 +103,110 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
     for (int i = 0; i < 32; ++i) dbg_xq[(size_t)t * d + 32 * b + i] = (int8_t)q[i];
   }
   if (dbg_xs) dbg_xs[(size_t)t * nbd + b] = scale;
+}
+
+// Work list: expert e (one per thread, E <= blockDim.x = kPrepThreads) with c pairs
+// contributes ceil(c/npc) chunk records, in expert order. off/pidx may be LDS or global.
+__device__ __forceinline__ void build_work_list(const int32_t* off, const int32_t* pidx, int E,
+                                                int k, int npc, int* __restrict__ chunks,
+                                                int* __restrict__ nchunks, int* s_wsum) {
+  const int tid = threadIdx.x;
+  const int lane = tid & (kWave - 1), wave = tid / kWave;
+  const int e = tid;
+  const int beg = e < E ? off[e] : 0;
+  const int c = e < E ? off[e + 1] - beg : 0;
+  const int cnt = (c + npc - 1) / npc;
+  int incl = cnt;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int v = __shfl_up(incl, o);
+    if (lane >= o) incl += v;
+  }
+  if (lane == kWave - 1) s_wsum[wave] = incl;
+  __syncthreads();
+  int base = incl - cnt;
+  for (int w = 0; w < wave; ++w) base += s_wsum[w];
+  for (int j = 0; j < cnt; ++j) {
+    int* rec = chunks + (size_t)(base + j) * kChunkInts;
+    const int first = beg + j * npc, np = min(npc, c - j * npc);
+    int p[kMaxChunkPairs];
+#pragma unroll
+    for (int q = 0; q < kMaxChunkPairs; ++q) p[q] = pidx[first + min(q, np - 1)];
+    rec[0] = e;
+    rec[1] = first;
+    rec[2] = np;
+    rec[3] = 0;
+#pragma unroll
+    for (int q = 0; q < kMaxChunkPairs; ++q) {
+      rec[4 + q] = p[q];
+      rec[4 + kMaxChunkPairs + q] = p[q] / k;
+    }
+  }
+  if (tid == kPrepThreads - 1) *nchunks = base + cnt;
+}
+
+// prep after a separate routing call: block 0 builds the work list from the routing in
+// global memory, the other blocks quantize x.
+template <int BITS>
+__global__ __launch_bounds__(kPrepThreads) void k_prep(
+    const float* __restrict__ x, int n, int d, const int32_t* __restrict__ offsets,
+    const int32_t* __restrict__ pair_index, int E, int k, int npc, int* __restrict__ chunks,
+    int* __restrict__ nchunks, int8_t* __restrict__ xq,
+    double2* __restrict__ xsc, int8_t* __restrict__ dbg_xq, float* __restrict__ dbg_xs) {
+  if (blockIdx.x == 0) {
+    __shared__ int s_wsum[kPrepWaves];
+    build_work_list(offsets, pair_index, E, k, npc, chunks, nchunks, s_wsum);
+    return;
+  }
+  const int nbd = d / 32;
+  const int gid = (blockIdx.x - 1) * kPrepThreads + threadIdx.x;
+  if (gid >= n * nbd) return;
+  quant_x_block<BITS>(x, d, gid / nbd, gid % nbd, xq, xsc, dbg_xq, dbg_xs);
+}
+
+// Routing fused with prep for small batches (n <= kFusedMaxTokens): block 0 selects the
+// top-k experts of every token (one wavefront per token), groups the pairs by expert and
+// builds the work list without leaving LDS, writing the routing outputs on the way; the
+// other blocks quantize x meanwhile.
+constexpr int kFusedMaxTokens = 64;
+constexpr int kFusedMaxPairs = kFusedMaxTokens * MOE_MAX_TOP_K;
+constexpr int kFusedGroupWaves = 8;
+
+template <int BITS, int KPL>
+__global__ __launch_bounds__(kPrepThreads) void k_route_prep(
+    const float* __restrict__ logits, const float* __restrict__ x, int n, int d, int E, int k,
+    int npc, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ pair_index, int* __restrict__ chunks,
+    int* __restrict__ nchunks, int8_t* __restrict__ xq, double2* __restrict__ xsc,
+    int8_t* __restrict__ dbg_xq, float* __restrict__ dbg_xs) {
+  if (blockIdx.x == 0) {
+    __shared__ int s_ids[kFusedMaxPairs];
+    __shared__ int s_pidx[kFusedMaxPairs];
+    __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+    __shared__ int s_hist[kFusedGroupWaves * MOE_MAX_EXPERTS];
+    __shared__ int s_wsum[kPrepWaves];
+    const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
+    const int P = n * k;
+    for (int t = wave; t < n; t += kPrepWaves) {
+      const int id = wave_topk<KPL>(logits + (size_t)t * E, E, k, topk_ids + (size_t)t * k,
+                                    topk_w + (size_t)t * k);
+      if (lane < k) s_ids[t * k + lane] = id;
+    }
+    __syncthreads();
+    if (P <= kSmallPairs)
+      group_small(s_ids, P, E, s_off, s_pidx);
+    else
+      group_block<kFusedGroupWaves>(s_ids, P, E, s_hist, s_off, s_wsum, s_off, s_pidx);
+    __syncthreads();
+    for (int e = tid; e <= E; e += kPrepThreads) offsets[e] = s_off[e];
+    for (int i = tid; i < P; i += kPrepThreads) pair_index[i] = s_pidx[i];
+    build_work_list(s_off, s_pidx, E, k, npc, chunks, nchunks, s_wsum);
+    return;
+  }
+  const int nbd = d / 32;
+  const int gid = (blockIdx.x - 1) * kPrepThreads + threadIdx.x;
+  if (gid >= n * nbd) return;
+  quant_x_block<BITS>(x, d, gid / nbd, gid % nbd, xq, xsc, dbg_xq, dbg_xs);
 }
 
 // ---------------------------------------------------------------- streaming block loads
@@ -182,15 +244,27 @@ __device__ __forceinline__ double reduce_waves(double (*red)[NPC][kWave], int j,
   return s;
 }
 
+// All-lane reductions over each 32-lane half of a wave: DPP steps combine lanes within a
+// 16-lane row (quad swaps, then the half-row and row mirrors), and one ds_swizzle swaps the
+// two rows of the half (xor 16).
+template <class Op>
+__device__ __forceinline__ uint32_t half_wave_allreduce(uint32_t v, Op op) {
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0xB1, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x4E, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x141, 0xF, 0xF, false));
+  v = op(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x140, 0xF, 0xF, false));
+  // bit-mask swizzle within 32 lanes: and 0x1f, or 0, xor 0x10
+  v = op(v, (uint32_t)__builtin_amdgcn_ds_swizzle((int)v, 0x1F | (0x10 << 10)));
+  return v;
+}
+
 // Quantize h over 32-lane halves of a wave (rows 32b .. 32b+31): returns the code; the
-// scale and the code sum of the half are returned through scale/sum.
+// scale and the code sum of the half are returned through scale/sum. |h| is compared as
+// unsigned bit patterns, which orders non-negative floats like their values.
 __device__ __forceinline__ int quant_half_wave(float h, float& scale, int& sum) {
-  float amax = fabsf(h);
-#pragma unroll
-  for (int off = 1; off < 32; off <<= 1) {
-    const float o = __shfl_xor(amax, off);
-    amax = o > amax ? o : amax;
-  }
+  const uint32_t abits = half_wave_allreduce(__float_as_uint(fabsf(h)),
+                                             [](uint32_t a, uint32_t b) { return a > b ? a : b; });
+  const float amax = __uint_as_float(abits);
   int q = 0;
   scale = 0.0f;
   if (amax != 0.0f) {
@@ -201,27 +275,28 @@ __device__ __forceinline__ int quant_half_wave(float h, float& scale, int& sum) 
     t = t < -127.0f ? -127.0f : t;
     q = (int)t;
   }
-  sum = q;
-#pragma unroll
-  for (int off = 1; off < 32; off <<= 1) sum += __shfl_xor(sum, off);
+  sum = (int)half_wave_allreduce((uint32_t)q, [](uint32_t a, uint32_t b) { return a + b; });
   return q;
 }
 
 // ---------------------------------------------------------------- gate/up + SwiGLU + h quant
 
-// A workgroup of kGuWaves waves takes one item = (chunk of pairs of one expert, 64 rows).
-// Waves 0..3 stream the gate matrix and waves 4..7 the up matrix; wave w covers the
-// reduction blocks w%4, w%4+4, ... in groups of kUnroll and issues all loads of a group
-// (codes and scale/min) as soon as the item's expert is known. The chunk's activation
-// codes and scales are staged in LDS and read back with wave-uniform addresses.
+// A workgroup of kGuWaves waves takes one item = (chunk of pairs of one expert, 32 rows of
+// f): exactly one 32-row block of h, so the int8 quantization of h closes inside the
+// workgroup. Waves 0..3 stream the gate matrix and waves 4..7 the up matrix. Lane l of a
+// wave owns row l%32 of the item and one eighth of the reduction axis, ke = 2*(wave%4) +
+// l/32: it reads blocks ke, ke+8, ke+16, ... in groups of kUnroll. All loads of a group are
+// issued at once (the whole reduction axis at d = 2048), so every weight byte of the item
+// is in flight after one memory latency, and the dots of a block start as soon as that
+// block lands. The chunk's activation codes and scales are staged in LDS per group of
+// 8*kUnroll blocks and read back with half-wave-uniform addresses.
 constexpr int kGuWaves = 8;
 constexpr int kGuThreads = kGuWaves * kWave;
 constexpr int kGuKWaves = kGuWaves / 2;  // waves per matrix
-// blocks in flight per wave: fewer when the chunk holds more pairs (more accumulators)
-template <int NPC>
-struct Unroll {
-  static constexpr int value = 8;
-};
+constexpr int kGuRows = 32;              // rows of f per item
+constexpr int kGuSplit = 2 * kGuKWaves;  // reduction-axis eighths
+constexpr int kGuUnroll = 8;             // blocks per lane per group
+constexpr int kGuGroup = kGuSplit * kGuUnroll;  // blocks per group (64)
 
 // Activation staging straight into LDS with global_load_lds_dwordx4: each wave-level load
 // writes 64 consecutive 16-byte entries of s_act[j][bb][part] (part 0/1: the two halves of
@@ -289,26 +364,24 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     const int* __restrict__ chunks, const int* __restrict__ nchunks, const int8_t* __restrict__ xq,
     const double2* __restrict__ xsc, int8_t* __restrict__ hq, double2* __restrict__ hsc,
     DecodeDebug dbg) {
-  constexpr int kUnroll = Unroll<NPC>::value;
-  constexpr int kGroup = kGuKWaves * kUnroll;  // blocks per weight-load group
-  constexpr int kStage = 2 * kGroup;           // blocks per activation staging
-  __shared__ double red[kGuWaves][NPC][kWave];
-  __shared__ int4 s_act_raw[ActLds<NPC, kStage, kGuThreads>::kPadded];
-  int4 (*s_act)[kStage][3] = reinterpret_cast<int4 (*)[kStage][3]>(s_act_raw);
+  __shared__ double red[kGuWaves][NPC][kGuRows];
+  __shared__ int4 s_act_raw[ActLds<NPC, kGuGroup, kGuThreads>::kPadded];
+  int4 (*s_act)[kGuGroup][3] = reinterpret_cast<int4 (*)[kGuGroup][3]>(s_act_raw);
   const int nbd = d / 32, nbf = f / 32;
-  const int ntiles = (f + kWave - 1) / kWave;
+  const int ntiles = f / kGuRows;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int mat = wave / kGuKWaves;  // 0: gate, 1: up
-  const int kw = wave % kGuKWaves;
+  const int ke = 2 * (wave % kGuKWaves) + lane / kGuRows;  // reduction-axis eighth
+  const int rl = lane % kGuRows;
   const uint32_t* __restrict__ codes = mat ? ucodes : gcodes;
   const uint32_t* __restrict__ smp = mat ? usm : gsm;
   // One scalar load of a chunk's work record gives expert, pair and token ids. The grid
   // never exceeds max_chunks * ntiles, so the first record is inside the work-list buffer.
   int item = blockIdx.x;
   const int nitems = load_uniform(nchunks) * ntiles;
-  int e, np, pid[NPC], tok[NPC];
+  int e, np, pid[NPC];
   const int* rec_rows;  // token ids of the chunk's pairs (activation rows)
   auto read_record = [&](int it) {
     const int* rec = chunks + (size_t)(it / ntiles) * kChunkInts;
@@ -316,18 +389,13 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     e = load_uniform(rec);
     np = load_uniform(rec + 2);
 #pragma unroll
-    for (int j = 0; j < NPC; ++j) {
-      pid[j] = load_uniform(rec + 4 + j);
-      tok[j] = load_uniform(rec + 4 + kMaxChunkPairs + j);
-    }
+    for (int j = 0; j < NPC; ++j) pid[j] = load_uniform(rec + 4 + j);
   };
   read_record(item);
   for (; item < nitems; item += gridDim.x) {
     if (item != (int)blockIdx.x) read_record(item);
     const int tile = item % ntiles;
-    const int r = tile * kWave + lane;
-    const bool rvalid = r < f;
-    const int rr = rvalid ? r : 0;
+    const int r = tile * kGuRows + rl;
     double acc[NPC];
 #pragma unroll
     for (int j = 0; j < NPC; ++j) acc[j] = 0.0;
@@ -335,22 +403,26 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     const __amdgpu_buffer_rsrc_t rs_c =
         buffer_rsrc(codes + (size_t)e * nbd * f * BITS, (uint32_t)(nbd * f * BITS * 4));
     const __amdgpu_buffer_rsrc_t rs_s = buffer_rsrc(smp + (size_t)e * nbd * f, (uint32_t)(nbd * f * 4));
-    // activations are staged per super-group of kStage blocks, weights per group of kGroup
-    uint32_t w[kUnroll][BITS], smw[kUnroll];
-    auto load_weights = [&](int g0) {
+    uint32_t w[kGuUnroll][BITS], smw[kGuUnroll];
+    for (int g0 = 0; g0 < nbd; g0 += kGuGroup) {
+      __syncthreads();  // earlier readers of s_act are done
+      act_load_lds<NPC, kGuGroup, kGuThreads>(s_act_raw, xq, xsc, rec_rows, np, g0, nbd, d, wave,
+                                              lane);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
+      for (int u = 0; u < kGuUnroll; ++u) {
         // blocks past the end (partial last group) re-read the last block; never used
-        const int b = min(g0 + kw + kGuKWaves * u, nbd - 1);
-        BlockLoad<BITS>::load(rs_c, rr * BITS * 4, b * f * BITS * 4, w[u]);
-        smw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, rr * 4, b * f * 4, 0);
+        const int b = min(g0 + ke + kGuSplit * u, nbd - 1);
+        BlockLoad<BITS>::load(rs_c, r * BITS * 4, b * f * BITS * 4, w[u]);
+        smw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, r * 4, b * f * 4, 0);
       }
-    };
-    auto compute = [&](int g0, int s0) {
+      __builtin_amdgcn_sched_barrier(0);
+      wait_vmcnt<2 * kGuUnroll>();  // this wave's staging loads have landed
+      barrier_after_lds_dma();
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) {
-        const int b = g0 + kw + kGuKWaves * u;
-        const int bb = b - s0;
+      for (int u = 0; u < kGuUnroll; ++u) {
+        const int bb = ke + kGuSplit * u;
+        const int b = g0 + bb;
         if (b < nbd) {
           const double sc_w = half_bits_to_double(smw[u] & 0xffffu);
           const double mn_w = half_bits_to_double(smw[u] >> 16);
@@ -362,9 +434,10 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
               double2 sc;
               __builtin_memcpy(&sc, &scv, 16);
               const int dt = block_dot<BITS>(w[u], a);
-              acc[j] += (sc_w * sc.x) * (double)dt;
-              acc[j] += mn_w * sc.y;
-              if (DBG && rvalid) {
+              // both block terms are exact in binary64, so fma rounds exactly like acc + term
+              acc[j] = __builtin_fma(sc_w * sc.x, (double)dt, acc[j]);
+              acc[j] = __builtin_fma(mn_w, sc.y, acc[j]);
+              if (DBG) {
                 int32_t* dots = mat ? dbg.up_dots : dbg.gate_dots;
                 if (dots) dots[((size_t)pid[j] * f + r) * nbd + b] = dt;
               }
@@ -372,53 +445,51 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
           }
         }
       }
-    };
-    for (int s0 = 0; s0 < nbd; s0 += kStage) {
-      __syncthreads();  // earlier readers of s_act are done
-      act_load_lds<NPC, kStage, kGuThreads>(s_act_raw, xq, xsc, rec_rows, np, s0, nbd, d, wave, lane);
-      __builtin_amdgcn_sched_barrier(0);
-      load_weights(s0);  // issues exactly 2 * kUnroll vector loads
-      __builtin_amdgcn_sched_barrier(0);
-      wait_vmcnt<2 * kUnroll>();  // this wave's staging loads have landed
-      barrier_after_lds_dma();
-      compute(s0, s0);
-      for (int g0 = s0 + kGroup; g0 < min(nbd, s0 + kStage); g0 += kGroup) {
-        load_weights(g0);
-        compute(g0, s0);
-      }
     }
+    // the two reduction halves of a row sit in lanes l and l+32
 #pragma unroll
-    for (int j = 0; j < NPC; ++j)
-      if (j < np) red[wave][j][lane] = acc[j];
+    for (int j = 0; j < NPC; ++j) {
+      const double o = __shfl_xor(acc[j], kGuRows);
+      acc[j] = lane < kGuRows ? acc[j] + o : o + acc[j];
+    }
+    if (lane < kGuRows) {
+#pragma unroll
+      for (int j = 0; j < NPC; ++j)
+        if (j < np) red[wave][j][rl] = acc[j];
+    }
     __syncthreads();
     if (wave == 0) {
+      // lanes 0..31 take even pair slots, lanes 32..63 odd ones; each half quantizes the
+      // 32 rows of its pair
+      const int hh = lane / kGuRows;
 #pragma unroll
-      for (int j = 0; j < NPC; ++j) {
+      for (int jj = 0; jj < (NPC + 1) / 2; ++jj) {
+        const int j = 2 * jj + hh;
         if (j < np) {
           // sums over the four waves of each matrix, in wave order
-          double g = red[0][j][lane], u = red[kGuKWaves][j][lane];
+          double g = red[0][j][rl], u = red[kGuKWaves][j][rl];
 #pragma unroll
           for (int w2 = 1; w2 < kGuKWaves; ++w2) {
-            g += red[w2][j][lane];
-            u += red[kGuKWaves + w2][j][lane];
+            g += red[w2][j][rl];
+            u += red[kGuKWaves + w2][j][rl];
           }
           const double silu = g / (1.0 + exp(-g));
-          const float h = rvalid ? (float)(silu * u) : 0.0f;
+          const float h = (float)(silu * u);
           float scale;
           int qsum;
           const int q = quant_half_wave(h, scale, qsum);
-          const int hb = r / 32;
-          if (rvalid) {
-            hq[(size_t)pid[j] * f + 32 * hb + act_byte_pos<BITS>(r % 32)] = (int8_t)q;
-            if ((lane & 31) == 0)
-              hsc[(size_t)pid[j] * nbf + hb] = make_double2((double)scale, (double)scale * qsum);
-          }
-          if (DBG && rvalid) {
-            if (dbg.g) dbg.g[(size_t)pid[j] * f + r] = (float)g;
-            if (dbg.u) dbg.u[(size_t)pid[j] * f + r] = (float)u;
-            if (dbg.h) dbg.h[(size_t)pid[j] * f + r] = h;
-            if (dbg.hq) dbg.hq[(size_t)pid[j] * f + r] = (int8_t)q;
-            if (dbg.hs && (lane & 31) == 0) dbg.hs[(size_t)pid[j] * nbf + hb] = scale;
+          const int p = pid[0];
+          int pj = p;
+#pragma unroll
+          for (int j2 = 1; j2 < NPC; ++j2) pj = j == j2 ? pid[j2] : pj;
+          hq[(size_t)pj * f + 32 * tile + act_byte_pos<BITS>(rl)] = (int8_t)q;
+          if (rl == 0) hsc[(size_t)pj * nbf + tile] = make_double2((double)scale, (double)scale * qsum);
+          if (DBG) {
+            if (dbg.g) dbg.g[(size_t)pj * f + r] = (float)g;
+            if (dbg.u) dbg.u[(size_t)pj * f + r] = (float)u;
+            if (dbg.h) dbg.h[(size_t)pj * f + r] = h;
+            if (dbg.hq) dbg.hq[(size_t)pj * f + r] = (int8_t)q;
+            if (dbg.hs && rl == 0) dbg.hs[(size_t)pj * nbf + tile] = scale;
           }
         }
       }
@@ -497,8 +568,8 @@ __global__ __launch_bounds__(kDnThreads) void k_down(
               double2 sc;
               __builtin_memcpy(&sc, &scv, 16);
               const int dd = block_dot<BITS>(dw[u], a);
-              ay[j] += (s * sc.x) * (double)dd;
-              ay[j] += m * sc.y;
+              ay[j] = __builtin_fma(s * sc.x, (double)dd, ay[j]);  // exact terms: see k_gateup
+              ay[j] = __builtin_fma(m, sc.y, ay[j]);
               if (DBG && rvalid && dbg.down_dots)
                 dbg.down_dots[((size_t)pid[j] * d + r) * nbf + b] = dd;
             }
@@ -573,9 +644,26 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   hipError_t err = hipSuccess;
   if (a.stages & MOE_DECODE_PREP) {
     const int prep_blocks = 1 + (n * nbd + kPrepThreads - 1) / kPrepThreads;
-    hipLaunchKernelGGL(k_prep<BITS>, dim3(prep_blocks), dim3(kPrepThreads), 0, a.stream, a.x, n,
-                       d, a.r->expert_offsets, a.r->pair_index, E, k, NPC, chunks, nchunks, xq,
-                       xsc, DBG ? dbg.xq : nullptr, DBG ? dbg.xs : nullptr);
+    if (a.logits && n <= kFusedMaxTokens) {
+      const int kpl = (E + kWave - 1) / kWave;
+      auto kern = kpl <= 1   ? k_route_prep<BITS, 1>
+                  : kpl <= 2 ? k_route_prep<BITS, 2>
+                  : kpl <= 4 ? k_route_prep<BITS, 4>
+                  : kpl <= 8 ? k_route_prep<BITS, 8>
+                             : k_route_prep<BITS, 16>;
+      hipLaunchKernelGGL(kern, dim3(prep_blocks), dim3(kPrepThreads), 0, a.stream, a.logits, a.x,
+                         n, d, E, k, NPC, a.r->topk_ids, a.r->topk_w, a.r->expert_offsets,
+                         a.r->pair_index, chunks, nchunks, xq, xsc, DBG ? dbg.xq : nullptr,
+                         DBG ? dbg.xs : nullptr);
+    } else {
+      if (a.logits) {
+        err = launch_route(a.logits, n, E, k, a.r, a.stream);
+        if (err != hipSuccess) return err;
+      }
+      hipLaunchKernelGGL(k_prep<BITS>, dim3(prep_blocks), dim3(kPrepThreads), 0, a.stream, a.x,
+                         n, d, a.r->expert_offsets, a.r->pair_index, E, k, NPC, chunks, nchunks,
+                         xq, xsc, DBG ? dbg.xq : nullptr, DBG ? dbg.xs : nullptr);
+    }
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
@@ -585,7 +673,7 @@ hipError_t launch_ffn(const DecodeArgs& a) {
       std::min<long long>((long long)n * k, (long long)E * ((n + NPC - 1) / NPC));
   const int cap = a.num_cus * 8;
   if (a.stages & MOE_DECODE_GATE_UP) {
-    const long long gu_items = max_chunks * ((f + kWave - 1) / kWave);
+    const long long gu_items = max_chunks * (f / kGuRows);
     const int gu_grid = (int)std::max<long long>(1, std::min<long long>(gu_items, cap));
     hipLaunchKernelGGL((k_gateup<BITS, NPC, DBG>), dim3(gu_grid), dim3(kGuThreads), 0, a.stream,
                        L.gate.codes, reinterpret_cast<const uint32_t*>(L.gate.scale_min),

@@ -208,6 +208,7 @@ struct DecodeDebug {
 
 struct DecodeArgs {
   const moe_layer* L;
+  const float* logits;  // non-null: route inside the prep stage (moe_layer_decode)
   const float* x;
   int n;
   const moe_routing* r;

@@ -1,0 +1,222 @@
+// Device routines of the router: top-k selection with routing weights by one wavefront,
+// and the stable grouping of token-expert pairs by expert inside one workgroup.
+//
+// Selection follows the router of the Strata engine explainer (m.lqnn.cn/news/264700,
+// "Architecture overview": each token keeps the 10 of 512 experts its router picks); the
+// expert ids and routing weights form the hand-over record of the "Doorbell handshake"
+// section, and grouping by expert feeds a grouped expert kernel ("Expert cache" section).
+#pragma once
+
+#include "qmoe_internal.h"
+
+namespace qmoe {
+
+// Order-preserving unsigned image of a float; -0 and +0 map to the same value. Finite
+// inputs map to values >= 0x00800000, so 0 is free to mark an expert as taken.
+__device__ __forceinline__ uint32_t order_bits(float f) {
+  f = f + 0.0f;  // -0 becomes +0, so the two compare equal
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float order_bits_to_float(uint32_t o) {
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
+
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+
+// Maximum of a 32-bit value over the wavefront, returned wave-uniform: DPP steps reduce
+// within quads, 8- and 16-lane rows, then across rows (row_bcast15/31) into lane 63.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<0xB1, 0xF>(v));   // quad_perm [1,0,3,2]
+  v = max(v, dpp_u32<0x4E, 0xF>(v));   // quad_perm [2,3,0,1]
+  v = max(v, dpp_u32<0x141, 0xF>(v));  // row_half_mirror
+  v = max(v, dpp_u32<0x140, 0xF>(v));  // row_mirror
+  v = max(v, dpp_u32<0x142, 0xA>(v));  // row_bcast:15
+  v = max(v, dpp_u32<0x143, 0xC>(v));  // row_bcast:31
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
+}
+
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+  uint64_t u;
+  __builtin_memcpy(&u, &v, 8);
+  const uint32_t lo = __builtin_amdgcn_readlane((uint32_t)u, lane);
+  const uint32_t hi = __builtin_amdgcn_readlane((uint32_t)(u >> 32), lane);
+  u = ((uint64_t)hi << 32) | lo;
+  double r;
+  __builtin_memcpy(&r, &u, 8);
+  return r;
+}
+
+// Top-k of one token by one full wavefront. Lane l holds the logits of experts l, l+64,
+// ... as order bits. Each of the k rounds takes the wave maximum of the order bits; the
+// lowest expert id holding that maximum (ties favour the lower id) is found with one ballot
+// per register slot, since ids grow with the slot first and the lane second. Weights are
+// exp(l_j - l_0) / sum_i exp(l_i - l_0) in binary64, summed in slot order. Lane j < k
+// writes slot j and returns its expert id.
+template <int KPL>
+__device__ int wave_topk(const float* __restrict__ lrow, int E, int k, int32_t* __restrict__ ids,
+                         float* __restrict__ w) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t key[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const int e = lane + kWave * i;
+    // valid experts never take 0 (only one NaN pattern maps there), so every round finds
+    // a maximum held by some untaken expert while j < k <= E
+    key[i] = e < E ? max(order_bits(lrow[e]), 1u) : 0u;
+  }
+  int my_id = 0;
+  uint32_t my_bits = 0;
+  for (int j = 0; j < k; ++j) {
+    uint32_t best = key[0];
+#pragma unroll
+    for (int i = 1; i < KPL; ++i) best = max(best, key[i]);
+    best = wave_max_u32(best);
+    int slot = KPL - 1;
+    uint64_t hit = 0;
+#pragma unroll
+    for (int i = KPL - 1; i >= 0; --i) {
+      const uint64_t b = __ballot(key[i] == best);
+      if (b) {
+        slot = i;
+        hit = b;
+      }
+    }
+    const int owner = __builtin_ctzll(hit);
+    const int e = owner + kWave * slot;
+#pragma unroll
+    for (int i = 0; i < KPL; ++i)
+      if (i == slot && lane == owner) key[i] = 0u;
+    if (lane == j) {
+      my_id = e;
+      my_bits = best;
+    }
+  }
+  const float my_l = order_bits_to_float(my_bits);
+  const float l0f = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(my_l)));
+  const double ex = lane < k ? exp((double)my_l - (double)l0f) : 0.0;
+  double sum = 0.0;
+  for (int j = 0; j < k; ++j) sum += readlane_f64(ex, j);  // slot order
+  if (lane < k) {
+    ids[lane] = my_id;
+    w[lane] = (float)(ex / sum);
+  }
+  return my_id;  // lane j < k: the expert of slot j
+}
+
+// Exclusive scan of v[0..n) (n <= 2 * blockDim.x) in LDS; wsum holds one int per wave.
+__device__ inline void block_exclusive_scan(int* v, int n, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int a = 2 * tid < n ? v[2 * tid] : 0;
+  const int b = 2 * tid + 1 < n ? v[2 * tid + 1] : 0;
+  int s = a + b, incl = s;
+#pragma unroll
+  for (int off = 1; off < kWave; off <<= 1) {
+    const int o = __shfl_up(incl, off);
+    if (lane >= off) incl += o;
+  }
+  if (lane == kWave - 1) wsum[wave] = incl;
+  __syncthreads();
+  int wbase = 0;
+  for (int i = 0; i < wave; ++i) wbase += wsum[i];
+  const int excl = wbase + incl - s;
+  __syncthreads();
+  if (2 * tid < n) v[2 * tid] = excl;
+  if (2 * tid + 1 < n) v[2 * tid + 1] = excl + a;
+  __syncthreads();
+}
+
+// Stable counting sort of pair ids 0..P-1 by ids[p] (ids may live in LDS or global
+// memory), by the first NW waves of the workgroup; the rest of the workgroup only joins
+// the barriers. hist: LDS of NW*E ints; s_off: LDS of E+1 ints, which ends up holding the
+// offsets too (offsets may be s_off itself). Writes offsets[0..E] and pair_index[0..P).
+// Per-wave histograms in LDS, a scan, and an in-order scatter where lanes holding the same
+// expert are ranked with ballots over the bits of the expert id.
+template <int NW>
+__device__ void group_block(const int32_t* ids, int P, int E, int* hist, int* s_off, int* wsum,
+                            int32_t* offsets, int32_t* __restrict__ pair_index) {
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int nt = blockDim.x;
+  for (int i = tid; i < NW * E; i += nt) hist[i] = 0;
+  __syncthreads();
+  const int chunk = (P + NW - 1) / NW;
+  const int beg = min(P, wave * chunk), end = wave < NW ? min(P, beg + chunk) : beg;
+  for (int p = beg + lane; p < end; p += kWave) atomicAdd(&hist[wave * E + ids[p]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += nt) {
+    int run = 0;
+    for (int w = 0; w < NW; ++w) {
+      const int c = hist[w * E + e];
+      hist[w * E + e] = run;
+      run += c;
+    }
+    s_off[e] = run;
+  }
+  __syncthreads();
+  block_exclusive_scan(s_off, E, wsum);
+  for (int e = tid; e < E; e += nt) {
+    offsets[e] = s_off[e];
+    for (int w = 0; w < NW; ++w) hist[w * E + e] += s_off[e];
+  }
+  if (tid == 0) {
+    offsets[E] = P;
+    s_off[E] = P;
+  }
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int base = beg; base < end; base += kWave) {
+    const int p = base + lane;
+    const bool valid = p < end;
+    const int e = valid ? ids[p] : 0;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 10; ++bit) {  // experts < 1024
+      const bool set = (e >> bit) & 1;
+      const uint64_t bal = __ballot(set);
+      same &= set ? bal : ~bal;
+    }
+    const int rank = __popcll(same & below);
+    const int cnt = __popcll(same);
+    int slot = 0;
+    if (valid) slot = hist[wave * E + e];
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      pair_index[slot + rank] = p;
+      if (rank == cnt - 1) hist[wave * E + e] = slot + cnt;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
+// Grouping for small batches (P = n*k <= kSmallPairs) with the pair ids in LDS: thread e
+// computes offsets[e] = #{q : ids[q] < e} and pair p lands at
+// #{q : ids[q] < ids[p]} + #{q < p : ids[q] == ids[p]}, the position a stable counting sort
+// gives it. O(P) LDS broadcasts per thread, no atomics and no scans.
+constexpr int kSmallPairs = 256;
+
+__device__ inline void group_small(const int* s_ids, int P, int E, int32_t* __restrict__ offsets,
+                                   int32_t* __restrict__ pair_index) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  for (int e = tid; e <= E; e += nt) {
+    int c = 0;
+#pragma unroll 8
+    for (int q = 0; q < P; ++q) c += s_ids[q] < e;
+    offsets[e] = c;
+  }
+  for (int p = tid; p < P; p += nt) {
+    const int ep = s_ids[p];
+    int pos = 0;
+#pragma unroll 8
+    for (int q = 0; q < P; ++q) {
+      const int eq = s_ids[q];
+      pos += (eq < ep) | ((eq == ep) & (q < p));
+    }
+    pair_index[pos] = p;
+  }
+}
+
+}  // namespace qmoe

@@ -26,7 +26,8 @@ MAX_PREFILL_TOKENS = 8192
 
 EXPORTS = ("moe_status_string", "moe_route_workspace_bytes", "moe_route",
            "moe_ffn_workspace_bytes", "moe_expert_ffn_decode", "moe_expert_ffn_decode_stages",
-           "moe_expert_ffn_prefill", "moe_expert_ffn_prefill_stages")
+           "moe_layer_decode", "moe_layer_decode_stages", "moe_expert_ffn_prefill",
+           "moe_expert_ffn_prefill_stages")
 
 DECODE_PREP, DECODE_GATE_UP, DECODE_DOWN, DECODE_COMBINE, DECODE_ALL = 1, 2, 4, 8, 15
 PREFILL_PREP, PREFILL_GATE_UP, PREFILL_DOWN, PREFILL_COMBINE, PREFILL_ALL = 1, 2, 4, 8, 15
@@ -78,6 +79,11 @@ def _load():
                                         vp, vp, sz, ctypes.POINTER(_Debug), vp]
     L.moe_expert_ffn_decode_stages.argtypes = [
         ctypes.POINTER(_Layer), vp, i32, ctypes.POINTER(_Routing), vp, vp, sz,
+        ctypes.POINTER(_Debug), ctypes.c_uint, vp]
+    L.moe_layer_decode.argtypes = [ctypes.POINTER(_Layer), vp, vp, i32, ctypes.POINTER(_Routing),
+                                   vp, vp, sz, ctypes.POINTER(_Debug), vp]
+    L.moe_layer_decode_stages.argtypes = [
+        ctypes.POINTER(_Layer), vp, vp, i32, ctypes.POINTER(_Routing), vp, vp, sz,
         ctypes.POINTER(_Debug), ctypes.c_uint, vp]
     L.moe_expert_ffn_prefill.argtypes = [ctypes.POINTER(_Layer), vp, i32, ctypes.POINTER(_Routing),
                                          vp, vp, sz, vp]
@@ -209,6 +215,34 @@ def ffn_decode(layer: Layer, x: torch.Tensor, routing: Routing, residual: torch.
         fn = "moe_expert_ffn_decode_stages"
     if rc != MOE_OK:
         raise MoeError(fn, rc)
+
+
+def layer_decode(layer: Layer, logits: torch.Tensor, x: torch.Tensor, residual: torch.Tensor,
+                 routing: Routing | None = None, ws: torch.Tensor | None = None,
+                 debug: dict | None = None, stream=None, stages: int | None = None) -> Routing:
+    """moe_layer_decode: route `logits` and run the decode expert FFN (residual in place).
+    Returns the routing it wrote."""
+    n = x.shape[0]
+    if routing is None:
+        routing = Routing.empty(n, layer.n_experts, layer.top_k, x.device)
+    if ws is None:
+        ws = workspace(layer, n, device=x.device)
+    st, rs = layer._struct(), routing._struct()
+    dbg = None
+    if debug is not None:
+        dbg = ctypes.byref(_Debug(**{k_: _ptr(debug.get(k_)) for k_ in DEBUG_FIELDS}))
+    if stages is None:
+        rc = lib.moe_layer_decode(ctypes.byref(st), _ptr(logits), _ptr(x), n, ctypes.byref(rs),
+                                  _ptr(residual), _ptr(ws), ws.numel(), dbg, _stream(stream))
+        fn = "moe_layer_decode"
+    else:
+        rc = lib.moe_layer_decode_stages(ctypes.byref(st), _ptr(logits), _ptr(x), n,
+                                         ctypes.byref(rs), _ptr(residual), _ptr(ws), ws.numel(),
+                                         dbg, stages, _stream(stream))
+        fn = "moe_layer_decode_stages"
+    if rc != MOE_OK:
+        raise MoeError(fn, rc)
+    return routing
 
 
 def ffn_prefill(layer: Layer, x_bf16: torch.Tensor, routing: Routing, residual: torch.Tensor,

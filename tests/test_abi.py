@@ -159,3 +159,24 @@ def test_built_for_gfx950(name):
     path = os.path.join(os.path.dirname(qmoe.LIB_PATH), name)
     data = open(path, "rb").read()
     assert b"gfx950" in data
+
+
+def test_layer_decode_argument_checks():
+    r = _routing()
+    call = lambda logits, n=4, stages=None: (  # noqa: E731
+        qmoe.lib.moe_layer_decode(ctypes.byref(_layer()), logits, FAKE + 0x600000, n,
+                                  ctypes.byref(r), FAKE + 0x700000, FAKE + 0x800000, 1 << 30,
+                                  None, None)
+        if stages is None else
+        qmoe.lib.moe_layer_decode_stages(ctypes.byref(_layer()), logits, FAKE + 0x600000, n,
+                                         ctypes.byref(r), FAKE + 0x700000, FAKE + 0x800000,
+                                         1 << 30, None, stages, None))
+    assert call(None) == INVALID                     # logits missing
+    assert call(FAKE + 0x900000, n=513) == INVALID   # beyond the decode limit
+    assert call(FAKE + 0x900002) == INVALID          # logits not 4-byte aligned
+    assert call(FAKE + 0x900000, stages=0) == INVALID
+    assert call(FAKE + 0x900000, stages=16) == INVALID
+    L = _layer(bits=3)
+    assert qmoe.lib.moe_layer_decode(ctypes.byref(L), FAKE + 0x900000, FAKE + 0x600000, 4,
+                                     ctypes.byref(r), FAKE + 0x700000, FAKE + 0x800000, 1 << 30,
+                                     None, None) == UNSUPPORTED

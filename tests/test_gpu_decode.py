@@ -248,3 +248,71 @@ def test_decode_config3_2bit_batched(T):
     host = synth.host_layer(w, 0, experts=experts)
     device_layer_matches_host(layer, host, experts[::37], w.E)
     _decode_parity(w, host, lg, x, layer=layer, dots=False)
+
+
+# ------------------------------------------------------------------ fused layer entry point
+
+def _layer_vs_two_calls(w, host_or_layer, lg, x, logits_kind=None):
+    """moe_layer_decode must reproduce moe_route + moe_expert_ffn_decode bit for bit."""
+    layer = (host_or_layer if isinstance(host_or_layer, qmoe.Layer)
+             else workloads.layer_from_host(*host_or_layer, w.k))
+    lg_d, x_d = to_dev(lg), to_dev(x)
+    res_a = x_d.clone()
+    r_a = qmoe.route(lg_d, w.k)
+    qmoe.ffn_decode(layer, x_d, r_a, res_a)
+    res_b = x_d.clone()
+    r_b = qmoe.layer_decode(layer, lg_d, x_d, res_b)
+    torch.cuda.synchronize()
+    n = x.shape[0]
+    for name in ("topk_ids", "topk_w", "expert_offsets"):
+        assert torch.equal(getattr(r_a, name), getattr(r_b, name)), name
+    assert torch.equal(r_a.pair_index[: n * w.k], r_b.pair_index[: n * w.k])
+    assert torch.equal(res_a, res_b)
+    check_routing(lg, w.k, r_b)
+    return res_b.cpu().numpy(), r_b
+
+
+@pytest.mark.parametrize("E,d,f,k,n,bits", [
+    (8, 256, 128, 2, 1, 4),      # config 1 shape, one expert slot per lane
+    (64, 128, 96, 8, 5, 2),      # T = 5 window
+    (1024, 64, 64, 64, 64, 4),   # largest fused batch: 4096 pairs, grouped by histograms
+    (100, 96, 64, 3, 64, 4),     # E not a multiple of 64
+    (16, 64, 64, 4, 65, 2),      # one token past the fused limit: separate routing kernels
+])
+def test_layer_decode_matches_two_calls(E, d, f, k, n, bits):
+    w, host, lg, x = _small(E, d, f, k, n, bits)
+    _layer_vs_two_calls(w, host, lg, x)
+
+
+def test_layer_decode_ties():
+    # many equal logits (and -0 / +0) through the fused router
+    E, k, n = 64, 8, 16
+    w = synth.Workload("ties", 64, 64, E, k, n, 4, "normal")
+    host = synth.host_layer(w, 0)
+    lg = np.round(synth.normal(0, 99, 0, (n, E)) * 2.0).astype(np.float32) / 2.0
+    lg[0, :] = 0.0
+    lg[0, ::3] = -0.0
+    x = synth.activations(0, 0, n, 64)
+    _layer_vs_two_calls(w, host, lg, x)
+
+
+def test_layer_decode_config2_oracle(cfg2_layer):
+    w, layer = cfg2_layer
+    lg, x = synth.layer_inputs(w, 3)
+    out, r = _layer_vs_two_calls(w, layer, lg, x)
+    ids, wt = O.route(lg, w.k)
+    host = synth.host_layer(w, 0, experts=np.unique(ids))
+    out_o, _ = O.ffn_decode(*(omat(h) for h in host), w.E, x, ids, wt, x)
+    assert_output_tolerance(out, out_o)
+    assert_output_tolerance(out - x, out_o - x, what="moe delta")
+
+
+def test_layer_decode_zero_tokens_writes_empty_offsets():
+    w, host, _, _ = _small(8, 64, 64, 2, 1, 4)
+    layer = workloads.layer_from_host(*host, w.k)
+    r = qmoe.Routing.empty(0, w.E, w.k)
+    r.expert_offsets.fill_(7)
+    empty = torch.empty((0, w.d), dtype=torch.float32, device="cuda")
+    qmoe.layer_decode(layer, torch.empty((0, w.E), device="cuda"), empty, empty, routing=r)
+    torch.cuda.synchronize()
+    assert not r.expert_offsets.any()
