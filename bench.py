@@ -355,10 +355,13 @@ class PrefillStep:
         self.lg, self.xb, self.res, self.ws = lg, xb, res, ws
         self.n, self.E = lg.shape
         self.k = layer.top_k
+        self.route_ws = q.route_workspace(self.n, self.E, self.k)
 
     def route(self, stream):
+        rws = self.route_ws
         rc = self.q.lib.moe_route(self.lg.data_ptr(), self.n, self.E, self.k,
-                                  ctypes.byref(self.rout_s), None, 0, stream)
+                                  ctypes.byref(self.rout_s), None if rws is None else rws.data_ptr(),
+                                  0 if rws is None else rws.numel(), stream)
         assert rc == 0, rc
 
     def prefill(self, stream, stages):

@@ -133,13 +133,17 @@ typedef struct {
 /* Human-readable name of a status code (static storage). */
 const char* moe_status_string(moe_status s);
 
-/* Bytes of device workspace moe_route needs for these sizes (0 when none). */
+/* Bytes of device workspace moe_route needs for these sizes: 0 up to 64 tokens or 4096
+ * token-expert pairs; above that, per-chunk expert histograms of a grouping spread over
+ * many workgroups (4 bytes per expert per 2048 pairs). Returns 0 for sizes out of range. */
 size_t moe_route_workspace_bytes(int n_tokens, int n_experts, int top_k);
 
 /* Router top-k, routing weights and grouping (see moe_routing for the outputs).
  * logits: device fp32 [n_tokens][n_experts], finite values (NaN/Inf are a caller
- * error with unspecified selection). Errors: MOE_ERR_INVALID_ARGUMENT for sizes out
- * of range or NULL outputs; MOE_ERR_WORKSPACE_TOO_SMALL. */
+ * error with unspecified selection). ws: device workspace of at least
+ * moe_route_workspace_bytes(n, E, k) bytes, 256-byte aligned, no initialisation needed
+ * (may be NULL when that is 0). Errors: MOE_ERR_INVALID_ARGUMENT for sizes out of range,
+ * NULL outputs or a misaligned workspace; MOE_ERR_WORKSPACE_TOO_SMALL. */
 moe_status moe_route(const float* logits, int n_tokens, int n_experts, int top_k,
                      const moe_routing* out, void* ws, size_t ws_bytes, void* stream);
 
@@ -199,8 +203,8 @@ moe_status moe_layer_decode_stages(const moe_layer* L, const float* logits, cons
  * dequantized to bf16 (bf16 of fp32 scale*q + min), x_bf16: device bf16 bits [n][d];
  * gate/up accumulate in fp32; h = bf16(silu(g) * u); down accumulates in fp32;
  * residual (fp32 [n][d]) += routing-weighted sum of the pair outputs (binary64 sum in
- * slot order, rounded once). 4-bit and 2-bit weights. x_bf16 must be 16-byte aligned and
- * must not overlap residual. r: routing from moe_route for the same n, E and k. ws: at
+ * slot order, rounded once). 4-bit and 2-bit weights. x_bf16 and residual must be
+ * 16-byte aligned and must not overlap. r: routing from moe_route for the same n, E and k. ws: at
  * least moe_ffn_workspace_bytes(L, n, 1) bytes, 256-byte aligned, no initialisation
  * needed; it holds h (bf16 [n*k][f]) and the pair outputs (fp32 [n*k][d]).
  * Limits: n <= MOE_MAX_PREFILL_TOKENS; n == 0 enqueues nothing. */

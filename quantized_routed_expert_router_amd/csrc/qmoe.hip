@@ -118,23 +118,26 @@ const char* moe_status_string(moe_status s) {
 }
 
 size_t moe_route_workspace_bytes(int n_tokens, int n_experts, int top_k) {
-  (void)n_tokens;
-  (void)n_experts;
-  (void)top_k;
-  return 0;
+  if (n_tokens < 0 || n_tokens > MOE_MAX_ROUTE_TOKENS) return 0;
+  if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS) return 0;
+  if (top_k < 1 || top_k > n_experts || top_k > MOE_MAX_TOP_K) return 0;
+  return route_workspace_bytes(n_tokens, n_experts, top_k);
 }
 
 moe_status moe_route(const float* logits, int n_tokens, int n_experts, int top_k,
                      const moe_routing* out, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   if (n_tokens < 0 || n_tokens > MOE_MAX_ROUTE_TOKENS) return MOE_ERR_INVALID_ARGUMENT;
   if (n_experts < 1 || n_experts > MOE_MAX_EXPERTS) return MOE_ERR_INVALID_ARGUMENT;
   if (top_k < 1 || top_k > n_experts || top_k > MOE_MAX_TOP_K) return MOE_ERR_INVALID_ARGUMENT;
   if (!out || !out->expert_offsets) return MOE_ERR_INVALID_ARGUMENT;
   if (n_tokens > 0 && (check_routing(out) != MOE_OK || !logits)) return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = route_workspace_bytes(n_tokens, n_experts, top_k);
+  if (need > 0) {
+    if (!ws || ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!aligned(ws, 256)) return MOE_ERR_INVALID_ARGUMENT;
+  }
   const hipError_t err =
-      launch_route(logits, n_tokens, n_experts, top_k, out, (hipStream_t)stream);
+      launch_route(logits, n_tokens, n_experts, top_k, out, ws, (hipStream_t)stream);
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
 
@@ -206,7 +209,7 @@ moe_status moe_expert_ffn_prefill_stages(const moe_layer* L, const uint16_t* x_b
   if (n_tokens == 0) return MOE_OK;
   if (check_routing(r) != MOE_OK) return MOE_ERR_INVALID_ARGUMENT;
   if (!x_bf16 || !residual || !ws) return MOE_ERR_INVALID_ARGUMENT;
-  if (!aligned(x_bf16, 16) || !aligned(residual, 4) || !aligned(ws, 256))
+  if (!aligned(x_bf16, 16) || !aligned(residual, 16) || !aligned(ws, 256))
     return MOE_ERR_INVALID_ARGUMENT;
   const size_t x_bytes = (size_t)n_tokens * L->d_model * sizeof(uint16_t);
   const size_t res_bytes = (size_t)n_tokens * L->d_model * sizeof(float);

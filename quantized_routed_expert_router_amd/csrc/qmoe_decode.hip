@@ -17,9 +17,12 @@
 //               row sums round only in the additions. The workgroup then applies SwiGLU
 //               and quantizes h per 32 rows (two halves of a wave) to int8.
 //   k_down      the same streaming scheme over the down projection's d rows.
-//   k_combine   residual[t] += sum_j w[t][j] * y[t*k+j] in slot order, binary64. (Folding
-//               it into k_down with a last-arriver counter needs device-scope fences, which
-//               write back the XCD's L2 and cost far more than this small launch.)
+//   k_combine   residual[t] += sum_j w[t][j] * y[t*k+j] in slot order, binary64. It stays a
+//               launch of its own: folding it into k_down through a last-arriver counter
+//               needs the pair outputs to cross XCDs, either through device-scope fences
+//               (an L2 writeback per workgroup) or through write-through stores and loads,
+//               and both put a chain of memory round trips on the last workgroup that costs
+//               more than this small launch.
 //
 // Every expert's weights are read once per chunk of up to NPC pairs; at n <= NPC tokens
 // (the T = 4 window) every touched expert is read exactly once per call.
@@ -657,7 +660,10 @@ hipError_t launch_ffn(const DecodeArgs& a) {
                          DBG ? dbg.xs : nullptr);
     } else {
       if (a.logits) {
-        err = launch_route(a.logits, n, E, k, a.r, a.stream);
+        // the histograms of a multi-workgroup grouping live in the pair-output region,
+        // which is only written later (it holds at least 256 bytes per pair, the
+        // histograms at most 2 bytes per pair plus 4 KB)
+        err = launch_route(a.logits, n, E, k, a.r, a.ws + W.y, a.stream);
         if (err != hipSuccess) return err;
       }
       hipLaunchKernelGGL(k_prep<BITS>, dim3(prep_blocks), dim3(kPrepThreads), 0, a.stream, a.x,

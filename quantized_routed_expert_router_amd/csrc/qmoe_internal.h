@@ -222,8 +222,9 @@ struct DecodeArgs {
 
 // ------------------------------------------------------------------ launchers
 
+size_t route_workspace_bytes(int n, int E, int k);
 hipError_t launch_route(const float* logits, int n, int E, int k, const moe_routing* out,
-                        hipStream_t stream);
+                        void* ws, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 

@@ -305,19 +305,48 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_down(
 
 // ---------------------------------------------------------------- combine
 
-__global__ __launch_bounds__(256) void k_pf_combine(const float* __restrict__ y,
-                                                    const int* __restrict__ g_of_p,
-                                                    const float* __restrict__ w, int n, int d,
-                                                    int k, float* residual) {
-  const size_t gid = (size_t)blockIdx.x * 256 + threadIdx.x;
-  if (gid >= (size_t)n * d) return;
-  const int t = (int)(gid / d), c = (int)(gid % d);
-  double acc = 0.0;
-  for (int j = 0; j < k; ++j) {
-    const int g = g_of_p[t * k + j];
-    acc += (double)w[(size_t)t * k + j] * (double)y[(size_t)g * d + c];
+// One workgroup per token, 4 columns per thread: the token's k pair-output rows are all
+// requested before the first is summed, then residual[t] += sum_j w[t][j] * y[g(t,j)] in
+// slot order (binary64, one rounding).
+constexpr int kCombineBatch = 16;
+
+__global__ __launch_bounds__(1024) void k_pf_combine(const float* __restrict__ y,
+                                                     const int* __restrict__ g_of_p,
+                                                     const float* __restrict__ w, int d, int k,
+                                                     float* residual) {
+  const int t = blockIdx.x;
+  for (int c = 4 * threadIdx.x; c < d; c += 4 * blockDim.x) {
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    for (int j0 = 0; j0 < k; j0 += kCombineBatch) {
+      float4 v[kCombineBatch];
+      float wj[kCombineBatch];
+#pragma unroll
+      for (int i = 0; i < kCombineBatch; ++i) {
+        if (j0 + i < k) {
+          const int g = load_uniform(g_of_p + (size_t)t * k + j0 + i);
+          wj[i] = w[(size_t)t * k + j0 + i];
+          v[i] = *reinterpret_cast<const float4*>(y + (size_t)g * d + c);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kCombineBatch; ++i) {
+        if (j0 + i < k) {
+          const double wd = (double)wj[i];
+          acc[0] += wd * (double)v[i].x;
+          acc[1] += wd * (double)v[i].y;
+          acc[2] += wd * (double)v[i].z;
+          acc[3] += wd * (double)v[i].w;
+        }
+      }
+    }
+    float4* rp = reinterpret_cast<float4*>(residual + (size_t)t * d + c);
+    float4 r = *rp;
+    r.x = (float)((double)r.x + acc[0]);
+    r.y = (float)((double)r.y + acc[1]);
+    r.z = (float)((double)r.z + acc[2]);
+    r.w = (float)((double)r.w + acc[3]);
+    *rp = r;
   }
-  residual[gid] = (float)((double)residual[gid] + acc);
 }
 
 template <int BITS>
@@ -362,9 +391,9 @@ hipError_t launch_prefill_bits(const PrefillArgs& a) {
     if (err != hipSuccess) return err;
   }
   if (a.stages & MOE_PREFILL_COMBINE) {
-    const size_t nd = (size_t)n * d;
-    hipLaunchKernelGGL(k_pf_combine, dim3((unsigned)((nd + 255) / 256)), dim3(256), 0, a.stream,
-                       y, g_of_p, a.r->topk_w, n, d, k, a.residual);
+    const int threads = std::min(1024, ((d / 4 + kWave - 1) / kWave) * kWave);
+    hipLaunchKernelGGL(k_pf_combine, dim3(n), dim3(threads), 0, a.stream, y, g_of_p,
+                       a.r->topk_w, d, k, a.residual);
     err = hipGetLastError();
   }
   return err;

@@ -21,6 +21,8 @@ namespace {
 
 constexpr int kGroupWaves = 8;
 constexpr int kGroupThreads = kGroupWaves * kWave;
+// up to this many pairs one workgroup groups them (k_route_group) without a workspace
+constexpr int kSingleGroupPairs = 4096;
 
 template <int KPL>
 __global__ __launch_bounds__(kGroupThreads) void k_route_fused(
@@ -64,9 +66,100 @@ __global__ __launch_bounds__(kGroupThreads) void k_route_group(const int32_t* __
   group_block<kGroupWaves>(ids, P, E, s_hist, s_off, s_wsum, offsets, pair_index);
 }
 
+// ---- grouping of large batches over many workgroups -------------------------------
+//
+// Pairs are cut into chunks of kChunkPairs; chunk b is handled by workgroup b of both
+// kernels. k_group_count writes each chunk's per-expert histogram to hist[b][E].
+// k_group_scatter lets every workgroup derive what it needs from those histograms: the
+// expert totals (hence the offsets, by a scan) and the number of pairs of each expert in
+// earlier chunks; inside its chunk the scatter is the stable per-wave one of group_block.
+constexpr int kChunkPairs = 2048;
+constexpr int kScatterThreads = 1024;
+constexpr int kScatterWaves = kScatterThreads / kWave;
+
+__global__ __launch_bounds__(kScatterThreads) void k_group_count(const int32_t* __restrict__ ids,
+                                                                 int P, int E,
+                                                                 int* __restrict__ hist) {
+  __shared__ int s_hist[MOE_MAX_EXPERTS];
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kScatterThreads) s_hist[e] = 0;
+  __syncthreads();
+  const int beg = blockIdx.x * kChunkPairs, end = min(P, beg + kChunkPairs);
+  for (int p = beg + tid; p < end; p += kScatterThreads) atomicAdd(&s_hist[ids[p]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += kScatterThreads) hist[(size_t)blockIdx.x * E + e] = s_hist[e];
+}
+
+__global__ __launch_bounds__(kScatterThreads) void k_group_scatter(
+    const int32_t* __restrict__ ids, int P, int E, int nchunks, const int* __restrict__ hist,
+    int32_t* __restrict__ offsets, int32_t* __restrict__ pair_index) {
+  __shared__ int s_whist[kScatterWaves * MOE_MAX_EXPERTS];  // [wave][E]
+  __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+  __shared__ int s_base[MOE_MAX_EXPERTS];
+  __shared__ int s_wsum[kScatterWaves];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int b = blockIdx.x;
+  // expert totals and the pairs of each expert in earlier chunks
+  for (int e = tid; e < E; e += kScatterThreads) {
+    int tot = 0, before = 0;
+    for (int c = 0; c < nchunks; ++c) {
+      const int v = hist[(size_t)c * E + e];
+      tot += v;
+      before += c < b ? v : 0;
+    }
+    s_off[e] = tot;
+    s_base[e] = before;
+  }
+  for (int i = tid; i < kScatterWaves * E; i += kScatterThreads) s_whist[i] = 0;
+  __syncthreads();
+  block_exclusive_scan(s_off, E, s_wsum);
+  if (b == 0) {
+    for (int e = tid; e < E; e += kScatterThreads) offsets[e] = s_off[e];
+    if (tid == 0) offsets[E] = P;
+  }
+  // this chunk: per-wave histograms over contiguous sub-ranges, in pair order
+  const int cbeg = b * kChunkPairs, cend = min(P, cbeg + kChunkPairs);
+  const int per = (cend - cbeg + kScatterWaves - 1) / kScatterWaves;
+  const int wbeg = min(cend, cbeg + wave * per), wend = min(cend, wbeg + per);
+  for (int p = wbeg + lane; p < wend; p += kWave) atomicAdd(&s_whist[wave * E + ids[p]], 1);
+  __syncthreads();
+  for (int e = tid; e < E; e += kScatterThreads) {
+    int run = s_off[e] + s_base[e];
+    for (int w = 0; w < kScatterWaves; ++w) {
+      const int c = s_whist[w * E + e];
+      s_whist[w * E + e] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int base = wbeg; base < wend; base += kWave) {
+    const int p = base + lane;
+    const bool valid = p < wend;
+    const int e = valid ? ids[p] : 0;
+    uint64_t same = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 10; ++bit) {  // experts < 1024
+      const bool set = (e >> bit) & 1;
+      const uint64_t bal = __ballot(set);
+      same &= set ? bal : ~bal;
+    }
+    const int rank = __popcll(same & below);
+    const int cnt = __popcll(same);
+    int slot = 0;
+    if (valid) slot = s_whist[wave * E + e];
+    __builtin_amdgcn_wave_barrier();
+    if (valid) {
+      pair_index[slot + rank] = p;
+      if (rank == cnt - 1) s_whist[wave * E + e] = slot + cnt;
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+}
+
 template <int KPL>
 hipError_t launch_route_kpl(const float* logits, int n, int E, int k, const moe_routing* out,
-                            hipStream_t stream) {
+                            void* ws, hipStream_t stream) {
   if (n <= 64) {
     hipLaunchKernelGGL(k_route_fused<KPL>, dim3(1), dim3(kGroupThreads), 0, stream, logits, n, E,
                        k, out->topk_ids, out->topk_w, out->expert_offsets, out->pair_index);
@@ -76,21 +169,40 @@ hipError_t launch_route_kpl(const float* logits, int n, int E, int k, const moe_
                      out->topk_ids, out->topk_w);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  hipLaunchKernelGGL(k_route_group, dim3(1), dim3(kGroupThreads), 0, stream, out->topk_ids, n * k,
-                     E, out->expert_offsets, out->pair_index);
+  const int P = n * k;
+  if (P <= kSingleGroupPairs) {
+    hipLaunchKernelGGL(k_route_group, dim3(1), dim3(kGroupThreads), 0, stream, out->topk_ids, P,
+                       E, out->expert_offsets, out->pair_index);
+    return hipGetLastError();
+  }
+  const int nchunks = (P + kChunkPairs - 1) / kChunkPairs;
+  int* hist = static_cast<int*>(ws);
+  hipLaunchKernelGGL(k_group_count, dim3(nchunks), dim3(kScatterThreads), 0, stream,
+                     out->topk_ids, P, E, hist);
+  err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(k_group_scatter, dim3(nchunks), dim3(kScatterThreads), 0, stream,
+                     out->topk_ids, P, E, nchunks, hist, out->expert_offsets, out->pair_index);
   return hipGetLastError();
 }
 
 }  // namespace
 
+size_t route_workspace_bytes(int n, int E, int k) {
+  const long long P = (long long)n * k;
+  if (n <= 64 || P <= kSingleGroupPairs) return 0;
+  const long long nchunks = (P + kChunkPairs - 1) / kChunkPairs;
+  return (size_t)(nchunks * E * (long long)sizeof(int));
+}
+
 hipError_t launch_route(const float* logits, int n, int E, int k, const moe_routing* out,
-                        hipStream_t stream) {
+                        void* ws, hipStream_t stream) {
   const int kpl = (E + kWave - 1) / kWave;
-  if (kpl <= 1) return launch_route_kpl<1>(logits, n, E, k, out, stream);
-  if (kpl <= 2) return launch_route_kpl<2>(logits, n, E, k, out, stream);
-  if (kpl <= 4) return launch_route_kpl<4>(logits, n, E, k, out, stream);
-  if (kpl <= 8) return launch_route_kpl<8>(logits, n, E, k, out, stream);
-  return launch_route_kpl<16>(logits, n, E, k, out, stream);
+  if (kpl <= 1) return launch_route_kpl<1>(logits, n, E, k, out, ws, stream);
+  if (kpl <= 2) return launch_route_kpl<2>(logits, n, E, k, out, ws, stream);
+  if (kpl <= 4) return launch_route_kpl<4>(logits, n, E, k, out, ws, stream);
+  if (kpl <= 8) return launch_route_kpl<8>(logits, n, E, k, out, ws, stream);
+  return launch_route_kpl<16>(logits, n, E, k, out, ws, stream);
 }
 
 }  // namespace qmoe

@@ -159,13 +159,22 @@ class Routing:
                         self.expert_offsets.data_ptr(), self.pair_index.data_ptr())
 
 
-def route(logits: torch.Tensor, top_k: int, out: Routing | None = None, stream=None) -> Routing:
+def route_workspace(n: int, E: int, top_k: int, device="cuda") -> torch.Tensor | None:
+    nbytes = int(lib.moe_route_workspace_bytes(n, E, top_k))
+    return torch.empty(nbytes, dtype=torch.uint8, device=device) if nbytes else None
+
+
+def route(logits: torch.Tensor, top_k: int, out: Routing | None = None, stream=None,
+          ws: torch.Tensor | None = None) -> Routing:
     """moe_route: top-k experts, routing weights and expert grouping of `logits` [n, E]."""
     n, E = logits.shape
     if out is None:
         out = Routing.empty(n, E, top_k, logits.device)
+    if ws is None:
+        ws = route_workspace(n, E, top_k, logits.device)
     st = out._struct()
-    rc = lib.moe_route(_ptr(logits), n, E, top_k, ctypes.byref(st), None, 0, _stream(stream))
+    rc = lib.moe_route(_ptr(logits), n, E, top_k, ctypes.byref(st), _ptr(ws),
+                       0 if ws is None else ws.numel(), _stream(stream))
     if rc != MOE_OK:
         raise MoeError("moe_route", rc)
     return out

@@ -109,6 +109,13 @@ def test_workspace_bytes_grow_with_tokens():
     assert sizes == sorted(sizes) and sizes[0] > 0
     assert all(s % 256 == 0 for s in sizes)
     assert qmoe.lib.moe_route_workspace_bytes(4, 512, 10) == 0
+    # multi-workgroup grouping: one 512-expert histogram per 2048 pairs
+    assert qmoe.lib.moe_route_workspace_bytes(8192, 512, 10) == 40 * 512 * 4
+    assert qmoe.lib.moe_route_workspace_bytes(409, 512, 10) == 0  # 4090 pairs: one workgroup
+    r = _routing()
+    assert qmoe.lib.moe_route(FAKE, 8192, 512, 10, ctypes.byref(r), None, 0, None) == WS_SMALL
+    assert qmoe.lib.moe_route(FAKE, 8192, 512, 10, ctypes.byref(r), FAKE + 0x10, 1 << 20,
+                              None) == INVALID  # workspace not 256-byte aligned
 
 
 def _prefill(L, n=300, x=FAKE + 0x600000, res=FAKE + 0x700000, ws=FAKE + 0x10000000,
@@ -129,7 +136,8 @@ def test_prefill_argument_checks():
     assert _prefill(_layer(), n=8193) == INVALID                # beyond the prefill limit
     assert _prefill(_layer(), n=-1) == INVALID
     assert _prefill(_layer(), x=FAKE + 0x600008) == INVALID     # x not 16-byte aligned
-    assert _prefill(_layer(), res=FAKE + 0x600000 + 4) == INVALID  # residual overlaps x
+    assert _prefill(_layer(), res=FAKE + 0x600000 + 16) == INVALID  # residual overlaps x
+    assert _prefill(_layer(), res=FAKE + 0x700004) == INVALID  # residual not 16-byte aligned
     assert _prefill(_layer(), ws=FAKE + 0x10000010) == INVALID  # ws not 256-byte aligned
     assert _prefill(_layer(), routing=qmoe._Routing(FAKE, 0, FAKE, FAKE)) == INVALID
     need = qmoe.lib.moe_ffn_workspace_bytes(ctypes.byref(_layer()), 300, 1)

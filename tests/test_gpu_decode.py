@@ -76,7 +76,10 @@ def test_route_golden_ties():
     (1, 8, 2, "normal"), (4, 512, 10, "zipf"), (5, 33, 7, "normal"), (3, 8, 8, "normal"),
     (6, 100, 1, "normal"), (64, 512, 10, "uniform"), (65, 512, 10, "uniform"),
     (256, 512, 10, "uniform"), (8192, 512, 10, "zipf"), (2, 1024, 64, "normal"),
-    (300, 1000, 3, "normal")])
+    (300, 1000, 3, "normal"),
+    # grouping spread over many workgroups (more than 4096 pairs): ragged last chunk,
+    # the largest expert count, tiny E
+    (4097, 7, 1, "normal"), (1000, 1024, 64, "normal"), (20000, 512, 10, "zipf")])
 def test_route_matches_oracle(n, E, k, kind):
     lg = synth.logits(0, 7, n, E, kind)
     r = qmoe.route(to_dev(lg), k)
@@ -92,6 +95,15 @@ def test_route_many_ties():
     r = qmoe.route(to_dev(lg), 10)
     torch.cuda.synchronize()
     check_routing(lg, 10, r)
+
+
+def test_route_many_ties_many_workgroups():
+    # ties across chunk boundaries of the multi-workgroup grouping
+    rng = np.random.default_rng(4)
+    lg = (rng.integers(-2, 3, (3000, 64)) * 0.25).astype(np.float32)
+    r = qmoe.route(to_dev(lg), 8)
+    torch.cuda.synchronize()
+    check_routing(lg, 8, r)
 
 
 def test_route_zero_tokens_writes_empty_offsets():
