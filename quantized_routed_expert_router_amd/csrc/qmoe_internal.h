@@ -142,7 +142,7 @@ inline DecodeWs decode_ws_layout(int n, int k, int d, int f) {
 
 // Prefill workspace. M-tiles hold up to kPrefillBM consecutive grouped pairs of one
 // expert; h and y are kept in grouped pair order.
-constexpr int kPrefillBM = 128;
+constexpr int kPrefillBM = 256;
 
 struct PrefillWs {
   size_t tiles;     // int4 [max M-tiles] (expert, first grouped position, rows, 0)

@@ -8,7 +8,7 @@
 //
 //   k_pf_prep     M-tile work list (expert, first grouped position, rows) and the token
 //                 and grouped-position maps of every pair.
-//   k_pf_gateup   one workgroup per (M-tile of 128 pairs, 128 rows of f): the gathered bf16
+//   k_pf_gateup   one workgroup per (M-tile of 256 pairs, 128 rows of f): the gathered bf16
 //                 activations and the gate and up weight tiles, dequantized from the packed
 //                 codes to bf16 (bf16 of fp32 scale*q + min) straight into LDS, go through
 //                 v_mfma_f32_32x32x16_bf16 with fp32 accumulators; the epilogue applies
@@ -17,8 +17,8 @@
 //                 and the dequantized down tile as B, fp32 outputs y in grouped order.
 //   k_pf_combine  residual[t] += sum_j w[t][j] * y[pair (t, j)], slot order, binary64 sum.
 //
-// The K loop steps over one 32-column quantization block at a time with two LDS buffers:
-// the global loads of step k+1 are issued before the matrix-core work of step k.
+// The K loop steps over one 32-column quantization block at a time with two LDS buffers
+// (see GemmCore below).
 #include <algorithm>
 
 #include "qmoe_internal.h"
@@ -34,8 +34,6 @@ constexpr int kBM = kPrefillBM;  // pairs per M-tile
 constexpr int kBN = 128;         // weight rows (output columns) per N-tile
 constexpr int kBK = 32;          // one quantization block of the reduction axis
 constexpr int kLdsRow = kBK + 8; // bf16 per LDS row (padding against bank conflicts)
-constexpr int kPfThreads = 512;  // 8 waves
-constexpr int kPfWaves = kPfThreads / kWave;
 
 // ---------------------------------------------------------------- prep
 
@@ -77,44 +75,37 @@ __global__ __launch_bounds__(1024) void k_pf_prep(const int32_t* __restrict__ of
 
 // ---------------------------------------------------------------- dequantization
 
-// 8 consecutive codes (block positions 8*seg .. 8*seg+7) of one packed block -> 8 bf16 of
-// fp32(scale*q + min) rounded to nearest even.
+// Thread (row lr, segment seg) of a K-step dequantizes codes 8*seg .. 8*seg+7 of one
+// 32-weight block: one 32-bit code word (4-bit: word seg; 2-bit: half of word seg/2).
 template <int BITS>
-__device__ __forceinline__ bf16x8 dequant8(const uint32_t (&words)[BITS], int seg, uint32_t sm) {
-  constexpr int per = 32 / BITS;
-  const int i0 = 8 * seg;
-  const uint32_t w = words[i0 / per];
-  const int sh0 = BITS * (i0 % per);
-  const float s = half_bits_to_float(sm & 0xffffu), mn = half_bits_to_float(sm >> 16);
-  bf16x8 out;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t q = (w >> (sh0 + BITS * i)) & ((1u << BITS) - 1u);
-    out[i] = (__bf16)__builtin_fmaf(s, (float)q, mn);
-  }
-  return out;
+__device__ __forceinline__ int code_word_index(int seg) {
+  return BITS == 4 ? seg : seg / 2;
 }
 
+// 8 codes of one word -> 8 bf16 of fp32(scale*q + min) rounded to nearest even (scale*q
+// is exact in fp32, so the fma rounds once, like the separate multiply and add).
 template <int BITS>
-struct Words;
-template <>
-struct Words<4> {
-  __device__ static __forceinline__ void load(const uint32_t* p, uint32_t (&w)[4]) {
-    const uint4 v = *reinterpret_cast<const uint4*>(p);
-    w[0] = v.x;
-    w[1] = v.y;
-    w[2] = v.z;
-    w[3] = v.w;
+__device__ __forceinline__ bf16x8 dequant_word(uint32_t w, int seg, uint32_t sm) {
+  const float s = half_bits_to_float(sm & 0xffffu), mn = half_bits_to_float(sm >> 16);
+  float q[8];
+  if (BITS == 4) {
+    // byte j of lo holds code 2j, byte j of hi code 2j+1 (byte-to-float conversions)
+    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      q[2 * j] = (float)((lo >> (8 * j)) & 0xffu);
+      q[2 * j + 1] = (float)((hi >> (8 * j)) & 0xffu);
+    }
+  } else {
+    const uint32_t v = w >> (16 * (seg & 1));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) q[i] = (float)((v >> (2 * i)) & 3u);
   }
-};
-template <>
-struct Words<2> {
-  __device__ static __forceinline__ void load(const uint32_t* p, uint32_t (&w)[2]) {
-    const uint2 v = *reinterpret_cast<const uint2*>(p);
-    w[0] = v.x;
-    w[1] = v.y;
-  }
-};
+  bf16x8 out;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) out[i] = (__bf16)__builtin_fmaf(s, q[i], mn);
+  return out;
+}
 
 // XCD-aware placement. Workgroups are dealt to the 8 XCDs round robin by workgroup id;
 // XCD x takes the contiguous item range [x*per, (x+1)*per) of the live items, so that the
@@ -129,20 +120,156 @@ __device__ __forceinline__ int xcd_item(int nitems) {
 
 __device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
 
+// ---------------------------------------------------------------- grouped GEMM core
+//
+// One workgroup computes a kBM (256 pairs) x kBN (128 weight rows) tile for NMAT weight
+// matrices that share the A operand. 8 waves: wave w covers pairs 64*(w/2) .. +64 and
+// weight rows 64*(w%2) .. +64 of every matrix with 2 x 2 x NMAT accumulators of 32x32, so
+// each A fragment read from LDS feeds 2*NMAT matrix-core ops and each B fragment 2, and
+// each dequantized weight serves 256 pairs. Waves whose pair range lies past the tile's
+// rows skip their matrix-core work. Each K-step is one 32-wide quantization block.
+// Thread (lr = tid/4, seg = tid%4) brings in 8 consecutive A values of rows lr and lr+128
+// and one code word plus the scale/min word of weight row lr of each matrix, and writes
+// them (dequantized) into the LDS buffer of its K-step. Raw operands run two K-steps
+// ahead in a register ring; step kb dequantizes step kb+1 into the other LDS buffer right
+// after issuing its matrix-core work.
+//
+// (Measured on MI355X: the dequantization and the matrix-core work of a SIMD do not
+// overlap, whether they are issued by the same waves or by separate producer and consumer
+// waves; the time per tile is their sum, so the 256-pair tile, which halves the
+// dequantization per flop against a 128-pair tile, is the one that pays.)
+constexpr int kGemmThreads = 512;
+static_assert(kBM == 256 && kBN == 128, "tile shape of the grouped GEMM core");
+
+template <int BITS, int NMAT>
+struct GemmCore {
+  typedef __bf16 ATile[kBM][kLdsRow];
+  typedef __bf16 BTile[kBN][kLdsRow];
+  static constexpr size_t kLdsBytes = 2 * sizeof(ATile) + (size_t)2 * NMAT * sizeof(BTile);
+
+  struct Raw {
+    uint4 a[2];
+    uint32_t w[NMAT], sm[NMAT];
+  };
+
+  ATile* sA;                    // [2]
+  BTile* sB;                    // [NMAT][2]
+  const uint16_t* arow[2];      // A rows lr and lr+128 of this thread, at column 8*seg
+  const uint32_t* wcol[NMAT];   // code word of weight row lr at K-step 0
+  const uint32_t* smcol[NMAT];  // scale/min word at K-step 0
+  size_t wstep, smstep;         // stride of one K-step in words
+  int lr, seg, lane, wm, wn, nk;
+  bool active;                  // this wave's pair range holds rows of the tile
+  f32x16 acc[NMAT][2][2];
+
+  __device__ __forceinline__ Raw load(int kb) const {
+    Raw R;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      R.a[i] = *reinterpret_cast<const uint4*>(arow[i] + (size_t)kb * kBK);
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m) {
+      R.w[m] = wcol[m][(size_t)kb * wstep];
+      R.sm[m] = smcol[m][(size_t)kb * smstep];
+    }
+    return R;
+  }
+
+  __device__ __forceinline__ void stage(const Raw& R, int buf) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<uint4*>(&sA[buf][lr + 128 * i][8 * seg]) = R.a[i];
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+      *reinterpret_cast<bf16x8*>(&sB[2 * m + buf][lr][8 * seg]) =
+          dequant_word<BITS>(R.w[m], seg, R.sm[m]);
+  }
+
+  __device__ __forceinline__ void mma(int buf) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const int kk = ks * 16 + (lane / 32) * 8;
+      bf16x8 a[2], b[NMAT][2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        a[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][wm + 32 * i + lane % 32][kk]);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+          b[m][j] =
+              *reinterpret_cast<const bf16x8*>(&sB[2 * m + buf][wn + 32 * j + lane % 32][kk]);
+#pragma unroll
+      for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+            acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[m][j], acc[m][i][j],
+                                                                   0, 0, 0);
+    }
+  }
+
+  // One K-step: the matrix-core work of step kb (skipped past the last step and by waves
+  // with no rows), then step kb+1 dequantized into the other buffer and step kb+3
+  // requested into the freed ring slot. Staging and loads run unconditionally (past the
+  // end they repeat the last block into a buffer no matrix-core step reads), so the loop
+  // has no data-dependent branches around its memory operations and the wait counts stay
+  // exact across iterations.
+  __device__ __forceinline__ Raw step(int kb, const Raw next) {
+    if (active && kb < nk) mma(kb & 1);
+    stage(next, (kb + 1) & 1);
+    const Raw refill = load(min(kb + 3, nk - 1));
+    __syncthreads();
+    return refill;
+  }
+
+  __device__ __forceinline__ void run() {
+#pragma unroll
+    for (int m = 0; m < NMAT; ++m)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+          for (int q = 0; q < 16; ++q) acc[m][i][j][q] = 0.0f;
+    Raw r0 = load(0);
+    Raw r1 = load(min(1, nk - 1));
+    stage(r0, 0);
+    r0 = load(min(2, nk - 1));
+    __syncthreads();
+    for (int kb = 0; kb < nk; kb += 2) {
+      r1 = step(kb, r1);
+      r0 = step(kb + 1, r0);
+    }
+  }
+
+  // Set up the LDS views and the wave's tile position.
+  __device__ __forceinline__ void init(char* smem, int rows, int nk_) {
+    const int tid = threadIdx.x, wave = tid / kWave;
+    sA = reinterpret_cast<ATile*>(smem);
+    sB = reinterpret_cast<BTile*>(smem + 2 * sizeof(ATile));
+    lr = tid / 4;
+    seg = tid % 4;
+    lane = tid & (kWave - 1);
+    wm = (wave / 2) * 64;
+    wn = (wave % 2) * 64;
+    nk = nk_;
+    active = wm < rows;
+  }
+};
+
 // ---------------------------------------------------------------- gate/up GEMM
 
 template <int BITS>
-__global__ __launch_bounds__(kPfThreads) void k_pf_gateup(
+__global__ __launch_bounds__(kGemmThreads) void k_pf_gateup(
     const uint32_t* __restrict__ gcodes, const uint32_t* __restrict__ gsm,
     const uint32_t* __restrict__ ucodes, const uint32_t* __restrict__ usm, int d, int f,
     const int4* __restrict__ tiles, const int* __restrict__ ntiles,
     const uint16_t* __restrict__ x, const int* __restrict__ tok_of_g, uint16_t* __restrict__ h,
     int) {
-  typedef __bf16 Tile[kBM][kLdsRow];
-  __shared__ __attribute__((aligned(16))) char smem[6 * sizeof(Tile)];
-  Tile* sA = reinterpret_cast<Tile*>(smem);
-  Tile* sG = sA + 2;
-  Tile* sU = sA + 4;
+  typedef GemmCore<BITS, 2> Core;
+  __shared__ __attribute__((aligned(16))) char smem[Core::kLdsBytes];
   const int ntn = (f + kBN - 1) / kBN;
   const int item = xcd_item(load_uniform(ntiles) * ntn);
   if (item < 0) return;
@@ -150,81 +277,50 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(
   const int4 tile = load_uniform(tiles + mt);
   const int e = tile.x, g0 = tile.y, rows = tile.z;
   const int nbd = d / kBK;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
 
-  // load roles: thread -> (tile row lr, 8-column segment seg)
-  const int lr = tid / 4, seg = tid % 4;
-  const int tok = tok_of_g[g0 + min(lr, rows - 1)];  // padded rows repeat a valid token
-  const uint16_t* xrow = x + (size_t)tok * d + 8 * seg;
-  const int wrow = min(nt * kBN + lr, f - 1);  // rows past f load row f-1, never stored
-
-  uint4 xa;
-  uint32_t gw[BITS], uw[BITS], gs, us;
-  auto gload = [&](int kb) {
-    xa = *reinterpret_cast<const uint4*>(xrow + kb * kBK);
-    const size_t blk = ((size_t)e * nbd + kb) * f + wrow;
-    Words<BITS>::load(gcodes + blk * BITS, gw);
-    Words<BITS>::load(ucodes + blk * BITS, uw);
-    gs = gsm[blk];
-    us = usm[blk];
-  };
-  auto lstore = [&](int buf) {
-    *reinterpret_cast<uint4*>(&sA[buf][lr][8 * seg]) = xa;
-    *reinterpret_cast<bf16x8*>(&sG[buf][lr][8 * seg]) = dequant8<BITS>(gw, seg, gs);
-    *reinterpret_cast<bf16x8*>(&sU[buf][lr][8 * seg]) = dequant8<BITS>(uw, seg, us);
-  };
-
-  // wave tile: 32 pairs x 64 weight rows of both matrices
-  const int wm = (wave / 2) * 32, wn = (wave % 2) * 64;
-  f32x16 accg[2], accu[2];
+  Core c;
+  c.init(smem, rows, nbd);
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) accg[j][i] = accu[j][i] = 0.0f;
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kb = 0; kb < nbd; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nbd) gload(kb + 1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int kk = ks * 16 + (lane / 32) * 8;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sA[buf][wm + lane % 32][kk]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8 bg = *reinterpret_cast<const bf16x8*>(&sG[buf][wn + 32 * j + lane % 32][kk]);
-        const bf16x8 bu = *reinterpret_cast<const bf16x8*>(&sU[buf][wn + 32 * j + lane % 32][kk]);
-        accg[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bg, accg[j], 0, 0, 0);
-        accu[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, bu, accu[j], 0, 0, 0);
-      }
-    }
-    if (kb + 1 < nbd) lstore(buf ^ 1);
-    __syncthreads();
+  for (int i = 0; i < 2; ++i) {
+    const int tok = tok_of_g[g0 + min(c.lr + 128 * i, rows - 1)];  // padded rows repeat
+    c.arow[i] = x + (size_t)tok * d + 8 * c.seg;                   // a valid token
   }
+  const int wrow = min(nt * kBN + c.lr, f - 1);  // rows past f load row f-1, never stored
+  const size_t blk0 = (size_t)e * nbd * f + wrow;
+  c.wcol[0] = gcodes + blk0 * BITS + code_word_index<BITS>(c.seg);
+  c.wcol[1] = ucodes + blk0 * BITS + code_word_index<BITS>(c.seg);
+  c.smcol[0] = gsm + blk0;
+  c.smcol[1] = usm + blk0;
+  c.wstep = (size_t)f * BITS;
+  c.smstep = (size_t)f;
+  c.run();
 
-  // epilogue: h = bf16(silu(g) * u), staged per wave in LDS for 16-byte global stores
-  __bf16* st = reinterpret_cast<__bf16*>(smem) + wave * (32 * 64);  // 4 KB per wave
+  // epilogue: h = bf16(silu(g) * u), staged per wave in LDS (64 x 64 bf16 = 8 KB per wave)
+  // for 16-byte global stores
+  if (!c.active) return;
+  __bf16* st = reinterpret_cast<__bf16*>(smem) + wave * (64 * 64);
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rr = (i / 4) * 8 + (lane / 32) * 4 + (i % 4);
-      const int cc = 32 * j + lane % 32;
-      st[rr * 64 + cc] = (__bf16)silu_mul(accg[j][i], accu[j][i]);
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int rr = 32 * i + (q / 4) * 8 + (lane / 32) * 4 + (q % 4);
+        const int cc = 32 * j + lane % 32;
+        st[rr * 64 + cc] = (__bf16)silu_mul(c.acc[0][i][j][q], c.acc[1][i][j][q]);
+      }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int c = lane + kWave * q;  // 256 chunks of 8 bf16
-    const int rr = c / 8, cc = (c % 8) * 8;
-    const int col = nt * kBN + wn + cc;
-    if (wm + rr < rows && col < f) {
+  for (int q = 0; q < 8; ++q) {
+    const int ch = lane + kWave * q;  // 512 chunks of 8 bf16
+    const int rr = ch / 8, cc = (ch % 8) * 8;
+    const int col = nt * kBN + c.wn + cc;
+    if (c.wm + rr < rows && col < f) {
       const uint4 v = *reinterpret_cast<const uint4*>(&st[rr * 64 + cc]);
-      *reinterpret_cast<uint4*>(h + (size_t)(g0 + wm + rr) * f + col) = v;
+      *reinterpret_cast<uint4*>(h + (size_t)(g0 + c.wm + rr) * f + col) = v;
     }
   }
 }
@@ -232,14 +328,12 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_gateup(
 // ---------------------------------------------------------------- down GEMM
 
 template <int BITS>
-__global__ __launch_bounds__(kPfThreads) void k_pf_down(
+__global__ __launch_bounds__(kGemmThreads) void k_pf_down(
     const uint32_t* __restrict__ dcodes, const uint32_t* __restrict__ dsm, int d, int f,
     const int4* __restrict__ tiles, const int* __restrict__ ntiles,
     const uint16_t* __restrict__ h, float* __restrict__ y, int) {
-  typedef __bf16 Tile[kBM][kLdsRow];
-  __shared__ __attribute__((aligned(16))) char smem[4 * sizeof(Tile)];
-  Tile* sA = reinterpret_cast<Tile*>(smem);
-  Tile* sW = sA + 2;
+  typedef GemmCore<BITS, 1> Core;
+  __shared__ __attribute__((aligned(16))) char smem[Core::kLdsBytes];
   const int ntn = (d + kBN - 1) / kBN;
   const int item = xcd_item(load_uniform(ntiles) * ntn);
   if (item < 0) return;
@@ -247,60 +341,33 @@ __global__ __launch_bounds__(kPfThreads) void k_pf_down(
   const int4 tile = load_uniform(tiles + mt);
   const int e = tile.x, g0 = tile.y, rows = tile.z;
   const int nbf = f / kBK;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int lane = threadIdx.x & (kWave - 1);
 
-  const int lr = tid / 4, seg = tid % 4;
-  const uint16_t* hrow = h + (size_t)(g0 + min(lr, rows - 1)) * f + 8 * seg;
-  const int wrow = min(nt * kBN + lr, d - 1);  // rows past d load row d-1, never stored
+  Core c;
+  c.init(smem, rows, nbf);
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    c.arow[i] = h + (size_t)(g0 + min(c.lr + 128 * i, rows - 1)) * f + 8 * c.seg;
+  const int wrow = min(nt * kBN + c.lr, d - 1);  // rows past d load row d-1, never stored
+  const size_t blk0 = (size_t)e * nbf * d + wrow;
+  c.wcol[0] = dcodes + blk0 * BITS + code_word_index<BITS>(c.seg);
+  c.smcol[0] = dsm + blk0;
+  c.wstep = (size_t)d * BITS;
+  c.smstep = (size_t)d;
+  c.run();
+  if (!c.active) return;
 
-  uint4 ha;
-  uint32_t dw[BITS], ds;
-  auto gload = [&](int kb) {
-    ha = *reinterpret_cast<const uint4*>(hrow + kb * kBK);
-    const size_t blk = ((size_t)e * nbf + kb) * d + wrow;
-    Words<BITS>::load(dcodes + blk * BITS, dw);
-    ds = dsm[blk];
-  };
-  auto lstore = [&](int buf) {
-    *reinterpret_cast<uint4*>(&sA[buf][lr][8 * seg]) = ha;
-    *reinterpret_cast<bf16x8*>(&sW[buf][lr][8 * seg]) = dequant8<BITS>(dw, seg, ds);
-  };
-
-  const int wm = (wave / 2) * 32, wn = (wave % 2) * 64;
-  f32x16 acc[2];
-#pragma unroll
-  for (int j = 0; j < 2; ++j)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) acc[j][i] = 0.0f;
-
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  for (int kb = 0; kb < nbf; ++kb) {
-    const int buf = kb & 1;
-    if (kb + 1 < nbf) gload(kb + 1);
-#pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      const int kk = ks * 16 + (lane / 32) * 8;
-      const bf16x8 a = *reinterpret_cast<const bf16x8*>(&sA[buf][wm + lane % 32][kk]);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const bf16x8 b = *reinterpret_cast<const bf16x8*>(&sW[buf][wn + 32 * j + lane % 32][kk]);
-        acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
-      }
-    }
-    if (kb + 1 < nbf) lstore(buf ^ 1);
-    __syncthreads();
-  }
   // y in grouped order: lanes 0..31 of a row write 32 consecutive floats
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int rr = wm + (i / 4) * 8 + (lane / 32) * 4 + (i % 4);
-      const int col = nt * kBN + wn + 32 * j + lane % 32;
-      if (rr < rows && col < d) y[(size_t)(g0 + rr) * d + col] = acc[j][i];
-    }
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) {
+        const int rr = c.wm + 32 * i + (q / 4) * 8 + (lane / 32) * 4 + (q % 4);
+        const int col = nt * kBN + c.wn + 32 * j + lane % 32;
+        if (rr < rows && col < d) y[(size_t)(g0 + rr) * d + col] = c.acc[0][i][j][q];
+      }
 }
 
 // ---------------------------------------------------------------- combine
@@ -375,7 +442,7 @@ hipError_t launch_prefill_bits(const PrefillArgs& a) {
   const int max_mt = prefill_max_mtiles(P, E);
   if (a.stages & MOE_PREFILL_GATE_UP) {
     const int gu_items = ((max_mt * ((f + kBN - 1) / kBN) + 7) / 8) * 8;
-    hipLaunchKernelGGL(k_pf_gateup<BITS>, dim3(gu_items), dim3(kPfThreads), 0, a.stream,
+    hipLaunchKernelGGL(k_pf_gateup<BITS>, dim3(gu_items), dim3(kGemmThreads), 0, a.stream,
                        L.gate.codes, reinterpret_cast<const uint32_t*>(L.gate.scale_min),
                        L.up.codes, reinterpret_cast<const uint32_t*>(L.up.scale_min), d, f, tiles,
                        ntiles, a.x, tok_of_g, h, gu_items);
@@ -384,7 +451,7 @@ hipError_t launch_prefill_bits(const PrefillArgs& a) {
   }
   if (a.stages & MOE_PREFILL_DOWN) {
     const int dn_items = ((max_mt * ((d + kBN - 1) / kBN) + 7) / 8) * 8;
-    hipLaunchKernelGGL(k_pf_down<BITS>, dim3(dn_items), dim3(kPfThreads), 0, a.stream,
+    hipLaunchKernelGGL(k_pf_down<BITS>, dim3(dn_items), dim3(kGemmThreads), 0, a.stream,
                        L.down.codes, reinterpret_cast<const uint32_t*>(L.down.scale_min), d, f,
                        tiles, ntiles, h, y, dn_items);
     err = hipGetLastError();
