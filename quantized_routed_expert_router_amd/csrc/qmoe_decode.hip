@@ -183,18 +183,20 @@ __global__ __launch_bounds__(kPrepThreads) void k_route_prep(
     int* __restrict__ nchunks, int8_t* __restrict__ xq, double2* __restrict__ xsc,
     int8_t* __restrict__ dbg_xq, float* __restrict__ dbg_xs) {
   if (blockIdx.x == 0) {
-    __shared__ int s_ids[kFusedMaxPairs];
+    __shared__ __attribute__((aligned(16))) int s_ids[kFusedMaxPairs + 4];
     __shared__ int s_pidx[kFusedMaxPairs];
     __shared__ int s_off[MOE_MAX_EXPERTS + 1];
     __shared__ int s_hist[kFusedGroupWaves * MOE_MAX_EXPERTS];
     __shared__ int s_wsum[kPrepWaves];
+    __shared__ TopkScratch s_tk[kPrepWaves];
     const int tid = threadIdx.x, wave = tid / kWave, lane = tid & (kWave - 1);
     const int P = n * k;
     for (int t = wave; t < n; t += kPrepWaves) {
       const int id = wave_topk<KPL>(logits + (size_t)t * E, E, k, topk_ids + (size_t)t * k,
-                                    topk_w + (size_t)t * k);
+                                    topk_w + (size_t)t * k, &s_tk[wave]);
       if (lane < k) s_ids[t * k + lane] = id;
     }
+    if (tid < 4 && P + tid < ((P + 3) & ~3)) s_ids[P + tid] = 0x7fffffff;  // group_small pad
     __syncthreads();
     if (P <= kSmallPairs)
       group_small(s_ids, P, E, s_off, s_pidx);

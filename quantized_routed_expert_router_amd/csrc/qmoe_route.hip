@@ -28,17 +28,20 @@ template <int KPL>
 __global__ __launch_bounds__(kGroupThreads) void k_route_fused(
     const float* __restrict__ logits, int n, int E, int k, int32_t* ids, float* __restrict__ w,
     int32_t* __restrict__ offsets, int32_t* __restrict__ pair_index) {
-  __shared__ int s_ids[kSmallPairs];
+  __shared__ __attribute__((aligned(16))) int s_ids[kSmallPairs + 4];
   __shared__ int s_hist[kGroupWaves * MOE_MAX_EXPERTS];
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
   __shared__ int s_wsum[kGroupWaves];
+  __shared__ TopkScratch s_tk[kGroupWaves];
   const int wave = threadIdx.x / kWave, lane = threadIdx.x & (kWave - 1);
   const int P = n * k;
   for (int t = wave; t < n; t += kGroupWaves) {
     const int id = wave_topk<KPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k,
-                                  w + (size_t)t * k);
+                                  w + (size_t)t * k, &s_tk[wave]);
     if (P <= kSmallPairs && lane < k) s_ids[t * k + lane] = id;
   }
+  if (P <= kSmallPairs && threadIdx.x < 4 && P + (int)threadIdx.x < ((P + 3) & ~3))
+    s_ids[P + threadIdx.x] = 0x7fffffff;  // padding read by group_small
   __threadfence_block();
   __syncthreads();
   if (P <= kSmallPairs)
@@ -51,9 +54,11 @@ template <int KPL>
 __global__ __launch_bounds__(256) void k_route_topk(const float* __restrict__ logits, int n, int E,
                                                     int k, int32_t* __restrict__ ids,
                                                     float* __restrict__ w) {
+  __shared__ TopkScratch s_tk[256 / kWave];
   const int t = blockIdx.x * (256 / kWave) + threadIdx.x / kWave;
   if (t >= n) return;
-  wave_topk<KPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k);
+  wave_topk<KPL>(logits + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k,
+                 &s_tk[threadIdx.x / kWave]);
 }
 
 __global__ __launch_bounds__(kGroupThreads) void k_route_group(const int32_t* __restrict__ ids,

@@ -51,15 +51,31 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
   return r;
 }
 
+// Per-wave LDS scratch of the threshold selection in wave_topk.
+struct TopkScratch {
+  uint32_t key[kWave];
+  int id[kWave];
+  uint32_t slot_key[MOE_MAX_TOP_K];
+  int slot_id[MOE_MAX_TOP_K];
+};
+
 // Top-k of one token by one full wavefront. Lane l holds the logits of experts l, l+64,
-// ... as order bits. Each of the k rounds takes the wave maximum of the order bits; the
-// lowest expert id holding that maximum (ties favour the lower id) is found with one ballot
-// per register slot, since ids grow with the slot first and the lane second. Weights are
-// exp(l_j - l_0) / sum_i exp(l_i - l_0) in binary64, summed in slot order. Lane j < k
-// writes slot j and returns its expert id.
+// ... as order bits (ties favour the lower expert id; -0 equals +0).
+//
+// Selection by threshold: T = the k-th largest of the 64 lane maxima, found bit by bit
+// with ballots. At least k experts (those lane maxima) have keys >= T, so every expert
+// of the top k has a key >= T, and ranking the candidates (keys >= T) by (key desc, id
+// asc) ranks the top k exactly. The candidates are compacted into LDS with ballots and
+// each one counts how many candidates precede it. When more than 64 candidates tie at the
+// threshold, k rounds of a wave maximum select instead (the lowest id holding the maximum
+// is found with one ballot per register slot, since ids grow with the slot first and the
+// lane second).
+//
+// Weights are exp(l_j - l_0) / sum_i exp(l_i - l_0) in binary64, summed in slot order.
+// Lane j < k writes slot j and returns its expert id.
 template <int KPL>
 __device__ int wave_topk(const float* __restrict__ lrow, int E, int k, int32_t* __restrict__ ids,
-                         float* __restrict__ w) {
+                         float* __restrict__ w, TopkScratch* sc) {
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t key[KPL];
 #pragma unroll
@@ -69,31 +85,81 @@ __device__ int wave_topk(const float* __restrict__ lrow, int E, int k, int32_t* 
     // a maximum held by some untaken expert while j < k <= E
     key[i] = e < E ? max(order_bits(lrow[e]), 1u) : 0u;
   }
+  uint32_t lmax = key[0];
+#pragma unroll
+  for (int i = 1; i < KPL; ++i) lmax = max(lmax, key[i]);
+  // T: the largest value with at least k lane maxima >= T (at least k lanes hold valid
+  // experts, since k <= E and k <= 64)
+  uint32_t T = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t t = T | (1u << b);
+    if (__popcll(__ballot(lmax >= t)) >= k) T = t;
+  }
+  // compact the candidates in (slot, lane) order
+  const uint64_t below = (1ull << lane) - 1ull;
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) {
+    const bool c = key[i] >= T;
+    const uint64_t b = __ballot(c);
+    const int pos = total + __popcll(b & below);
+    if (c && pos < kWave) {
+      sc->key[pos] = key[i];
+      sc->id[pos] = lane + kWave * i;
+    }
+    total += __popcll(b);
+  }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   int my_id = 0;
   uint32_t my_bits = 0;
-  for (int j = 0; j < k; ++j) {
-    uint32_t best = key[0];
-#pragma unroll
-    for (int i = 1; i < KPL; ++i) best = max(best, key[i]);
-    best = wave_max_u32(best);
-    int slot = KPL - 1;
-    uint64_t hit = 0;
-#pragma unroll
-    for (int i = KPL - 1; i >= 0; --i) {
-      const uint64_t b = __ballot(key[i] == best);
-      if (b) {
-        slot = i;
-        hit = b;
+  if (total <= kWave) {
+    if (lane < total) {
+      const uint32_t mk = sc->key[lane];
+      const int mi = sc->id[lane];
+      int rank = 0;
+      for (int q = 0; q < total; ++q) {
+        const uint32_t qk = sc->key[q];
+        rank += (qk > mk) | ((qk == mk) & (sc->id[q] < mi));
+      }
+      if (rank < k) {
+        sc->slot_key[rank] = mk;
+        sc->slot_id[rank] = mi;
       }
     }
-    const int owner = __builtin_ctzll(hit);
-    const int e = owner + kWave * slot;
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (lane < k) {
+      my_id = sc->slot_id[lane];
+      my_bits = sc->slot_key[lane];
+    }
+  } else {
+    for (int j = 0; j < k; ++j) {
+      uint32_t best = key[0];
 #pragma unroll
-    for (int i = 0; i < KPL; ++i)
-      if (i == slot && lane == owner) key[i] = 0u;
-    if (lane == j) {
-      my_id = e;
-      my_bits = best;
+      for (int i = 1; i < KPL; ++i) best = max(best, key[i]);
+      best = wave_max_u32(best);
+      int slot = KPL - 1;
+      uint64_t hit = 0;
+#pragma unroll
+      for (int i = KPL - 1; i >= 0; --i) {
+        const uint64_t b = __ballot(key[i] == best);
+        if (b) {
+          slot = i;
+          hit = b;
+        }
+      }
+      const int owner = __builtin_ctzll(hit);
+      const int e = owner + kWave * slot;
+#pragma unroll
+      for (int i = 0; i < KPL; ++i)
+        if (i == slot && lane == owner) key[i] = 0u;
+      if (lane == j) {
+        my_id = e;
+        my_bits = best;
+      }
     }
   }
   const float my_l = order_bits_to_float(my_bits);
@@ -200,20 +266,31 @@ constexpr int kSmallPairs = 256;
 
 __device__ inline void group_small(const int* s_ids, int P, int E, int32_t* __restrict__ offsets,
                                    int32_t* __restrict__ pair_index) {
+  // s_ids holds P ids followed by padding up to a multiple of 4 filled with INT_MAX, which
+  // is neither below nor equal to any expert id
   const int tid = threadIdx.x, nt = blockDim.x;
+  const int4* s4 = reinterpret_cast<const int4*>(s_ids);
+  const int P4 = (P + 3) / 4;
   for (int e = tid; e <= E; e += nt) {
     int c = 0;
-#pragma unroll 8
-    for (int q = 0; q < P; ++q) c += s_ids[q] < e;
+#pragma unroll 4
+    for (int q = 0; q < P4; ++q) {
+      const int4 v = s4[q];
+      c += (v.x < e) + (v.y < e) + (v.z < e) + (v.w < e);
+    }
     offsets[e] = c;
   }
   for (int p = tid; p < P; p += nt) {
     const int ep = s_ids[p];
     int pos = 0;
-#pragma unroll 8
-    for (int q = 0; q < P; ++q) {
-      const int eq = s_ids[q];
-      pos += (eq < ep) | ((eq == ep) & (q < p));
+#pragma unroll 4
+    for (int q = 0; q < P4; ++q) {
+      const int4 v = s4[q];
+      const int q0 = 4 * q;
+      pos += (v.x < ep) | ((v.x == ep) & (q0 < p));
+      pos += (v.y < ep) | ((v.y == ep) & (q0 + 1 < p));
+      pos += (v.z < ep) | ((v.z == ep) & (q0 + 2 < p));
+      pos += (v.w < ep) | ((v.w == ep) & (q0 + 3 < p));
     }
     pair_index[pos] = p;
   }

@@ -97,6 +97,26 @@ def test_route_many_ties():
     check_routing(lg, 10, r)
 
 
+@pytest.mark.parametrize("E,k,tied", [(512, 10, 512), (512, 10, 100), (512, 10, 30),
+                                       (1024, 64, 200), (64, 8, 12)])
+def test_route_tied_threshold(E, k, tied):
+    # `tied` experts share the largest logit: more than 64 of them at the threshold makes
+    # the selection fall back to wave-maximum rounds; fewer are ranked as candidates
+    rng = np.random.default_rng(E + k + tied)
+    n = 6
+    lg = rng.normal(size=(n, E)).astype(np.float32) - 10.0
+    for t in range(n):
+        lg[t, rng.permutation(E)[:tied]] = 3.0 if t % 2 else -0.0
+    for fused in (False, True):
+        if fused:
+            w, host, _, x = _small(E, 64, 64, k, n, 4)
+            _layer_vs_two_calls(w, host, lg, x)
+        else:
+            r = qmoe.route(to_dev(lg), k)
+            torch.cuda.synchronize()
+            check_routing(lg, k, r)
+
+
 def test_route_many_ties_many_workgroups():
     # ties across chunk boundaries of the multi-workgroup grouping
     rng = np.random.default_rng(4)
