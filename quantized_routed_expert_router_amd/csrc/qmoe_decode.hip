@@ -119,12 +119,7 @@ __device__ __forceinline__ void build_work_list(const int32_t* off, const int32_
   const int beg = e < E ? off[e] : 0;
   const int c = e < E ? off[e + 1] - beg : 0;
   const int cnt = (c + npc - 1) / npc;
-  int incl = cnt;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int v = __shfl_up(incl, o);
-    if (lane >= o) incl += v;
-  }
+  const int incl = wave_inclusive_scan(cnt);
   if (lane == kWave - 1) s_wsum[wave] = incl;
   __syncthreads();
   int base = incl - cnt;

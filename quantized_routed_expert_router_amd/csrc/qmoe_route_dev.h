@@ -40,6 +40,19 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   return (uint32_t)__builtin_amdgcn_readlane((int)v, kWave - 1);
 }
 
+// Inclusive prefix sum over the wavefront with DPP: row shifts by 1, 2, 4 and 8 (lanes
+// without a source add 0), then row 0's total into row 1 and row 2's into row 3
+// (row_bcast:15), then rows 0-1's total into rows 2-3 (row_bcast:31).
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xF, 0xF, false);  // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xF, 0xF, false);  // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xF, 0xF, false);  // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xF, 0xF, false);  // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xA, 0xF, false);  // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xC, 0xF, false);  // row_bcast:31
+  return v;
+}
+
 __device__ __forceinline__ double readlane_f64(double v, int lane) {
   uint64_t u;
   __builtin_memcpy(&u, &v, 8);
@@ -52,9 +65,9 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
 }
 
 // Per-wave LDS scratch of the threshold selection in wave_topk.
-struct TopkScratch {
-  uint32_t key[kWave];
-  int id[kWave];
+struct alignas(16) TopkScratch {
+  uint32_t key[kWave + 4];  // 4 entries of padding for the 4-wide rank loop
+  int id[kWave + 4];
   uint32_t slot_key[MOE_MAX_TOP_K];
   int slot_id[MOE_MAX_TOP_K];
 };
@@ -115,13 +128,27 @@ __device__ int wave_topk(const float* __restrict__ lrow, int E, int k, int32_t* 
   int my_id = 0;
   uint32_t my_bits = 0;
   if (total <= kWave) {
+    if (lane < 4) {  // padding: key 0 is below every candidate
+      sc->key[total + lane] = 0u;
+      sc->id[total + lane] = 0x7fffffff;
+    }
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (lane < total) {
       const uint32_t mk = sc->key[lane];
       const int mi = sc->id[lane];
       int rank = 0;
-      for (int q = 0; q < total; ++q) {
-        const uint32_t qk = sc->key[q];
-        rank += (qk > mk) | ((qk == mk) & (sc->id[q] < mi));
+      const uint4* k4 = reinterpret_cast<const uint4*>(sc->key);
+      const int4* i4 = reinterpret_cast<const int4*>(sc->id);
+#pragma unroll 4
+      for (int q = 0; q < (total + 3) / 4; ++q) {
+        const uint4 kq = k4[q];
+        const int4 iq = i4[q];
+        rank += (kq.x > mk) | ((kq.x == mk) & (iq.x < mi));
+        rank += (kq.y > mk) | ((kq.y == mk) & (iq.y < mi));
+        rank += (kq.z > mk) | ((kq.z == mk) & (iq.z < mi));
+        rank += (kq.w > mk) | ((kq.w == mk) & (iq.w < mi));
       }
       if (rank < k) {
         sc->slot_key[rank] = mk;
