@@ -623,6 +623,135 @@ __global__ __launch_bounds__(kThreads) void k_combine(const double* __restrict__
   residual[gid] = (float)((double)residual[gid] + acc);
 }
 
+// ---------------------------------------------------------------- down + combine, token-major
+//
+// For small windows the down projection is organised by token instead of by expert: a
+// workgroup owns (token t, 32 rows of d), computes those rows of the down outputs of all
+// k pairs of t and applies the routing-weighted combine itself (slot order, binary64), so
+// the pair outputs never leave the workgroup and the combine needs no launch of its own.
+// An expert shared by several tokens of the window is read once per token; the row tiles
+// are laid out so that all tokens of one row tile run on one XCD, whose L2 then serves
+// the repeats. Lane l of wave w owns row l%32 and the experts j = l/32, l/32 + 2, ... of
+// the token, for blocks w, w+8, ... of f; all of its U*I weight blocks are requested at
+// once (the whole token at f = 768, k = 10), the token's h codes and scales are staged in
+// LDS meanwhile, and the 8 waves' partial sums meet in LDS.
+constexpr int kDtRows = 32;
+constexpr int kDtWaves = 8;
+constexpr int kDtThreads = kDtWaves * kWave;
+constexpr int kDtMaxK = 16;       // top-k handled by this path
+constexpr int kDtMaxBlocks = 32;  // f/32 handled by this path
+constexpr int kDtMaxTokens = 16;  // window tokens handled by this path
+constexpr int kDtSlots = 16;      // weight blocks in flight per lane
+
+template <int BITS, int U, bool DBG>
+__global__ __launch_bounds__(kDtThreads) void k_down_tok(
+    const uint32_t* __restrict__ dcodes, const uint32_t* __restrict__ dsm, int d, int f, int k,
+    int n, const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w,
+    const int8_t* __restrict__ hq, const double2* __restrict__ hsc, float* residual,
+    DecodeDebug dbg) {
+  constexpr int I = kDtSlots / U;  // experts per lane half
+  __shared__ int4 s_act[kDtMaxK * kDtMaxBlocks * 3];
+  __shared__ double red[kDtWaves][kDtMaxK][kDtRows];
+  const int nbf = f / 32, nrt = d / kDtRows;
+  const int per = (nrt + 7) / 8;  // row tiles per XCD
+  const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
+  const int rt = xcd * per + slot / n, t = slot % n;
+  if (slot >= per * n || rt >= nrt) return;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int r = lane % kDtRows, h = lane / kDtRows;
+  const int row = rt * kDtRows + r;
+
+  // all weight blocks of this lane first (past k or nbf: a valid block, never used)
+  uint32_t w[I][U][BITS], smw[I][U];
+#pragma unroll
+  for (int i = 0; i < I; ++i) {
+    const int e = topk_ids[(size_t)t * k + min(h + 2 * i, k - 1)];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = min(wave + 8 * u, nbf - 1);
+      const size_t blk = ((size_t)e * nbf + b) * d + row;
+      if (BITS == 4) {
+        const uint4 v = *reinterpret_cast<const uint4*>(dcodes + blk * 4);
+        w[i][u][0] = v.x;
+        w[i][u][1] = v.y;
+        w[i][u][2 % BITS] = v.z;
+        w[i][u][3 % BITS] = v.w;
+      } else {
+        const uint2 v = *reinterpret_cast<const uint2*>(dcodes + blk * 2);
+        w[i][u][0] = v.x;
+        w[i][u][1] = v.y;
+      }
+      smw[i][u] = dsm[blk];
+    }
+  }
+  // the token's h codes and scales: entry (j, b) = 32 code bytes, then (scale, scale*sum)
+  for (int idx = tid; idx < k * nbf * 3; idx += kDtThreads) {
+    const int jb = idx / 3, part = idx % 3;
+    const int j = jb / nbf, b = jb % nbf;
+    const size_t p = (size_t)t * k + j;
+    s_act[idx] = part < 2 ? *reinterpret_cast<const int4*>(hq + p * f + 32 * b + 16 * part)
+                          : *reinterpret_cast<const int4*>(hsc + p * nbf + b);
+  }
+  __syncthreads();
+  double acc[I];
+#pragma unroll
+  for (int i = 0; i < I; ++i) {
+    acc[i] = 0.0;
+    const int j = h + 2 * i;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = wave + 8 * u;
+      if (j < k && b < nbf) {
+        const int4* e3 = s_act + (j * nbf + b) * 3;
+        const int4 a0 = e3[0], a1 = e3[1], scv = e3[2];
+        const int a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+        double2 sc;
+        __builtin_memcpy(&sc, &scv, 16);
+        const int dd = block_dot<BITS>(w[i][u], a);
+        const double s = half_bits_to_double(smw[i][u] & 0xffffu);
+        const double m = half_bits_to_double(smw[i][u] >> 16);
+        acc[i] = __builtin_fma(s * sc.x, (double)dd, acc[i]);  // exact terms: see k_gateup
+        acc[i] = __builtin_fma(m, sc.y, acc[i]);
+        if (DBG && dbg.down_dots) dbg.down_dots[(((size_t)t * k + j) * d + row) * nbf + b] = dd;
+      }
+    }
+    if (j < k) red[wave][j][r] = acc[i];
+  }
+  __syncthreads();
+  if (wave == 0 && lane < kDtRows) {
+    double tot = 0.0;
+    for (int j = 0; j < k; ++j) {  // slot order
+      double y = red[0][j][r];
+#pragma unroll
+      for (int w2 = 1; w2 < kDtWaves; ++w2) y += red[w2][j][r];  // wave order
+      if (DBG && dbg.y) dbg.y[((size_t)t * k + j) * d + row] = (float)y;
+      tot += (double)topk_w[(size_t)t * k + j] * y;
+    }
+    residual[(size_t)t * d + row] = (float)((double)residual[(size_t)t * d + row] + tot);
+  }
+}
+
+template <int BITS, bool DBG>
+hipError_t launch_down_tok(const DecodeArgs& a, const int8_t* hq, const double2* hsc,
+                           const DecodeDebug& dbg, int U) {
+  const moe_layer& L = *a.L;
+  const int d = L.d_model, f = L.d_ff, k = L.top_k, n = a.n;
+  const int per = (d / kDtRows + 7) / 8;
+  const dim3 grid(8 * per * n), block(kDtThreads);
+  const uint32_t* sm = reinterpret_cast<const uint32_t*>(L.down.scale_min);
+#define QMOE_DT(UU)                                                                            \
+  hipLaunchKernelGGL((k_down_tok<BITS, UU, DBG>), grid, block, 0, a.stream, L.down.codes, sm, d, \
+                     f, k, n, a.r->topk_ids, a.r->topk_w, hq, hsc, a.residual, dbg)
+  switch (U) {
+    case 1: QMOE_DT(1); break;
+    case 2: QMOE_DT(2); break;
+    case 3: QMOE_DT(3); break;
+    default: QMOE_DT(4); break;
+  }
+#undef QMOE_DT
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------- host side
 
 template <int BITS, int NPC, bool DBG>
@@ -685,6 +814,12 @@ hipError_t launch_ffn(const DecodeArgs& a) {
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
+  // down and combine together for a small window: the token-major kernel does both
+  const int nbf = f / 32, dt_u = (nbf + 7) / 8;
+  const bool token_major = (a.stages & MOE_DECODE_DOWN) && (a.stages & MOE_DECODE_COMBINE) &&
+                           n <= kDtMaxTokens && k <= kDtMaxK && nbf <= kDtMaxBlocks &&
+                           (k + 1) / 2 <= kDtSlots / dt_u;
+  if (token_major) return launch_down_tok<BITS, DBG>(a, hq, hsc, dbg, dt_u);
   if (a.stages & MOE_DECODE_DOWN) {
     const long long dn_items = max_chunks * ((d + kWave - 1) / kWave);
     const int dn_grid = (int)std::max<long long>(1, std::min<long long>(dn_items, cap));

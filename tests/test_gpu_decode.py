@@ -348,3 +348,31 @@ def test_layer_decode_zero_tokens_writes_empty_offsets():
     qmoe.layer_decode(layer, torch.empty((0, w.E), device="cuda"), empty, empty, routing=r)
     torch.cuda.synchronize()
     assert not r.expert_offsets.any()
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_decode_separate_down_and_combine_stages(bits):
+    # down and combine issued as separate stages take the expert-major down kernel and the
+    # combine launch; together (the default) they take the token-major kernel
+    w, host, lg, x = _small(32, 256, 128, 6, 4, bits, seed=5)
+    layer = workloads.layer_from_host(*host, w.k)
+    routing = qmoe.route(to_dev(lg), w.k)
+    ids, wt = check_routing(lg, w.k, routing)
+    out_o, _ = O.ffn_decode(*(omat(h) for h in host), w.E, x, ids, wt, x)
+    outs = []
+    for split in (True, False):
+        res = to_dev(x)
+        ws = qmoe.workspace(layer, w.n)
+        if split:
+            for st in (qmoe.DECODE_PREP, qmoe.DECODE_GATE_UP, qmoe.DECODE_DOWN,
+                       qmoe.DECODE_COMBINE):
+                qmoe.ffn_decode(layer, to_dev(x), routing, res, ws=ws, stages=st)
+        else:
+            qmoe.ffn_decode(layer, to_dev(x), routing, res, ws=ws)
+        torch.cuda.synchronize()
+        out = res.cpu().numpy()
+        assert_output_tolerance(out, out_o)
+        assert_output_tolerance(out - x, out_o - x, what="moe delta")
+        outs.append(out)
+    # the two paths sum the pair outputs in different orders: equal to the last ulps
+    np.testing.assert_allclose(outs[0], outs[1], rtol=1e-6, atol=1e-7)
