@@ -87,16 +87,25 @@ struct alignas(16) TopkScratch {
 // Weights are exp(l_j - l_0) / sum_i exp(l_i - l_0) in binary64, summed in slot order.
 // Lane j < k writes slot j and returns its expert id.
 template <int KPL>
-__device__ int wave_topk(const float* __restrict__ lrow, int E, int k, int32_t* __restrict__ ids,
-                         float* __restrict__ w, TopkScratch* sc) {
+__device__ __forceinline__ int wave_topk(const float* __restrict__ lrow, int E, int k,
+                                         int32_t* __restrict__ ids, float* __restrict__ w,
+                                         TopkScratch* sc) {
   const int lane = threadIdx.x & (kWave - 1);
+  // All KPL loads are issued unconditionally (clamped index) and pinned by an empty asm
+  // that uses every value: a load feeding only a guarded expression is otherwise sunk into
+  // a branch of its own with a wait behind it, one memory round trip per slot.
+  float lv[KPL];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) lv[i] = lrow[min(lane + kWave * i, E - 1)];
+#pragma unroll
+  for (int i = 0; i < KPL; ++i) asm volatile("" : "+v"(lv[i]));
   uint32_t key[KPL];
 #pragma unroll
   for (int i = 0; i < KPL; ++i) {
     const int e = lane + kWave * i;
     // valid experts never take 0 (only one NaN pattern maps there), so every round finds
     // a maximum held by some untaken expert while j < k <= E
-    key[i] = e < E ? max(order_bits(lrow[e]), 1u) : 0u;
+    key[i] = e < E ? max(order_bits(lv[i]), 1u) : 0u;
   }
   uint32_t lmax = key[0];
 #pragma unroll
@@ -202,7 +211,7 @@ __device__ int wave_topk(const float* __restrict__ lrow, int E, int k, int32_t* 
 }
 
 // Exclusive scan of v[0..n) (n <= 2 * blockDim.x) in LDS; wsum holds one int per wave.
-__device__ inline void block_exclusive_scan(int* v, int n, int* wsum) {
+__device__ __forceinline__ void block_exclusive_scan(int* v, int n, int* wsum) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int a = 2 * tid < n ? v[2 * tid] : 0;
   const int b = 2 * tid + 1 < n ? v[2 * tid + 1] : 0;
@@ -230,7 +239,7 @@ __device__ inline void block_exclusive_scan(int* v, int n, int* wsum) {
 // Per-wave histograms in LDS, a scan, and an in-order scatter where lanes holding the same
 // expert are ranked with ballots over the bits of the expert id.
 template <int NW>
-__device__ void group_block(const int32_t* ids, int P, int E, int* hist, int* s_off, int* wsum,
+__device__ __forceinline__ void group_block(const int32_t* ids, int P, int E, int* hist, int* s_off, int* wsum,
                             int32_t* offsets, int32_t* __restrict__ pair_index) {
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int nt = blockDim.x;
@@ -291,7 +300,7 @@ __device__ void group_block(const int32_t* ids, int P, int E, int* hist, int* s_
 // gives it. O(P) LDS broadcasts per thread, no atomics and no scans.
 constexpr int kSmallPairs = 256;
 
-__device__ inline void group_small(const int* s_ids, int P, int E, int32_t* __restrict__ offsets,
+__device__ __forceinline__ void group_small(const int* s_ids, int P, int E, int32_t* __restrict__ offsets,
                                    int32_t* __restrict__ pair_index) {
   // s_ids holds P ids followed by padding up to a multiple of 4 filled with INT_MAX, which
   // is neither below nor equal to any expert id
