@@ -377,10 +377,13 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
   const int rl = lane % kGuRows;
   const uint32_t* __restrict__ codes = mat ? ucodes : gcodes;
   const uint32_t* __restrict__ smp = mat ? usm : gsm;
-  // One scalar load of a chunk's work record gives expert, pair and token ids. The grid
-  // never exceeds max_chunks * ntiles, so the first record is inside the work-list buffer.
-  int item = blockIdx.x;
-  const int nitems = load_uniform(nchunks) * ntiles;
+  // One item per workgroup: the grid covers the largest possible item count and the
+  // workgroups past the live count exit. (A loop over items would make the compiler's wait
+  // counts conservative at its head: the first weight requests would wait for the
+  // activation staging.) One scalar load of a chunk's work record gives expert, pair and
+  // token ids; the grid never exceeds max_chunks * ntiles, so the record is inside the
+  // work-list buffer.
+  const int item = blockIdx.x;
   int e, np, pid[NPC];
   const int* rec_rows;  // token ids of the chunk's pairs (activation rows)
   auto read_record = [&](int it) {
@@ -391,9 +394,14 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
     for (int j = 0; j < NPC; ++j) pid[j] = load_uniform(rec + 4 + j);
   };
+  // The first record, the live chunk count and the weight pointers are fetched together:
+  // the empty asm needs all of them, so no load is sunk behind the loop test (which would
+  // chain two or three round trips before the first weight request).
   read_record(item);
-  for (; item < nitems; item += gridDim.x) {
-    if (item != (int)blockIdx.x) read_record(item);
+  int nch = load_uniform(nchunks);
+  asm volatile("" : "+s"(nch) : "s"(e), "s"(np), "s"(gcodes), "s"(gsm), "s"(ucodes), "s"(usm));
+  const int nitems = nch * ntiles;
+  if (item < nitems) {
     const int tile = item % ntiles;
     const int r = tile * kGuRows + rl;
     double acc[NPC];
@@ -412,9 +420,11 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
 #pragma unroll
       for (int u = 0; u < kGuUnroll; ++u) {
         // blocks past the end (partial last group) re-read the last block; never used
+        // ke differs between the two halves of the wave, so the whole offset goes into the
+        // per-lane offset (a lane-varying scalar offset would split every load in two)
         const int b = min(g0 + ke + kGuSplit * u, nbd - 1);
-        BlockLoad<BITS>::load(rs_c, r * BITS * 4, b * f * BITS * 4, w[u]);
-        smw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, r * 4, b * f * 4, 0);
+        BlockLoad<BITS>::load(rs_c, (b * f + r) * BITS * 4, 0, w[u]);
+        smw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, (b * f + r) * 4, 0, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<2 * kGuUnroll>();  // this wave's staging loads have landed
@@ -444,6 +454,15 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
             }
           }
         }
+      }
+      // Blocks past the reduction axis leave their loads unused; the empty asm takes every
+      // loaded register, so no load is outstanding at the loop's back edge (the compiler
+      // would otherwise wait for all loads, the new group's staging included, at the head).
+#pragma unroll
+      for (int u = 0; u < kGuUnroll; ++u) {
+#pragma unroll
+        for (int q = 0; q < BITS; ++q) asm volatile("" ::"v"(w[u][q]));
+        asm volatile("" ::"v"(smw[u]));
       }
     }
     // the two reduction halves of a row sit in lanes l and l+32
@@ -632,9 +651,13 @@ __global__ __launch_bounds__(kThreads) void k_combine(const double* __restrict__
 // An expert shared by several tokens of the window is read once per token; the row tiles
 // are laid out so that all tokens of one row tile run on one XCD, whose L2 then serves
 // the repeats. Lane l of wave w owns row l%32 and the experts j = l/32, l/32 + 2, ... of
-// the token, for blocks w, w+8, ... of f; all of its U*I weight blocks are requested at
-// once (the whole token at f = 768, k = 10), the token's h codes and scales are staged in
-// LDS meanwhile, and the 8 waves' partial sums meet in LDS.
+// the token, for blocks w, w+8, ... of f.
+//
+// Order of requests: the experts of the lane's pairs, the token's residual values and its
+// h codes and scales go out first; then all U*I weight blocks of the lane (the whole token
+// at f = 768, k = 10), then the routing weights (scalar loads, needed only at the end). The wave waits only for the h loads
+// before writing them to LDS and meeting the barrier, and each block's dots start as
+// soon as that block has landed. The 8 waves' partial sums meet in LDS.
 constexpr int kDtRows = 32;
 constexpr int kDtWaves = 8;
 constexpr int kDtThreads = kDtWaves * kWave;
@@ -642,6 +665,8 @@ constexpr int kDtMaxK = 16;       // top-k handled by this path
 constexpr int kDtMaxBlocks = 32;  // f/32 handled by this path
 constexpr int kDtMaxTokens = 16;  // window tokens handled by this path
 constexpr int kDtSlots = 16;      // weight blocks in flight per lane
+constexpr int kDtStage = kDtMaxK * kDtMaxBlocks * 3;  // 16-byte LDS entries of h
+static_assert(kDtStage % kDtThreads == 0, "staging is whole wave-level loads");
 
 template <int BITS, int U, bool DBG>
 __global__ __launch_bounds__(kDtThreads) void k_down_tok(
@@ -650,22 +675,50 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
     const int8_t* __restrict__ hq, const double2* __restrict__ hsc, float* residual,
     DecodeDebug dbg) {
   constexpr int I = kDtSlots / U;  // experts per lane half
-  __shared__ int4 s_act[kDtMaxK * kDtMaxBlocks * 3];
-  __shared__ double red[kDtWaves][kDtMaxK][kDtRows];
+  __shared__ int4 s_act[kDtStage];
+  __shared__ double red[kDtWaves][kDtMaxK + 1][kDtRows];  // slot kDtMaxK: unused pairs
   const int nbf = f / 32, nrt = d / kDtRows;
   const int per = (nrt + 7) / 8;  // row tiles per XCD
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int rt = xcd * per + slot / n, t = slot % n;
   if (slot >= per * n || rt >= nrt) return;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int r = lane % kDtRows, h = lane / kDtRows;
   const int row = rt * kDtRows + r;
 
-  // all weight blocks of this lane first (past k or nbf: a valid block, never used)
+  // experts of the lane's pairs j = h, h+2, ... (slots past k repeat slot k-1, never used)
+  int eid[I];
+#pragma unroll
+  for (int i = 0; i < I; ++i) eid[i] = topk_ids[(size_t)t * k + min(h + 2 * i, k - 1)];
+  const bool epi = wave == 0 && lane < kDtRows;
+  const float res0 = residual[(size_t)t * d + (epi ? row : rt * kDtRows)];
+
+  // h of the token into registers: entry (j, b) = 32 code bytes, then (scale, scale*sum);
+  // entries past the end repeat the last one. They are written to LDS after the weight
+  // requests, so the compiler's own wait for them leaves the weight loads in flight.
+  typedef int v4i __attribute__((ext_vector_type(4)));
+  v4i stg[kDtStage / kDtThreads];
+  {
+    const int total = k * nbf * 3;
+#pragma unroll
+    for (int it = 0; it < kDtStage / kDtThreads; ++it) {
+      const int idx = min(it * kDtThreads + tid, total - 1);
+      const int jb = idx / 3, part = idx % 3;
+      const int j = jb / nbf, b = jb % nbf;
+      const size_t p = (size_t)t * k + j;
+      const uintptr_t src = part < 2 ? reinterpret_cast<uintptr_t>(hq + p * f + 32 * b + 16 * part)
+                                     : reinterpret_cast<uintptr_t>(hsc + p * nbf + b);
+      stg[it] = *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(src);
+    }
+  }
+  __builtin_amdgcn_sched_barrier(0);
+
+  // all weight blocks of this lane (past k or nbf: a valid block, never used)
   uint32_t w[I][U][BITS], smw[I][U];
 #pragma unroll
   for (int i = 0; i < I; ++i) {
-    const int e = topk_ids[(size_t)t * k + min(h + 2 * i, k - 1)];
+    const int e = eid[i];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int b = min(wave + 8 * u, nbf - 1);
@@ -684,15 +737,21 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
       smw[i][u] = dsm[blk];
     }
   }
-  // the token's h codes and scales: entry (j, b) = 32 code bytes, then (scale, scale*sum)
-  for (int idx = tid; idx < k * nbf * 3; idx += kDtThreads) {
-    const int jb = idx / 3, part = idx % 3;
-    const int j = jb / nbf, b = jb % nbf;
-    const size_t p = (size_t)t * k + j;
-    s_act[idx] = part < 2 ? *reinterpret_cast<const int4*>(hq + p * f + 32 * b + 16 * part)
-                          : *reinterpret_cast<const int4*>(hsc + p * nbf + b);
-  }
+  __builtin_amdgcn_sched_barrier(0);
+  // routing weights of the token, for the combine (uniform: scalar loads, needed last)
+  float sw[kDtMaxK];
+#pragma unroll
+  for (int j = 0; j < kDtMaxK; ++j)
+    sw[j] = __int_as_float(
+        load_uniform(reinterpret_cast<const int*>(topk_w) + (size_t)t * k + min(j, k - 1)));
+#pragma unroll
+  for (int it = 0; it < kDtStage / kDtThreads; ++it)
+    reinterpret_cast<v4i*>(s_act)[it * kDtThreads + tid] = stg[it];
   __syncthreads();
+
+  // Every block is computed and the unused ones (past k or nbf) are dropped by a select:
+  // a weight load feeding only a guarded branch would be sunk into it, behind a full wait.
+  // Unused blocks read LDS entries inside s_act (j < kDtMaxK, b < kDtMaxBlocks).
   double acc[I];
 #pragma unroll
   for (int i = 0; i < I; ++i) {
@@ -701,33 +760,37 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int b = wave + 8 * u;
-      if (j < k && b < nbf) {
-        const int4* e3 = s_act + (j * nbf + b) * 3;
-        const int4 a0 = e3[0], a1 = e3[1], scv = e3[2];
-        const int a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
-        double2 sc;
-        __builtin_memcpy(&sc, &scv, 16);
-        const int dd = block_dot<BITS>(w[i][u], a);
-        const double s = half_bits_to_double(smw[i][u] & 0xffffu);
-        const double m = half_bits_to_double(smw[i][u] >> 16);
-        acc[i] = __builtin_fma(s * sc.x, (double)dd, acc[i]);  // exact terms: see k_gateup
-        acc[i] = __builtin_fma(m, sc.y, acc[i]);
-        if (DBG && dbg.down_dots) dbg.down_dots[(((size_t)t * k + j) * d + row) * nbf + b] = dd;
-      }
+      const bool use = j < k && b < nbf;
+      const int4* e3 = s_act + (j * nbf + b) * 3;
+      const int4 a0 = e3[0], a1 = e3[1], scv = e3[2];
+      const int a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
+      double2 sc;
+      __builtin_memcpy(&sc, &scv, 16);
+      const int dd = block_dot<BITS>(w[i][u], a);
+      const double s = half_bits_to_double(smw[i][u] & 0xffffu);
+      const double m = half_bits_to_double(smw[i][u] >> 16);
+      // exact terms: see k_gateup
+      const double v = __builtin_fma(m, sc.y, __builtin_fma(s * sc.x, (double)dd, acc[i]));
+      acc[i] = use ? v : acc[i];
+      if (DBG && use && dbg.down_dots)
+        dbg.down_dots[(((size_t)t * k + j) * d + row) * nbf + b] = dd;
     }
-    if (j < k) red[wave][j][r] = acc[i];
+    red[wave][j < k ? j : kDtMaxK][r] = acc[i];  // unconditional: see above
   }
   __syncthreads();
-  if (wave == 0 && lane < kDtRows) {
+  if (epi) {
     double tot = 0.0;
-    for (int j = 0; j < k; ++j) {  // slot order
-      double y = red[0][j][r];
 #pragma unroll
-      for (int w2 = 1; w2 < kDtWaves; ++w2) y += red[w2][j][r];  // wave order
-      if (DBG && dbg.y) dbg.y[((size_t)t * k + j) * d + row] = (float)y;
-      tot += (double)topk_w[(size_t)t * k + j] * y;
+    for (int j = 0; j < kDtMaxK; ++j) {  // slot order
+      if (j < k) {
+        double y = red[0][j][r];
+#pragma unroll
+        for (int w2 = 1; w2 < kDtWaves; ++w2) y += red[w2][j][r];  // wave order
+        if (DBG && dbg.y) dbg.y[((size_t)t * k + j) * d + row] = (float)y;
+        tot += (double)sw[j] * y;
+      }
     }
-    residual[(size_t)t * d + row] = (float)((double)residual[(size_t)t * d + row] + tot);
+    residual[(size_t)t * d + row] = (float)((double)res0 + tot);
   }
 }
 
@@ -800,13 +863,16 @@ hipError_t launch_ffn(const DecodeArgs& a) {
     if (err != hipSuccess) return err;
   }
 
-  // upper bound of chunks: every chunk holds >= 1 pair, and an expert holds <= n pairs
-  const long long max_chunks =
-      std::min<long long>((long long)n * k, (long long)E * ((n + NPC - 1) / NPC));
+  // upper bound of chunks: every chunk holds >= 1 pair, an expert holds <= n pairs, and
+  // sum_e ceil(c_e / NPC) <= P / NPC + (number of experts with pairs)
+  const long long P = (long long)n * k;
+  const long long max_chunks = std::min<long long>(
+      std::min<long long>(P, (long long)E * ((n + NPC - 1) / NPC)),
+      (P + NPC - 1) / NPC + std::min<long long>(E, P));
   const int cap = a.num_cus * 8;
   if (a.stages & MOE_DECODE_GATE_UP) {
-    const long long gu_items = max_chunks * (f / kGuRows);
-    const int gu_grid = (int)std::max<long long>(1, std::min<long long>(gu_items, cap));
+    const long long gu_items = max_chunks * (f / kGuRows);  // one workgroup per item
+    const int gu_grid = (int)std::max<long long>(1, gu_items);
     hipLaunchKernelGGL((k_gateup<BITS, NPC, DBG>), dim3(gu_grid), dim3(kGuThreads), 0, a.stream,
                        L.gate.codes, reinterpret_cast<const uint32_t*>(L.gate.scale_min),
                        L.up.codes, reinterpret_cast<const uint32_t*>(L.up.scale_min), d, f,
