@@ -193,7 +193,9 @@ __global__ __launch_bounds__(kPrepThreads) void k_route_prep(
     }
     if (tid < 4 && P + tid < ((P + 3) & ~3)) s_ids[P + tid] = 0x7fffffff;  // group_small pad
     __syncthreads();
-    if (P <= kSmallPairs)
+    if (P <= kWave)
+      group_tiny(s_ids, P, E, s_off, s_pidx);
+    else if (P <= kSmallPairs)
       group_small(s_ids, P, E, s_off, s_pidx);
     else
       group_block<kFusedGroupWaves>(s_ids, P, E, s_hist, s_off, s_wsum, s_off, s_pidx);

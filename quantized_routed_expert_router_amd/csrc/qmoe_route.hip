@@ -44,7 +44,9 @@ __global__ __launch_bounds__(kGroupThreads) void k_route_fused(
     s_ids[P + threadIdx.x] = 0x7fffffff;  // padding read by group_small
   __threadfence_block();
   __syncthreads();
-  if (P <= kSmallPairs)
+  if (P <= kWave)
+    group_tiny(s_ids, P, E, offsets, pair_index);
+  else if (P <= kSmallPairs)
     group_small(s_ids, P, E, offsets, pair_index);
   else
     group_block<kGroupWaves>(ids, P, E, s_hist, s_off, s_wsum, offsets, pair_index);

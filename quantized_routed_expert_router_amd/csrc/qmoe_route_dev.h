@@ -66,8 +66,8 @@ __device__ __forceinline__ double readlane_f64(double v, int lane) {
 
 // Per-wave LDS scratch of the threshold selection in wave_topk.
 struct alignas(16) TopkScratch {
-  uint32_t key[kWave + 4];  // 4 entries of padding for the 4-wide rank loop
-  int id[kWave + 4];
+  uint32_t key[kWave];  // compacted candidates
+  int id[kWave];
   uint32_t slot_key[MOE_MAX_TOP_K];
   int slot_id[MOE_MAX_TOP_K];
 };
@@ -137,32 +137,26 @@ __device__ __forceinline__ int wave_topk(const float* __restrict__ lrow, int E, 
   int my_id = 0;
   uint32_t my_bits = 0;
   if (total <= kWave) {
-    if (lane < 4) {  // padding: key 0 is below every candidate
-      sc->key[total + lane] = 0u;
-      sc->id[total + lane] = 0x7fffffff;
+    // Each candidate is ranked by counting the candidates ahead of it. A candidate's
+    // (key desc, id asc) order is the unsigned order of key:~id (ids are below 2^31), and
+    // the wave reads the others' packed keys lane by lane from registers.
+    const uint32_t mk = lane < total ? sc->key[lane] : 0u;
+    const int mi = lane < total ? sc->id[lane] : 0x7fffffff;
+    const uint32_t mlo = ~(uint32_t)mi;
+    // chunks of 8 lanes (total <= 64 keeps them inside the wave); lanes past total hold
+    // key 0, which never ranks ahead of a candidate (candidate keys are >= T >= 1)
+    int rank = 0;
+    for (int q0 = 0; q0 < total; q0 += 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t qk = (uint32_t)__builtin_amdgcn_readlane((int)mk, q0 + i);
+        const uint32_t ql = (uint32_t)__builtin_amdgcn_readlane((int)mlo, q0 + i);
+        rank += (qk > mk) | ((qk == mk) & (ql > mlo));
+      }
     }
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    if (lane < total) {
-      const uint32_t mk = sc->key[lane];
-      const int mi = sc->id[lane];
-      int rank = 0;
-      const uint4* k4 = reinterpret_cast<const uint4*>(sc->key);
-      const int4* i4 = reinterpret_cast<const int4*>(sc->id);
-#pragma unroll 4
-      for (int q = 0; q < (total + 3) / 4; ++q) {
-        const uint4 kq = k4[q];
-        const int4 iq = i4[q];
-        rank += (kq.x > mk) | ((kq.x == mk) & (iq.x < mi));
-        rank += (kq.y > mk) | ((kq.y == mk) & (iq.y < mi));
-        rank += (kq.z > mk) | ((kq.z == mk) & (iq.z < mi));
-        rank += (kq.w > mk) | ((kq.w == mk) & (iq.w < mi));
-      }
-      if (rank < k) {
-        sc->slot_key[rank] = mk;
-        sc->slot_id[rank] = mi;
-      }
+    if (lane < total && rank < k) {
+      sc->slot_key[rank] = mk;
+      sc->slot_id[rank] = mi;
     }
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -329,6 +323,36 @@ __device__ __forceinline__ void group_small(const int* s_ids, int P, int E, int3
       pos += (v.w < ep) | ((v.w == ep) & (q0 + 3 < p));
     }
     pair_index[pos] = p;
+  }
+}
+
+// The same stable grouping for P <= 64 pairs, from registers: every wave holds the P ids
+// in one register (lane q: ids[q]) and reads them back lane by lane. Thread e counts the
+// ids below e (offsets[e]); the last wave ranks the keys id*64 + p, which are distinct
+// and order the pairs by (expert, pair index), so pair p lands at its key's rank.
+__device__ __forceinline__ void group_tiny(const int* s_ids, int P, int E,
+                                           int32_t* __restrict__ offsets,
+                                           int32_t* __restrict__ pair_index) {
+  const int tid = threadIdx.x, nt = blockDim.x, lane = tid & (kWave - 1);
+  const int idv = lane < P ? s_ids[lane] : 0x7fffffff;
+  // wave-uniform loop: every lane is active around the lane reads
+  for (int e0 = tid - lane; e0 <= E; e0 += nt) {
+    const int e = e0 + lane;
+    int c = 0;
+    for (int q0 = 0; q0 < P; q0 += 8) {  // lanes past P hold INT_MAX: never counted
+#pragma unroll
+      for (int i = 0; i < 8; ++i) c += __builtin_amdgcn_readlane(idv, q0 + i) < e;
+    }
+    if (e <= E) offsets[e] = c;
+  }
+  if (tid >= nt - kWave) {
+    const int key = lane < P ? idv * kWave + lane : 0x7fffffff;
+    int pos = 0;
+    for (int q0 = 0; q0 < P; q0 += 8) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) pos += __builtin_amdgcn_readlane(key, q0 + i) < key;
+    }
+    if (lane < P) pair_index[pos] = lane;
   }
 }
 
