@@ -165,12 +165,13 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
 // Routing fused with prep for small batches (n <= kFusedMaxTokens): block 0 selects the
 // top-k experts of every token (one wavefront per token), groups the pairs by expert and
 // builds the work list without leaving LDS, writing the routing outputs on the way; the
-// other blocks quantize x meanwhile.
+// other blocks quantize x meanwhile. Without GROUP, block 0 stops after the top-k: the
+// gate/up kernel then takes its chunks from the expert ids and writes the grouping.
 constexpr int kFusedMaxTokens = 64;
 constexpr int kFusedMaxPairs = kFusedMaxTokens * MOE_MAX_TOP_K;
 constexpr int kFusedGroupWaves = 8;
 
-template <int BITS, int KPL>
+template <int BITS, int KPL, bool GROUP>
 __global__ __launch_bounds__(kPrepThreads) void k_route_prep(
     const float* __restrict__ logits, const float* __restrict__ x, int n, int d, int E, int k,
     int npc, int32_t* __restrict__ topk_ids, float* __restrict__ topk_w,
@@ -191,6 +192,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_route_prep(
                                     topk_w + (size_t)t * k, &s_tk[wave]);
       if (lane < k) s_ids[t * k + lane] = id;
     }
+    if (!GROUP) return;  // the gate/up kernel groups (chunks from ids)
     if (tid < 4 && P + tid < ((P + 3) & ~3)) s_ids[P + tid] = 0x7fffffff;  // group_small pad
     __syncthreads();
     if (P <= kWave)
@@ -313,11 +315,27 @@ struct ActLds {
   static constexpr int kPadded = kIter * NT;               // entries allocated
 };
 
-template <int NPC, int G, int NT>
+// Activation row of chunk pair jc (wave-uniform): from the work record in memory, or from
+// uniform registers.
+template <int N>
+struct RowSet {
+  int r[N];
+};
+__device__ __forceinline__ int chunk_row(const int* __restrict__ rows, int jc) {
+  return load_uniform(rows + jc);
+}
+template <int N>
+__device__ __forceinline__ int chunk_row(RowSet<N> rows, int jc) {
+  int r = rows.r[0];
+#pragma unroll
+  for (int j = 1; j < N; ++j) r = jc == j ? rows.r[j] : r;
+  return r;
+}
+
+template <int NPC, int G, int NT, class Rows>
 __device__ __forceinline__ void act_load_lds(int4* s_act, const int8_t* __restrict__ act,
-                                             const double2* __restrict__ sc,
-                                             const int* __restrict__ rows, int np, int g0, int nb,
-                                             int rowlen, int wave, int lane) {
+                                             const double2* __restrict__ sc, Rows rows, int np,
+                                             int g0, int nb, int rowlen, int wave, int lane) {
   constexpr int kTotal = ActLds<NPC, G, NT>::kTotal;
   static_assert((G * 3) % kWave == 0, "a wave-level load stays within one pair's entries");
   // Every wave issues kIter loads with no branch (a branch would make the compiler wait for
@@ -326,10 +344,9 @@ __device__ __forceinline__ void act_load_lds(int4* s_act, const int8_t* __restri
   for (int it = 0; it < ActLds<NPC, G, NT>::kIter; ++it) {
     const int wbase = it * NT + wave * kWave;  // wave-uniform
     const int src_base = min(wbase, kTotal - kWave);
-    // the pair is uniform across the wave: its activation row is a scalar load from the
-    // chunk's work record (rows[0..np))
+    // the pair is uniform across the wave, and so is its activation row
     const int jc = min(src_base / (G * 3), np - 1);
-    const int rj = load_uniform(rows + jc);
+    const int rj = chunk_row(rows, jc);
     const int rem = src_base % (G * 3) + lane;
     const int bb = rem / 3, part = rem % 3;
     const int b = min(g0 + bb, nb - 1);
@@ -359,15 +376,63 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-template <int BITS, int NPC, bool DBG>
+// Chunks straight from the routing (IDS): for windows of n <= NPC tokens and P = n*k <= 64
+// pairs every expert's pairs form one chunk, so a workgroup derives its item's chunk from
+// the P expert ids instead of reading a work list (one wavefront does it). Lane p holds
+// ids[p] and sets bit ids[p] of an expert bitset in LDS (a wave's LDS operations complete
+// in order, so no barrier is needed); chunks are the experts present, in ascending id
+// order: a scan of the words' popcounts finds the word holding chunk c and a bit walk the
+// expert. The chunk's pairs are the lanes holding that expert, in pair order. This saves
+// the routing kernel its grouping and work list, which sit on the critical path there. With `offsets` given,
+// workgroup 0 writes the routing's expert offsets and pair index (the grouping) while the
+// other workgroups stream, and item i runs on workgroup i + 1.
+constexpr int kExpertWords = MOE_MAX_EXPERTS / 32;
+static_assert(kExpertWords <= kWave, "one bitset word per lane");
+
+template <int NPC>
+struct IdsChunk {
+  int e, np, nch;
+  int pid[NPC];
+};
+
+template <int NPC>
+__device__ __forceinline__ IdsChunk<NPC> chunk_from_ids(const int32_t* __restrict__ topk_ids,
+                                                        int P, int c, int lane, uint32_t* s_bits) {
+  const int idv = lane < P ? topk_ids[lane] : -1;
+  if (lane < kExpertWords) s_bits[lane] = 0u;
+  if (lane < P) atomicOr(&s_bits[idv >> 5], 1u << (idv & 31));
+  const uint32_t word = lane < kExpertWords ? s_bits[lane] : 0u;
+  const int cnt = __popc(word);
+  const int incl = wave_inclusive_scan(cnt);
+  IdsChunk<NPC> ch;
+  ch.nch = __builtin_amdgcn_readlane(incl, kWave - 1);
+  const uint64_t hit = __ballot(incl > c && incl - cnt <= c);  // the word holding chunk c
+  const int w = hit ? __builtin_ctzll(hit) : 0;
+  uint32_t wb = (uint32_t)__builtin_amdgcn_readlane((int)word, w);
+  const int skip = c - (__builtin_amdgcn_readlane(incl, w) - __builtin_amdgcn_readlane(cnt, w));
+  for (int i = 0; i < skip && wb; ++i) wb &= wb - 1;
+  ch.e = 32 * w + (wb ? __builtin_ctz(wb) : 0);
+  uint64_t pm = __ballot(lane < P && idv == ch.e);
+  ch.np = __popcll(pm);
+#pragma unroll
+  for (int j = 0; j < NPC; ++j) {  // slots past np repeat the last pair
+    ch.pid[j] = pm ? __builtin_ctzll(pm) : (j ? ch.pid[j - 1] : 0);
+    if (j + 1 < ch.np) pm &= pm - 1;
+  }
+  return ch;
+}
+
+template <int BITS, int NPC, bool DBG, bool IDS>
 __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4))) void k_gateup(
     const uint32_t* __restrict__ gcodes, const uint32_t* __restrict__ gsm,
     const uint32_t* __restrict__ ucodes, const uint32_t* __restrict__ usm, int d, int f,
     const int* __restrict__ chunks, const int* __restrict__ nchunks, const int8_t* __restrict__ xq,
     const double2* __restrict__ xsc, int8_t* __restrict__ hq, double2* __restrict__ hsc,
-    DecodeDebug dbg) {
+    const int32_t* __restrict__ topk_ids, int k, int P, int E, int32_t* __restrict__ offsets,
+    int32_t* __restrict__ pair_index, DecodeDebug dbg) {
   __shared__ double red[kGuWaves][NPC][kGuRows];
   __shared__ int4 s_act_raw[ActLds<NPC, kGuGroup, kGuThreads>::kPadded];
+  __shared__ uint32_t s_bits[kExpertWords];
   int4 (*s_act)[kGuGroup][3] = reinterpret_cast<int4 (*)[kGuGroup][3]>(s_act_raw);
   const int nbd = d / 32, nbf = f / 32;
   const int ntiles = f / kGuRows;
@@ -382,26 +447,60 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
   // One item per workgroup: the grid covers the largest possible item count and the
   // workgroups past the live count exit. (A loop over items would make the compiler's wait
   // counts conservative at its head: the first weight requests would wait for the
-  // activation staging.) One scalar load of a chunk's work record gives expert, pair and
-  // token ids; the grid never exceeds max_chunks * ntiles, so the record is inside the
-  // work-list buffer.
-  const int item = blockIdx.x;
+  // activation staging.) Without IDS, scalar loads of a chunk's work record give expert,
+  // pair and token ids; the grid never exceeds max_chunks * ntiles, so the record is
+  // inside the work-list buffer.
   int e, np, pid[NPC];
-  const int* rec_rows;  // token ids of the chunk's pairs (activation rows)
-  auto read_record = [&](int it) {
-    const int* rec = chunks + (size_t)(it / ntiles) * kChunkInts;
-    rec_rows = rec + 4 + kMaxChunkPairs;
+  RowSet<NPC> rows;
+  int item = blockIdx.x, nch;
+  if (IDS) {
+    if (offsets) {
+      if (blockIdx.x == 0) {  // the grouping of the routing outputs
+        int* s_ids = reinterpret_cast<int*>(s_act_raw);
+        if (tid < P) s_ids[tid] = topk_ids[tid];
+        __syncthreads();
+        group_tiny(s_ids, P, E, offsets, pair_index);
+        return;
+      }
+      --item;
+    }
+    // wave 0 derives the chunk and hands it to the others through LDS (a derivation in
+    // every wave costs more: all waves of all workgroups would read the same ids)
+    __shared__ IdsChunk<NPC> s_ch;
+    if (wave == 0) {
+      const IdsChunk<NPC> c0 = chunk_from_ids<NPC>(topk_ids, P, item / ntiles, lane, s_bits);
+      if (lane == 0) s_ch = c0;
+    }
+    __syncthreads();
+    IdsChunk<NPC> ch;
+    ch.e = __builtin_amdgcn_readfirstlane(s_ch.e);
+    ch.np = __builtin_amdgcn_readfirstlane(s_ch.np);
+    ch.nch = __builtin_amdgcn_readfirstlane(s_ch.nch);
+#pragma unroll
+    for (int j = 0; j < NPC; ++j) ch.pid[j] = __builtin_amdgcn_readfirstlane(s_ch.pid[j]);
+    e = ch.e;
+    np = ch.np;
+    nch = ch.nch;
+#pragma unroll
+    for (int j = 0; j < NPC; ++j) {
+      pid[j] = ch.pid[j];
+      rows.r[j] = pid[j] / k;
+    }
+  } else {
+    // The record, the live chunk count and the weight pointers are fetched together: the
+    // empty asm needs all of them, so no load is sunk behind the item test (which would
+    // chain two or three round trips before the first weight request).
+    const int* rec = chunks + (size_t)(item / ntiles) * kChunkInts;
     e = load_uniform(rec);
     np = load_uniform(rec + 2);
 #pragma unroll
-    for (int j = 0; j < NPC; ++j) pid[j] = load_uniform(rec + 4 + j);
-  };
-  // The first record, the live chunk count and the weight pointers are fetched together:
-  // the empty asm needs all of them, so no load is sunk behind the loop test (which would
-  // chain two or three round trips before the first weight request).
-  read_record(item);
-  int nch = load_uniform(nchunks);
-  asm volatile("" : "+s"(nch) : "s"(e), "s"(np), "s"(gcodes), "s"(gsm), "s"(ucodes), "s"(usm));
+    for (int j = 0; j < NPC; ++j) {
+      pid[j] = load_uniform(rec + 4 + j);
+      rows.r[j] = load_uniform(rec + 4 + kMaxChunkPairs + j);
+    }
+    nch = load_uniform(nchunks);
+    asm volatile("" : "+s"(nch) : "s"(e), "s"(np), "s"(gcodes), "s"(gsm), "s"(ucodes), "s"(usm));
+  }
   const int nitems = nch * ntiles;
   if (item < nitems) {
     const int tile = item % ntiles;
@@ -416,7 +515,7 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     uint32_t w[kGuUnroll][BITS], smw[kGuUnroll];
     for (int g0 = 0; g0 < nbd; g0 += kGuGroup) {
       __syncthreads();  // earlier readers of s_act are done
-      act_load_lds<NPC, kGuGroup, kGuThreads>(s_act_raw, xq, xsc, rec_rows, np, g0, nbd, d, wave,
+      act_load_lds<NPC, kGuGroup, kGuThreads>(s_act_raw, xq, xsc, rows, np, g0, nbd, d, wave,
                                               lane);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -836,15 +935,21 @@ hipError_t launch_ffn(const DecodeArgs& a) {
 
   const int nbd = d / 32;
   hipError_t err = hipSuccess;
+  // chunks straight from the expert ids (see k_gateup); with logits, the gate/up stage also
+  // writes the routing's grouping
+  const bool ids = n <= NPC && (long long)n * k <= kWave;
   if (a.stages & MOE_DECODE_PREP) {
     const int prep_blocks = 1 + (n * nbd + kPrepThreads - 1) / kPrepThreads;
     if (a.logits && n <= kFusedMaxTokens) {
       const int kpl = (E + kWave - 1) / kWave;
-      auto kern = kpl <= 1   ? k_route_prep<BITS, 1>
-                  : kpl <= 2 ? k_route_prep<BITS, 2>
-                  : kpl <= 4 ? k_route_prep<BITS, 4>
-                  : kpl <= 8 ? k_route_prep<BITS, 8>
-                             : k_route_prep<BITS, 16>;
+#define QMOE_RP(G)                                                                        \
+  (kpl <= 1   ? k_route_prep<BITS, 1, G>                                                  \
+   : kpl <= 2 ? k_route_prep<BITS, 2, G>                                                  \
+   : kpl <= 4 ? k_route_prep<BITS, 4, G>                                                  \
+   : kpl <= 8 ? k_route_prep<BITS, 8, G>                                                  \
+              : k_route_prep<BITS, 16, G>)
+      auto kern = ids ? QMOE_RP(false) : QMOE_RP(true);
+#undef QMOE_RP
       hipLaunchKernelGGL(kern, dim3(prep_blocks), dim3(kPrepThreads), 0, a.stream, a.logits, a.x,
                          n, d, E, k, NPC, a.r->topk_ids, a.r->topk_w, a.r->expert_offsets,
                          a.r->pair_index, chunks, nchunks, xq, xsc, DBG ? dbg.xq : nullptr,
@@ -874,11 +979,19 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   const int cap = a.num_cus * 8;
   if (a.stages & MOE_DECODE_GATE_UP) {
     const long long gu_items = max_chunks * (f / kGuRows);  // one workgroup per item
-    const int gu_grid = (int)std::max<long long>(1, gu_items);
-    hipLaunchKernelGGL((k_gateup<BITS, NPC, DBG>), dim3(gu_grid), dim3(kGuThreads), 0, a.stream,
-                       L.gate.codes, reinterpret_cast<const uint32_t*>(L.gate.scale_min),
-                       L.up.codes, reinterpret_cast<const uint32_t*>(L.up.scale_min), d, f,
-                       chunks, nchunks, xq, xsc, hq, hsc, dbg);
+    const bool group = ids && a.logits;  // workgroup 0 writes the routing's grouping
+    const int gu_grid = (int)std::max<long long>(1, gu_items + (group ? 1 : 0));
+    const uint32_t* gsm = reinterpret_cast<const uint32_t*>(L.gate.scale_min);
+    const uint32_t* usm = reinterpret_cast<const uint32_t*>(L.up.scale_min);
+    if (ids)
+      hipLaunchKernelGGL((k_gateup<BITS, NPC, DBG, true>), dim3(gu_grid), dim3(kGuThreads), 0,
+                         a.stream, L.gate.codes, gsm, L.up.codes, usm, d, f, chunks, nchunks, xq,
+                         xsc, hq, hsc, a.r->topk_ids, k, n * k, E,
+                         group ? a.r->expert_offsets : nullptr, a.r->pair_index, dbg);
+    else
+      hipLaunchKernelGGL((k_gateup<BITS, NPC, DBG, false>), dim3(gu_grid), dim3(kGuThreads), 0,
+                         a.stream, L.gate.codes, gsm, L.up.codes, usm, d, f, chunks, nchunks, xq,
+                         xsc, hq, hsc, a.r->topk_ids, k, n * k, E, nullptr, nullptr, dbg);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
