@@ -192,24 +192,25 @@ TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_t4_k_gateup_traffic.md"
 
 
 def measured_traffic(profile_path):
-    """Calibrated HBM bytes per launch from a committed counter summary, or None when the
-    kernel source has changed since the counters were taken."""
+    """Calibrated HBM bytes per launch from a committed counter summary, or None when any
+    source the kernel is built from has changed since the counters were taken."""
     import hashlib
     import re
 
     if not os.path.exists(profile_path):
         return None
     text = open(profile_path).read()
-    src = re.search(r"^kernel_source: (\S+)$", text, re.M)
-    sha = re.search(r"^kernel_source_sha256: ([0-9a-f]{64})$", text, re.M)
+    srcs = re.findall(r"^kernel_source: (\S+)$", text, re.M)
+    shas = re.findall(r"^kernel_source_sha256: ([0-9a-f]{64})$", text, re.M)
     val = re.search(r"^traffic_bytes_per_launch: (\d+)$", text, re.M)
-    if not (src and sha and val):
+    if not (srcs and len(srcs) == len(shas) and val):
         return None
-    path = os.path.join(ROOT, src.group(1))
-    if not os.path.exists(path):
-        return None
-    if hashlib.sha256(open(path, "rb").read()).hexdigest() != sha.group(1):
-        return None
+    for src, sha in zip(srcs, shas):
+        path = os.path.join(ROOT, src)
+        if not os.path.exists(path):
+            return None
+        if hashlib.sha256(open(path, "rb").read()).hexdigest() != sha:
+            return None
     return int(val.group(1))
 
 
