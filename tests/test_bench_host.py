@@ -1,0 +1,45 @@
+"""Host-side checks of the benchmark's step objects (no GPU)."""
+from __future__ import annotations
+
+import gc
+import weakref
+
+import pytest
+import torch
+
+import bench
+from quantized_routed_expert_router_amd import qmoe
+
+
+def _cpu_layer():
+    mk = lambda r, c: qmoe.QMatrix(torch.zeros(64, dtype=torch.int32),  # noqa: E731
+                                   torch.zeros(32, dtype=torch.int16), r, c, 4)
+    return qmoe.Layer(64, 32, 4, 2, mk(32, 64), mk(32, 64), mk(64, 32))
+
+
+@pytest.mark.parametrize("cls", [bench.Step, bench.PrefillStep])
+def test_step_keeps_its_weights_alive(cls):
+    # the step keeps raw device pointers (C structs); the tensors behind them must live as
+    # long as the step, or freed memory is handed to the next layer instance (instances
+    # then alias) and releasing the allocator's cache unmaps it under the step
+    layer = _cpu_layer()
+    probe = weakref.ref(layer.down.codes)
+    lg = torch.zeros((2, 4))
+    routing = qmoe.Routing.empty(2, 4, 2, device="cpu")
+
+    class Q:  # the step only needs route_workspace from the binding here
+        @staticmethod
+        def route_workspace(n, E, k):
+            return None
+
+    step = cls(Q, layer, lg, torch.zeros((2, 64)), torch.zeros((2, 64)), routing,
+               torch.zeros(16, dtype=torch.uint8))
+    del layer
+    gc.collect()
+    assert probe() is not None, "the step dropped its layer's weight tensors"
+    assert step.layer_s.down.codes == probe().data_ptr()
+    # the step's launch methods are still methods (not shadowed by stored attributes)
+    for name in ("full", "stages"):
+        assert callable(getattr(step, name))
+    if cls is bench.Step:
+        assert callable(step.layer) and callable(step.gate_up)
