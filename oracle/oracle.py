@@ -58,7 +58,8 @@ def lib():
         L.orc_weight_bf16.argtypes = [ctypes.POINTER(_Matrix), i32, i32, i32]
         L.orc_weight_bf16.restype = ctypes.c_uint16
         L.orc_ffn_decode.argtypes = [ctypes.POINTER(_Matrix)] * 3 + [i32] * 4 + [
-            vp, i32, vp, vp, vp, vp, i32, vp, ctypes.POINTER(_Trace), i32]
+            vp, i32, vp, vp, vp, vp, i32, vp, ctypes.POINTER(_Trace), i32] + [
+            ctypes.POINTER(_Matrix)] * 3
         L.orc_ffn_prefill.argtypes = [ctypes.POINTER(_Matrix)] * 3 + [i32] * 4 + [
             vp, i32, vp, vp, vp, vp, i32, vp, vp, vp, vp, vp, i32]
         L.orc_threads.argtypes = [i32]
@@ -136,8 +137,10 @@ def weight_bf16(M: Matrix, e: int, r: int, c: int) -> int:
 
 
 def ffn_decode(gate: Matrix, up: Matrix, down: Matrix, E: int, x, ids, w, residual,
-               tokens=None, trace: bool = False, nthreads: int = 0):
-    """Decode-layer output for the selected tokens (all when None): returns (out, trace)."""
+               tokens=None, trace: bool = False, nthreads: int = 0, shared=None):
+    """Decode-layer output for the selected tokens (all when None): returns (out, trace).
+    `shared` = (gate, up, down) of one always-active expert added with weight 1 (its trace
+    pairs follow the routed ones: pair n_sel*k + s for token position s)."""
     x = _c(x, np.float32)
     residual = _c(residual, np.float32)
     ids = _c(ids, np.int32)
@@ -151,7 +154,7 @@ def ffn_decode(gate: Matrix, up: Matrix, down: Matrix, E: int, x, ids, w, residu
     tr = {}
     ts = None
     if trace:
-        P = n_sel * k
+        P = n_sel * k + (n_sel if shared is not None else 0)
         tr = dict(xq=np.zeros((n_sel, d), np.int8), xs=np.zeros((n_sel, d // 32), np.float32),
                   gate_dots=np.zeros((P, f, d // 32), np.int32),
                   up_dots=np.zeros((P, f, d // 32), np.int32),
@@ -161,9 +164,10 @@ def ffn_decode(gate: Matrix, up: Matrix, down: Matrix, E: int, x, ids, w, residu
                   down_dots=np.zeros((P, d, f // 32), np.int32), y=np.zeros((P, d), np.float64))
         ts = _Trace(**{k_: v.ctypes.data for k_, v in tr.items()})
     sg, su, sd = gate._struct(), up._struct(), down._struct()
+    sh = [None, None, None] if shared is None else [ctypes.byref(m._struct()) for m in shared]
     rc = lib().orc_ffn_decode(ctypes.byref(sg), ctypes.byref(su), ctypes.byref(sd), d, f, E, k,
                               _p(x), n, _p(ids), _p(w), _p(residual), _p(tok), n_sel, _p(out),
-                              ctypes.byref(ts) if ts is not None else None, nthreads)
+                              ctypes.byref(ts) if ts is not None else None, nthreads, *sh)
     if rc != 0:
         raise ValueError("orc_ffn_decode: bad arguments")
     return out, tr

@@ -26,6 +26,11 @@
  *   combine  - routing-weighted sum of the k expert outputs added into the residual
  *              (same page, "Doorbell handshake": combine expert outputs, write back
  *              the residual).
+ *   shared   - optionally one always-active shared expert of the routed experts' shape
+ *              and quantization, run for every token and added with weight 1 after the
+ *              routed slots (reading of the model table's "10+1" active experts per
+ *              token and the GPU-resident shared expert of the Strata pages; the pages
+ *              give no gate for it, so its weight is 1).
  *   prefill  - the same layer for a long chunk with bf16 weights and activations
  *              (chunks of up to 8192 tokens, "Architecture overview").
  *
@@ -56,19 +61,20 @@ typedef struct {
 } orc_matrix;
 
 /* Optional intermediate outputs of orc_ffn_decode (each pointer may be NULL).
- * Pair index p = t*k + j for selected-token position t and slot j. */
+ * Pair index p = t*k + j for selected-token position t and slot j; with a shared expert,
+ * its pair of token position t follows all routed pairs: p = n*k + t (Q pairs in all). */
 typedef struct {
   int8_t* xq;         /* [n][d]          */
   float* xs;          /* [n][d/32]       */
-  int32_t* gate_dots; /* [n*k][f][d/32]  */
-  int32_t* up_dots;   /* [n*k][f][d/32]  */
-  double* g;          /* [n*k][f]        */
-  double* u;          /* [n*k][f]        */
-  float* h;           /* [n*k][f]        */
-  int8_t* hq;         /* [n*k][f]        */
-  float* hs;          /* [n*k][f/32]     */
-  int32_t* down_dots; /* [n*k][d][f/32]  */
-  double* y;          /* [n*k][d]        */
+  int32_t* gate_dots; /* [Q][f][d/32]    */
+  int32_t* up_dots;   /* [Q][f][d/32]    */
+  double* g;          /* [Q][f]          */
+  double* u;          /* [Q][f]          */
+  float* h;           /* [Q][f]          */
+  int8_t* hq;         /* [Q][f]          */
+  float* hs;          /* [Q][f/32]       */
+  int32_t* down_dots; /* [Q][d][f/32]    */
+  double* y;          /* [Q][d]          */
 } orc_trace;
 
 /* binary16 -> binary64 from the IEEE 754 definition */
@@ -264,15 +270,55 @@ static int matrices_ok(const orc_matrix* gate, const orc_matrix* up, const orc_m
 
 /* ---- decode layer: quant -> gate/up -> SwiGLU -> quant -> down -> combine ---------- */
 
+/* One expert e of (gate, up, down) on one quantized token (aq, as): gate and up through
+ * int32 block dots, SwiGLU, int8 quantization of h, down; y [d] in binary64. Trace slot p
+ * of tr receives the intermediates when tr is given. */
+static void orc_expert_ffn(const orc_matrix* gate, const orc_matrix* up, const orc_matrix* down,
+                           int e, const int8_t* aq, const float* as, int d, int f, double* y,
+                           const orc_trace* tr, size_t p) {
+  const int nbd = d / 32, nbf = f / 32;
+  double* g = (double*)malloc(sizeof(double) * (size_t)f);
+  double* u = (double*)malloc(sizeof(double) * (size_t)f);
+  float* h = (float*)malloc(sizeof(float) * (size_t)f);
+  int8_t* hq = (int8_t*)malloc((size_t)f);
+  float* hs = (float*)malloc(sizeof(float) * (size_t)nbf);
+  orc_qmatvec(gate, e, aq, as, g, tr && tr->gate_dots ? tr->gate_dots + p * f * nbd : NULL);
+  orc_qmatvec(up, e, aq, as, u, tr && tr->up_dots ? tr->up_dots + p * f * nbd : NULL);
+  for (int r = 0; r < f; ++r) {
+    const double silu = g[r] / (1.0 + exp(-g[r])); /* SwiGLU: silu(gate) * up */
+    h[r] = (float)(silu * u[r]);
+  }
+  orc_quant_act(h, f, hq, hs);
+  orc_qmatvec(down, e, hq, hs, y, tr && tr->down_dots ? tr->down_dots + p * d * nbf : NULL);
+  if (tr) {
+    if (tr->g) memcpy(tr->g + p * f, g, sizeof(double) * (size_t)f);
+    if (tr->u) memcpy(tr->u + p * f, u, sizeof(double) * (size_t)f);
+    if (tr->h) memcpy(tr->h + p * f, h, sizeof(float) * (size_t)f);
+    if (tr->hq) memcpy(tr->hq + p * f, hq, (size_t)f);
+    if (tr->hs) memcpy(tr->hs + p * nbf, hs, sizeof(float) * (size_t)nbf);
+    if (tr->y) memcpy(tr->y + p * d, y, sizeof(double) * (size_t)d);
+  }
+  free(g);
+  free(u);
+  free(h);
+  free(hq);
+  free(hs);
+}
+
 /* Tokens `tokens[0..n_sel)` (all n tokens in order when tokens == NULL) are evaluated:
- *   out[s][:] = residual[t][:] + sum_j w[t][j] * y_{t,j}[:]   (slot order j = 0..k-1)
- * with t = tokens[s]; the expert FFN of pair (t, j) uses expert ids[t][j].
+ *   out[s][:] = residual[t][:] + sum_j w[t][j] * y_{t,j}[:]  (+ y_shared_t[:])
+ * in binary64, slot order j = 0..k-1 and the shared expert last, with t = tokens[s]; the
+ * expert FFN of pair (t, j) uses expert ids[t][j], the shared one (when sgate, sup and
+ * sdown are given, each holding one expert) expert 0 of those matrices.
  * x, residual: [n][d] fp32; out: [n_sel][d] fp32. Returns 0, or 1 on bad arguments. */
 int orc_ffn_decode(const orc_matrix* gate, const orc_matrix* up, const orc_matrix* down, int d,
                    int f, int E, int k, const float* x, int n, const int32_t* ids, const float* w,
                    const float* residual, const int32_t* tokens, int n_sel, float* out,
-                   const orc_trace* tr, int nthreads) {
+                   const orc_trace* tr, int nthreads, const orc_matrix* sgate,
+                   const orc_matrix* sup, const orc_matrix* sdown) {
   if (!matrices_ok(gate, up, down, d, f) || k < 1 || k > E || n < 0) return 1;
+  const int shared = sgate != NULL;
+  if (shared && (!sup || !sdown || !matrices_ok(sgate, sup, sdown, d, f))) return 1;
   if (!tokens) n_sel = n;
   for (int s = 0; s < n_sel; ++s) {
     const int t = tokens ? tokens[s] : s;
@@ -280,11 +326,11 @@ int orc_ffn_decode(const orc_matrix* gate, const orc_matrix* up, const orc_matri
     for (int j = 0; j < k; ++j)
       if (ids[(size_t)t * k + j] < 0 || ids[(size_t)t * k + j] >= E) return 1;
   }
-  const int nbd = d / 32, nbf = f / 32;
-  const int P = n_sel * k;
-  double* y = (double*)malloc(sizeof(double) * (size_t)P * d);
-  int8_t* xq = (int8_t*)malloc((size_t)n_sel * d);
-  float* xs = (float*)malloc(sizeof(float) * (size_t)n_sel * nbd);
+  const int nbd = d / 32;
+  const int P = n_sel * k, Q = P + (shared ? n_sel : 0);
+  double* y = (double*)malloc(sizeof(double) * ((size_t)Q + 1) * d);
+  int8_t* xq = (int8_t*)malloc((size_t)n_sel * d + 1);
+  float* xs = (float*)malloc(sizeof(float) * ((size_t)n_sel * nbd + 1));
   if (!y || !xq || !xs) {
     free(y);
     free(xq);
@@ -299,39 +345,17 @@ int orc_ffn_decode(const orc_matrix* gate, const orc_matrix* up, const orc_matri
   if (nthreads > 0) omp_set_num_threads(nthreads);
 #pragma omp parallel for schedule(dynamic, 1)
 #endif
-  for (int p = 0; p < P; ++p) {
-    const int s = p / k, j = p % k;
-    const int t = tokens ? tokens[s] : s;
-    const int e = ids[(size_t)t * k + j];
-    double* g = (double*)malloc(sizeof(double) * (size_t)f);
-    double* u = (double*)malloc(sizeof(double) * (size_t)f);
-    float* h = (float*)malloc(sizeof(float) * (size_t)f);
-    int8_t* hq = (int8_t*)malloc((size_t)f);
-    float* hs = (float*)malloc(sizeof(float) * (size_t)nbf);
-    orc_qmatvec(gate, e, xq + (size_t)s * d, xs + (size_t)s * nbd, g,
-                tr && tr->gate_dots ? tr->gate_dots + (size_t)p * f * nbd : NULL);
-    orc_qmatvec(up, e, xq + (size_t)s * d, xs + (size_t)s * nbd, u,
-                tr && tr->up_dots ? tr->up_dots + (size_t)p * f * nbd : NULL);
-    for (int r = 0; r < f; ++r) {
-      const double silu = g[r] / (1.0 + exp(-g[r])); /* SwiGLU: silu(gate) * up */
-      h[r] = (float)(silu * u[r]);
+  for (int p = 0; p < Q; ++p) {
+    if (p < P) {
+      const int s = p / k, j = p % k;
+      const int t = tokens ? tokens[s] : s;
+      orc_expert_ffn(gate, up, down, ids[(size_t)t * k + j], xq + (size_t)s * d,
+                     xs + (size_t)s * nbd, d, f, y + (size_t)p * d, tr, (size_t)p);
+    } else {
+      const int s = p - P;
+      orc_expert_ffn(sgate, sup, sdown, 0, xq + (size_t)s * d, xs + (size_t)s * nbd, d, f,
+                     y + (size_t)p * d, tr, (size_t)p);
     }
-    orc_quant_act(h, f, hq, hs);
-    orc_qmatvec(down, e, hq, hs, y + (size_t)p * d,
-                tr && tr->down_dots ? tr->down_dots + (size_t)p * d * nbf : NULL);
-    if (tr) {
-      if (tr->g) memcpy(tr->g + (size_t)p * f, g, sizeof(double) * (size_t)f);
-      if (tr->u) memcpy(tr->u + (size_t)p * f, u, sizeof(double) * (size_t)f);
-      if (tr->h) memcpy(tr->h + (size_t)p * f, h, sizeof(float) * (size_t)f);
-      if (tr->hq) memcpy(tr->hq + (size_t)p * f, hq, (size_t)f);
-      if (tr->hs) memcpy(tr->hs + (size_t)p * nbf, hs, sizeof(float) * (size_t)nbf);
-      if (tr->y) memcpy(tr->y + (size_t)p * d, y + (size_t)p * d, sizeof(double) * (size_t)d);
-    }
-    free(g);
-    free(u);
-    free(h);
-    free(hq);
-    free(hs);
   }
   for (int s = 0; s < n_sel; ++s) {
     const int t = tokens ? tokens[s] : s;
@@ -339,6 +363,7 @@ int orc_ffn_decode(const orc_matrix* gate, const orc_matrix* up, const orc_matri
       double acc = 0.0;
       for (int j = 0; j < k; ++j)
         acc += (double)w[(size_t)t * k + j] * y[((size_t)s * k + j) * d + c];
+      if (shared) acc += y[((size_t)P + s) * d + c];
       out[(size_t)s * d + c] = (float)((double)residual[(size_t)t * d + c] + acc);
     }
   }

@@ -201,6 +201,59 @@ def test_decode_layer_vs_dense_bruteforce(bits):
     np.testing.assert_array_max_ulp(out, ref_out.astype(np.float32), maxulp=1)
 
 
+@pytest.mark.parametrize("bits", [4, 2])
+def test_shared_expert_vs_dense_bruteforce(bits):
+    # one always-active shared expert: every token runs it on its own quantized x, and its
+    # output is added with weight 1 after the k routed slots
+    E, d, f, k, n = 6, 128, 96, 3, 5
+    g, u, dn = _layer(E, d, f, bits)
+    sg, su, sd = _layer(1, d, f, bits, seed=9, layer=4)
+    rng = np.random.default_rng(7)
+    lg = rng.standard_normal((n, E)).astype(np.float32)
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    res = rng.standard_normal((n, d)).astype(np.float32)
+    ids, w = O.route(lg, k)
+    out, tr = O.ffn_decode(_M(g), _M(u), _M(dn), E, x, ids, w, res, trace=True,
+                           shared=(_M(sg), _M(su), _M(sd)))
+    Wg, Wu, Wd = (dequant(m.codes, m.scale_min, bits)[0] for m in (sg, su, sd))
+    xa = dequant_act(tr["xq"], tr["xs"])
+    P = n * k
+    for t in range(n):
+        p = P + t
+        np.testing.assert_allclose(tr["g"][p], Wg @ xa[t], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(tr["u"][p], Wu @ xa[t], rtol=1e-12, atol=1e-12)
+        h_ref = (tr["g"][p] * expit(tr["g"][p]) * tr["u"][p]).astype(np.float32)
+        np.testing.assert_array_max_ulp(tr["h"][p], h_ref, maxulp=1)
+        ha = dequant_act(tr["hq"][p], tr["hs"][p])
+        np.testing.assert_allclose(tr["y"][p], Wd @ ha, rtol=1e-12, atol=1e-12)
+    y = tr["y"][:P].reshape(n, k, d)
+    ref_out = (res.astype(np.float64) + np.einsum("tj,tjc->tc", w.astype(np.float64), y)
+               + tr["y"][P:])
+    np.testing.assert_array_max_ulp(out, ref_out.astype(np.float32), maxulp=1)
+    # the routed pairs are those of the layer without the shared expert
+    out0, tr0 = O.ffn_decode(_M(g), _M(u), _M(dn), E, x, ids, w, res, trace=True)
+    assert np.array_equal(tr0["y"], tr["y"][:P])
+    # composition: the routed layer, then a top-1 call with weight 1 to the shared expert
+    # on the same x, differs only by the extra fp32 rounding of the intermediate residual
+    out2, _ = O.ffn_decode(_M(sg), _M(su), _M(sd), 1, x, np.zeros((n, 1), np.int32),
+                           np.ones((n, 1), np.float32), out0)
+    np.testing.assert_array_max_ulp(out, out2, maxulp=2)
+
+
+def test_shared_expert_zero_weights_add_nothing():
+    E, d, f, k, n = 4, 64, 64, 2, 3
+    g, u, dn = _layer(E, d, f, 4)
+    sg, su, sd = _layer(1, d, f, 4, seed=2)
+    for m in (sg, su, sd):
+        m.scale_min[:] = 0
+    rng = np.random.default_rng(2)
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    ids, w = O.route(rng.standard_normal((n, E)).astype(np.float32), k)
+    out, _ = O.ffn_decode(_M(g), _M(u), _M(dn), E, x, ids, w, x, shared=(_M(sg), _M(su), _M(sd)))
+    out0, _ = O.ffn_decode(_M(g), _M(u), _M(dn), E, x, ids, w, x)
+    assert np.array_equal(out, out0)
+
+
 def test_int8_error_bound_against_unquantized_x():
     # |W.x - W.(xs*xq)| <= sum_c |w_c| * xs_b(c) / 2 (round-to-nearest bound per element)
     E, d, f, k, n = 4, 256, 64, 2, 3
