@@ -55,6 +55,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="--config 4: skip the HIP-graph replay of the 48-layer step")
+    ap.add_argument("--shared", action="store_true",
+                    help="--config 2 or 4: layers with one always-active shared expert")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device-to-device copy of MIB MiB (the reference "
                          "dispatch that scales hardware byte counters)")
@@ -221,13 +223,17 @@ def bench_decode(args, torch, q, synth, workloads):
     import numpy as np
 
     w = synth.config(args.config, args.T)
+    shared = args.shared and args.config == 2
+    if shared:
+        w.name += "_shared1"
     L = args.instances or (10 if args.config == 2 else 3)
     log(f"workload {w.name}: generating {L} layer instances on the GPU")
     t0 = time.perf_counter()
     steps, inputs = [], []
     for i in range(L):
-        ws = q.workspace(_shape_layer(q, w), w.n)  # one per instance: stages can be replayed
-        layer = workloads.device_layer(w, i)
+        # one workspace per instance: stages can be replayed
+        ws = q.workspace(_shape_layer(q, w, shared), w.n)
+        layer = workloads.device_layer(w, i, shared=shared)
         lg, x = synth.layer_inputs(w, i)
         inputs.append((lg, x))
         lg_d = torch.from_numpy(lg).cuda()
@@ -244,7 +250,8 @@ def bench_decode(args, torch, q, synth, workloads):
         st.full(sh)  # routing of each instance is fixed: bytes per step
     torch.cuda.synchronize()
     ebytes = synth.expert_bytes(w.d, w.f, w.bits)
-    touched = [touched_experts(st.routing) for st in steps]
+    # the shared expert is read once per step like a touched routed expert
+    touched = [touched_experts(st.routing) + (1 if shared else 0) for st in steps]
     step_bytes = [t * ebytes for t in touched]
     gu_bytes = [t * ebytes * 2 // 3 for t in touched]
 
@@ -279,7 +286,7 @@ def bench_decode(args, torch, q, synth, workloads):
         "data": "synthetic",
         "config": {"workload": w.name, "d_model": w.d, "d_ff": w.f, "experts": w.E,
                    "top_k": w.k, "tokens_per_step": w.n, "weight_bits": w.bits,
-                   "layer_instances": L,
+                   "layer_instances": L, "shared_expert": shared,
                    "step": "moe_layer_decode (routing + expert FFN: x quant, gate/up, SwiGLU, "
                            "h quant, down, combine)"},
         "tokens_per_s": round(tok_s, 1),
@@ -290,37 +297,42 @@ def bench_decode(args, torch, q, synth, workloads):
         "roofline": {"bound": "hbm", "kernel": "k_gateup (gate/up + SwiGLU + h quant)",
                      "achieved": round(gu_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_ach / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic(TRAFFIC_PROFILE) if args.config == 2 else None,
+                     "traffic": (measured_traffic(TRAFFIC_PROFILE)
+                                 if args.config == 2 and not shared else None),
                      "bytes_per_launch": round(float(np.mean([gu_bytes[i] for i in order])), 1)},
     }
-    if args.config == 2 and not args.no_cpu_baseline:
+    if args.config == 2 and not shared and not args.no_cpu_baseline:
         log("CPU oracle baseline ...")
         rec["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)
     return rec
 
 
-def _shape_layer(q, w):
+def _shape_layer(q, w, shared=False):
     """A layer description with the right sizes for workspace queries (no weights)."""
     import torch
 
     dummy = torch.empty(16, dtype=torch.int32, device="cuda")
     dummy16 = torch.empty(16, dtype=torch.int16, device="cuda")
     mk = lambda r, c: q.QMatrix(dummy, dummy16, r, c, w.bits)  # noqa: E731
-    return q.Layer(w.d, w.f, w.E, w.k, mk(w.f, w.d), mk(w.f, w.d), mk(w.d, w.f))
+    sh = (mk(w.f, w.d), mk(w.f, w.d), mk(w.d, w.f)) if shared else None
+    return q.Layer(w.d, w.f, w.E, w.k, mk(w.f, w.d), mk(w.f, w.d), mk(w.d, w.f), sh)
 
 
 def bench_chain(args, torch, q, synth, workloads):
     import numpy as np
 
     w = synth.config(4)
+    shared = args.shared
+    if shared:
+        w.name += "_shared1"
     log(f"workload {w.name}: generating {w.layers} layers on the GPU")
     t0 = time.perf_counter()
-    ws = q.workspace(_shape_layer(q, w), w.n)
+    ws = q.workspace(_shape_layer(q, w, shared), w.n)
     x0 = torch.from_numpy(synth.activations(w.seed, 0, w.n, w.d)).cuda()
     res = x0.clone()
     steps = []
     for l_ in range(w.layers):
-        layer = workloads.device_layer(w, l_)
+        layer = workloads.device_layer(w, l_, shared=shared)
         lg = torch.from_numpy(synth.logits(w.seed, l_, w.n, w.E, w.logits)).cuda()
         routing = q.Routing.empty(w.n, w.E, w.k)
         steps.append(Step(q, layer, lg, res, res, routing, ws))  # x is the residual stream
@@ -331,7 +343,7 @@ def bench_chain(args, torch, q, synth, workloads):
         st.full(sh)
     torch.cuda.synchronize()
     ebytes = synth.expert_bytes(w.d, w.f, w.bits)
-    touched = [touched_experts(st.routing) for st in steps]
+    touched = [touched_experts(st.routing) + (1 if shared else 0) for st in steps]
     chain_bytes = sum(touched) * ebytes
     order = list(range(w.layers)) * max(1, args.steps // w.layers)
     _, _, host_s, _ = timed_region(torch, steps, list(range(w.layers)), False, 0.1)
@@ -347,7 +359,7 @@ def bench_chain(args, torch, q, synth, workloads):
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
         "data": "synthetic",
         "config": {"workload": w.name, "layers": w.layers, "tokens_per_step": w.n,
-                   "step": "48 x moe_layer_decode, residual chained"},
+                   "shared_expert": shared, "step": "48 x moe_layer_decode, residual chained"},
         "tokens_per_s": round(n_chain * w.n / sec, 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "expert_bytes_per_step": chain_bytes,
@@ -498,9 +510,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py runs on exactly one GPU: this build measures the routed-expert layer on "
-              "one MI355X (how the layer would shard over several GPUs is described in "
-              "DESIGN.md); rerun with --gpus 1.", file=sys.stderr)
+        print("bench.py measures the routed-expert layer on exactly one MI355X; rerun with "
+              "--gpus 1.", file=sys.stderr)
         sys.exit(2)
     import torch
 

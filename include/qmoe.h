@@ -88,6 +88,17 @@ typedef struct {
   int32_t n_experts; /* E: 1..MOE_MAX_EXPERTS                                      */
   int32_t top_k;     /* k: 1..min(E, MOE_MAX_TOP_K)                                */
   moe_qmatrix gate, up, down;
+  /* Optional shared expert: one always-active expert in the routed experts' shape and
+   * format (rows, cols and bits as gate, up and down; one expert each), run for every
+   * token and added to the residual with weight 1 after the routed slots (the model
+   * table of the Strata pages counts "10+1" active experts per token, and the engine
+   * explainer's memory table keeps a shared expert on the GPU; the pages give it no
+   * gate). shared_gate.codes == NULL: none (the other two are then ignored). Supported by
+   * the decode entry points for windows of n <= 8 tokens with n*k <= 64 pairs, k + 1 <=
+   * 16, d_ff <= 1024, ceil((k+1)/2) * ceil(d_ff/256) <= 18 (k <= 10 at d_ff = 768) and
+   * the down and combine stages issued together; otherwise, and by the prefill entry
+   * points, MOE_ERR_UNSUPPORTED. */
+  moe_qmatrix shared_gate, shared_up, shared_down;
 } moe_layer;
 
 /* Routing record of n tokens (all device memory), written by moe_route and read by the
@@ -108,7 +119,8 @@ typedef struct {
 
 /* Optional intermediate outputs of moe_expert_ffn_decode, for checking (each may be
  * NULL; passing a non-NULL moe_debug selects a slower instance of the same kernels).
- * p = t*k + j is the pair id. Layouts:
+ * p = t*k + j is the pair id; with a shared expert, token t's shared pair is p = n*k + t
+ * and the [n*k] extents below become [n*k + n]. Layouts:
  *   xq int8 [n][d], xs fp32 [n][d/32]            activation codes and block scales
  *   gate_dots, up_dots int32 [n*k][f][d/32]       exact per-block integer dots
  *   g, u fp32 [n*k][f]                            gate/up projections (rounded to fp32)
@@ -153,7 +165,8 @@ size_t moe_ffn_workspace_bytes(const moe_layer* L, int n_tokens, int prefill);
 
 /* Decode-window expert FFN. x: device fp32 [n][d], the layer's MoE input; residual:
  * device fp32 [n][d], updated in place: residual[t] += sum_j w[t][j] * y[t*k+j] (slot
- * order). x may be the residual buffer itself (all of x is read before residual is
+ * order; then the shared expert's output with weight 1, when the layer has one). x may
+ * be the residual buffer itself (all of x is read before residual is
  * written); any other overlap is rejected. r: routing from moe_route for the same n,
  * E and k. ws: device workspace of at least moe_ffn_workspace_bytes(L, n, 0) bytes,
  * 256-byte aligned; its contents need no initialisation. dbg: NULL, or debug outputs.

@@ -54,7 +54,23 @@ moe_status check_layer(const moe_layer* L) {
   moe_status s = check_matrix(L->gate, f, d, bits);
   if (s == MOE_OK) s = check_matrix(L->up, f, d, bits);
   if (s == MOE_OK) s = check_matrix(L->down, d, f, bits);
+  if (s == MOE_OK && has_shared(*L)) {
+    s = check_matrix(L->shared_gate, f, d, bits);
+    if (s == MOE_OK) s = check_matrix(L->shared_up, f, d, bits);
+    if (s == MOE_OK) s = check_matrix(L->shared_down, d, f, bits);
+  }
   return s;
+}
+
+// The decode path runs a shared expert on the small-window kernels only: chunks taken
+// from the expert ids (n <= 8 tokens, n*k <= 64 pairs) and the token-major down with the
+// combine, with one more slot per token.
+bool shared_decode_supported(const moe_layer* L, int n, unsigned stages) {
+  const int k = L->top_k, nbf = L->d_ff / 32;
+  if (n > 8 || (long long)n * k > 64 || k + 1 > 16 || nbf > 32) return false;
+  if (((k + 2) / 2) * ((nbf + 7) / 8) > 18) return false;
+  const bool down = stages & MOE_DECODE_DOWN, combine = stages & MOE_DECODE_COMBINE;
+  return down == combine;
 }
 
 moe_status check_routing(const moe_routing* r) {
@@ -75,11 +91,14 @@ moe_status decode_entry(const moe_layer* L, const float* logits, const float* x,
   if (!x || !residual || !ws) return MOE_ERR_INVALID_ARGUMENT;
   if (!aligned(x, 16) || !aligned(residual, 4) || !aligned(ws, 256))
     return MOE_ERR_INVALID_ARGUMENT;
+  if (has_shared(*L) && !shared_decode_supported(L, n_tokens, stages))
+    return MOE_ERR_UNSUPPORTED;
   if (logits && !aligned(logits, 4)) return MOE_ERR_INVALID_ARGUMENT;
   const size_t act_bytes = (size_t)n_tokens * L->d_model * sizeof(float);
   if (x != residual && overlaps(x, act_bytes, residual, act_bytes))
     return MOE_ERR_INVALID_ARGUMENT;
-  const size_t need = decode_ws_layout(n_tokens, L->top_k, L->d_model, L->d_ff).total;
+  const size_t need =
+      decode_ws_layout(n_tokens, L->top_k, L->d_model, L->d_ff, has_shared(*L)).total;
   if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (overlaps(ws, need, residual, act_bytes) || overlaps(ws, need, x, act_bytes))
     return MOE_ERR_INVALID_ARGUMENT;
@@ -151,7 +170,7 @@ size_t moe_ffn_workspace_bytes(const moe_layer* L, int n_tokens, int prefill) {
     if (E < 1 || E > MOE_MAX_EXPERTS) return 0;
     return prefill_ws_layout(n_tokens, k, d, f, E).total;
   }
-  return decode_ws_layout(n_tokens, k, d, f).total;
+  return decode_ws_layout(n_tokens, k, d, f, has_shared(*L)).total;
 }
 
 moe_status moe_expert_ffn_decode(const moe_layer* L, const float* x, int n_tokens,
@@ -205,6 +224,7 @@ moe_status moe_expert_ffn_prefill_stages(const moe_layer* L, const uint16_t* x_b
   if (stages == 0 || (stages & ~MOE_PREFILL_ALL)) return MOE_ERR_INVALID_ARGUMENT;
   moe_status s = check_layer(L);
   if (s != MOE_OK) return s;
+  if (has_shared(*L)) return MOE_ERR_UNSUPPORTED;
   if (n_tokens < 0 || n_tokens > MOE_MAX_PREFILL_TOKENS) return MOE_ERR_INVALID_ARGUMENT;
   if (n_tokens == 0) return MOE_OK;
   if (check_routing(r) != MOE_OK) return MOE_ERR_INVALID_ARGUMENT;

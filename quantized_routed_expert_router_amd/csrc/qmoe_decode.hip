@@ -35,7 +35,6 @@ namespace qmoe {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kWaves = kThreads / kWave;
 
 // ---------------------------------------------------------------- int8 block quantizer
 
@@ -429,7 +428,9 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     const int* __restrict__ chunks, const int* __restrict__ nchunks, const int8_t* __restrict__ xq,
     const double2* __restrict__ xsc, int8_t* __restrict__ hq, double2* __restrict__ hsc,
     const int32_t* __restrict__ topk_ids, int k, int P, int E, int32_t* __restrict__ offsets,
-    int32_t* __restrict__ pair_index, DecodeDebug dbg) {
+    int32_t* __restrict__ pair_index, const uint32_t* __restrict__ sgcodes,
+    const uint32_t* __restrict__ sgsm, const uint32_t* __restrict__ sucodes,
+    const uint32_t* __restrict__ susm, int n, DecodeDebug dbg) {
   __shared__ double red[kGuWaves][NPC][kGuRows];
   __shared__ int4 s_act_raw[ActLds<NPC, kGuGroup, kGuThreads>::kPadded];
   __shared__ uint32_t s_bits[kExpertWords];
@@ -442,8 +443,6 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
   const int mat = wave / kGuKWaves;  // 0: gate, 1: up
   const int ke = 2 * (wave % kGuKWaves) + lane / kGuRows;  // reduction-axis eighth
   const int rl = lane % kGuRows;
-  const uint32_t* __restrict__ codes = mat ? ucodes : gcodes;
-  const uint32_t* __restrict__ smp = mat ? usm : gsm;
   // One item per workgroup: the grid covers the largest possible item count and the
   // workgroups past the live count exit. (A loop over items would make the compiler's wait
   // counts conservative at its head: the first weight requests would wait for the
@@ -465,10 +464,25 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
       --item;
     }
     // wave 0 derives the chunk and hands it to the others through LDS (a derivation in
-    // every wave costs more: all waves of all workgroups would read the same ids)
+    // every wave costs more: all waves of all workgroups would read the same ids). The
+    // weight pointers are fetched first, during the derivation (a pointer used on one side
+    // of a select would be fetched inside a branch, after the barrier).
+    // t = p / k as a multiply-high by ceil(2^32 / k), exact while p * k < 2^32 (here p < 72)
+    uint32_t kmul = 0xffffffffu / (uint32_t)k + 1u;
+    asm volatile("" : "+s"(gcodes), "+s"(gsm), "+s"(ucodes), "+s"(usm), "+s"(sgcodes),
+                 "+s"(sgsm), "+s"(sucodes), "+s"(susm), "+s"(xq), "+s"(xsc), "+s"(kmul));
     __shared__ IdsChunk<NPC> s_ch;
     if (wave == 0) {
-      const IdsChunk<NPC> c0 = chunk_from_ids<NPC>(topk_ids, P, item / ntiles, lane, s_bits);
+      IdsChunk<NPC> c0 = chunk_from_ids<NPC>(topk_ids, P, item / ntiles, lane, s_bits);
+      if (sgcodes) {  // the shared expert: one chunk after the routed ones, all n tokens
+        if (item / ntiles == c0.nch) {
+          c0.e = -1;
+          c0.np = n;
+#pragma unroll
+          for (int j = 0; j < NPC; ++j) c0.pid[j] = P + min(j, n - 1);
+        }
+        c0.nch += 1;
+      }
       if (lane == 0) s_ch = c0;
     }
     __syncthreads();
@@ -481,10 +495,15 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     e = ch.e;
     np = ch.np;
     nch = ch.nch;
+    // activation row: the token of the pair, taken for every pair and pinned, so that the
+    // select stays a select (a division feeding one side of it would be moved into a
+    // branch of its own ahead of the first weight request)
 #pragma unroll
     for (int j = 0; j < NPC; ++j) {
       pid[j] = ch.pid[j];
-      rows.r[j] = pid[j] / k;
+      int tq = k == 1 ? pid[j] : (int)__umulhi((uint32_t)pid[j], kmul);
+      asm volatile("" : "+s"(tq));
+      rows.r[j] = pid[j] < P ? tq : pid[j] - P;
     }
   } else {
     // The record, the live chunk count and the weight pointers are fetched together: the
@@ -508,10 +527,13 @@ __global__ __launch_bounds__(kGuThreads) __attribute__((amdgpu_waves_per_eu(4)))
     double acc[NPC];
 #pragma unroll
     for (int j = 0; j < NPC; ++j) acc[j] = 0.0;
-    // this expert's codes and scale/min of this matrix
-    const __amdgpu_buffer_rsrc_t rs_c =
-        buffer_rsrc(codes + (size_t)e * nbd * f * BITS, (uint32_t)(nbd * f * BITS * 4));
-    const __amdgpu_buffer_rsrc_t rs_s = buffer_rsrc(smp + (size_t)e * nbd * f, (uint32_t)(nbd * f * 4));
+    // this expert's codes and scale/min of this matrix (e < 0: the shared expert)
+    const uint32_t* __restrict__ codes = mat ? ucodes : gcodes;
+    const uint32_t* __restrict__ smp = mat ? usm : gsm;
+    const uint32_t* cbase = e < 0 ? (mat ? sucodes : sgcodes) : codes + (size_t)e * nbd * f * BITS;
+    const uint32_t* sbase = e < 0 ? (mat ? susm : sgsm) : smp + (size_t)e * nbd * f;
+    const __amdgpu_buffer_rsrc_t rs_c = buffer_rsrc(cbase, (uint32_t)(nbd * f * BITS * 4));
+    const __amdgpu_buffer_rsrc_t rs_s = buffer_rsrc(sbase, (uint32_t)(nbd * f * 4));
     uint32_t w[kGuUnroll][BITS], smw[kGuUnroll];
     for (int g0 = 0; g0 < nbd; g0 += kGuGroup) {
       __syncthreads();  // earlier readers of s_act are done
@@ -766,16 +788,20 @@ constexpr int kDtMaxK = 16;       // top-k handled by this path
 constexpr int kDtMaxBlocks = 32;  // f/32 handled by this path
 constexpr int kDtMaxTokens = 16;  // window tokens handled by this path
 constexpr int kDtSlots = 16;      // weight blocks in flight per lane
+constexpr int kDtSlotsShared = 18;  // the same with one more slot (a shared expert)
 constexpr int kDtStage = kDtMaxK * kDtMaxBlocks * 3;  // 16-byte LDS entries of h
 static_assert(kDtStage % kDtThreads == 0, "staging is whole wave-level loads");
 
-template <int BITS, int U, bool DBG>
+template <int BITS, int U, int I, bool SH, bool DBG>
 __global__ __launch_bounds__(kDtThreads) void k_down_tok(
     const uint32_t* __restrict__ dcodes, const uint32_t* __restrict__ dsm, int d, int f, int k,
     int n, const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w,
     const int8_t* __restrict__ hq, const double2* __restrict__ hsc, float* residual,
-    DecodeDebug dbg) {
-  constexpr int I = kDtSlots / U;  // experts per lane half
+    const uint32_t* __restrict__ sdcodes, const uint32_t* __restrict__ sdsm, DecodeDebug dbg) {
+  // slots j < k: the routed pairs t*k + j; with SH, slot k: the shared expert, pair n*k + t,
+  // weight 1. I slots per lane half (lane half h takes j = h, h+2, ...). Without SH every
+  // shared-slot select folds away.
+  const int ke = SH ? k + 1 : k;
   __shared__ int4 s_act[kDtStage];
   __shared__ double red[kDtWaves][kDtMaxK + 1][kDtRows];  // slot kDtMaxK: unused pairs
   const int nbf = f / 32, nrt = d / kDtRows;
@@ -787,11 +813,18 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int r = lane % kDtRows, h = lane / kDtRows;
   const int row = rt * kDtRows + r;
+  const int P = n * k;
+  auto pair_of = [&](int j) { return SH && j >= k ? (size_t)P + t : (size_t)t * k + j; };
 
-  // experts of the lane's pairs j = h, h+2, ... (slots past k repeat slot k-1, never used)
+  // experts of the lane's pairs (-1: the shared expert; slots past ke repeat slot ke-1,
+  // never used; the id load is unconditional, its value selected)
   int eid[I];
 #pragma unroll
-  for (int i = 0; i < I; ++i) eid[i] = topk_ids[(size_t)t * k + min(h + 2 * i, k - 1)];
+  for (int i = 0; i < I; ++i) {
+    const int j = min(h + 2 * i, ke - 1);
+    const int id = topk_ids[(size_t)t * k + min(j, k - 1)];
+    eid[i] = SH && j >= k ? -1 : id;
+  }
   const bool epi = wave == 0 && lane < kDtRows;
   const float res0 = residual[(size_t)t * d + (epi ? row : rt * kDtRows)];
 
@@ -801,13 +834,13 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
   typedef int v4i __attribute__((ext_vector_type(4)));
   v4i stg[kDtStage / kDtThreads];
   {
-    const int total = k * nbf * 3;
+    const int total = ke * nbf * 3;
 #pragma unroll
     for (int it = 0; it < kDtStage / kDtThreads; ++it) {
       const int idx = min(it * kDtThreads + tid, total - 1);
       const int jb = idx / 3, part = idx % 3;
       const int j = jb / nbf, b = jb % nbf;
-      const size_t p = (size_t)t * k + j;
+      const size_t p = pair_of(j);
       const uintptr_t src = part < 2 ? reinterpret_cast<uintptr_t>(hq + p * f + 32 * b + 16 * part)
                                      : reinterpret_cast<uintptr_t>(hsc + p * nbf + b);
       stg[it] = *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(src);
@@ -815,27 +848,29 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
   }
   __builtin_amdgcn_sched_barrier(0);
 
-  // all weight blocks of this lane (past k or nbf: a valid block, never used)
+  // all weight blocks of this lane (past ke or nbf: a valid block, never used)
   uint32_t w[I][U][BITS], smw[I][U];
 #pragma unroll
   for (int i = 0; i < I; ++i) {
     const int e = eid[i];
+    const uint32_t* cb = SH && e < 0 ? sdcodes : dcodes;
+    const uint32_t* sb = SH && e < 0 ? sdsm : dsm;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int b = min(wave + 8 * u, nbf - 1);
-      const size_t blk = ((size_t)e * nbf + b) * d + row;
+      const size_t blk = ((size_t)(SH && e < 0 ? 0 : e) * nbf + b) * d + row;
       if (BITS == 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(dcodes + blk * 4);
+        const uint4 v = *reinterpret_cast<const uint4*>(cb + blk * 4);
         w[i][u][0] = v.x;
         w[i][u][1] = v.y;
         w[i][u][2 % BITS] = v.z;
         w[i][u][3 % BITS] = v.w;
       } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(dcodes + blk * 2);
+        const uint2 v = *reinterpret_cast<const uint2*>(cb + blk * 2);
         w[i][u][0] = v.x;
         w[i][u][1] = v.y;
       }
-      smw[i][u] = dsm[blk];
+      smw[i][u] = sb[blk];
     }
   }
   __builtin_amdgcn_sched_barrier(0);
@@ -850,7 +885,7 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
     reinterpret_cast<v4i*>(s_act)[it * kDtThreads + tid] = stg[it];
   __syncthreads();
 
-  // Every block is computed and the unused ones (past k or nbf) are dropped by a select:
+  // Every block is computed and the unused ones (past ke or nbf) are dropped by a select:
   // a weight load feeding only a guarded branch would be sunk into it, behind a full wait.
   // Unused blocks read LDS entries inside s_act (j < kDtMaxK, b < kDtMaxBlocks).
   double acc[I];
@@ -861,8 +896,8 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int b = wave + 8 * u;
-      const bool use = j < k && b < nbf;
-      const int4* e3 = s_act + (j * nbf + b) * 3;
+      const bool use = j < ke && b < nbf;
+      const int4* e3 = s_act + (min(j, kDtMaxK - 1) * nbf + b) * 3;
       const int4 a0 = e3[0], a1 = e3[1], scv = e3[2];
       const int a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
       double2 sc;
@@ -873,47 +908,59 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
       // exact terms: see k_gateup
       const double v = __builtin_fma(m, sc.y, __builtin_fma(s * sc.x, (double)dd, acc[i]));
       acc[i] = use ? v : acc[i];
-      if (DBG && use && dbg.down_dots)
-        dbg.down_dots[(((size_t)t * k + j) * d + row) * nbf + b] = dd;
+      if (DBG && use && dbg.down_dots) dbg.down_dots[(pair_of(j) * d + row) * nbf + b] = dd;
     }
-    red[wave][j < k ? j : kDtMaxK][r] = acc[i];  // unconditional: see above
+    red[wave][j < ke ? j : kDtMaxK][r] = acc[i];  // unconditional: see above
   }
   __syncthreads();
   if (epi) {
     double tot = 0.0;
 #pragma unroll
-    for (int j = 0; j < kDtMaxK; ++j) {  // slot order
-      if (j < k) {
+    for (int j = 0; j < kDtMaxK; ++j) {  // slot order, the shared expert last
+      if (j < ke) {
         double y = red[0][j][r];
 #pragma unroll
         for (int w2 = 1; w2 < kDtWaves; ++w2) y += red[w2][j][r];  // wave order
-        if (DBG && dbg.y) dbg.y[((size_t)t * k + j) * d + row] = (float)y;
-        tot += (double)sw[j] * y;
+        if (DBG && dbg.y) dbg.y[pair_of(j) * d + row] = (float)y;
+        tot += (SH && j >= k ? 1.0 : (double)sw[j]) * y;
       }
     }
     residual[(size_t)t * d + row] = (float)((double)res0 + tot);
   }
 }
 
-template <int BITS, bool DBG>
-hipError_t launch_down_tok(const DecodeArgs& a, const int8_t* hq, const double2* hsc,
-                           const DecodeDebug& dbg, int U) {
+// Slots per lane half: kDtSlots / U weight blocks in flight per lane, or kDtSlotsShared / U
+// when the window needs one more slot than that (a shared expert).
+template <int BITS, int U, bool DBG>
+hipError_t launch_down_tok_u(const DecodeArgs& a, const int8_t* hq, const double2* hsc,
+                             const DecodeDebug& dbg) {
   const moe_layer& L = *a.L;
   const int d = L.d_model, f = L.d_ff, k = L.top_k, n = a.n;
   const int per = (d / kDtRows + 7) / 8;
   const dim3 grid(8 * per * n), block(kDtThreads);
   const uint32_t* sm = reinterpret_cast<const uint32_t*>(L.down.scale_min);
-#define QMOE_DT(UU)                                                                            \
-  hipLaunchKernelGGL((k_down_tok<BITS, UU, DBG>), grid, block, 0, a.stream, L.down.codes, sm, d, \
-                     f, k, n, a.r->topk_ids, a.r->topk_w, hq, hsc, a.residual, dbg)
-  switch (U) {
-    case 1: QMOE_DT(1); break;
-    case 2: QMOE_DT(2); break;
-    case 3: QMOE_DT(3); break;
-    default: QMOE_DT(4); break;
-  }
-#undef QMOE_DT
+  const bool shared = has_shared(L);
+  const uint32_t* sdc = shared ? L.shared_down.codes : nullptr;
+  const uint32_t* sds = shared ? reinterpret_cast<const uint32_t*>(L.shared_down.scale_min) : nullptr;
+  constexpr int I1 = kDtSlots / U, I2 = kDtSlotsShared / U;
+  const int ke = k + (shared ? 1 : 0);
+  auto kern = shared                  ? k_down_tok<BITS, U, I2, true, DBG>
+              : (ke + 1) / 2 <= I1 ? k_down_tok<BITS, U, I1, false, DBG>
+                                      : k_down_tok<BITS, U, I2, false, DBG>;
+  hipLaunchKernelGGL(kern, grid, block, 0, a.stream, L.down.codes, sm, d, f, k, n,
+                     a.r->topk_ids, a.r->topk_w, hq, hsc, a.residual, sdc, sds, dbg);
   return hipGetLastError();
+}
+
+template <int BITS, bool DBG>
+hipError_t launch_down_tok(const DecodeArgs& a, const int8_t* hq, const double2* hsc,
+                           const DecodeDebug& dbg, int U) {
+  switch (U) {
+    case 1: return launch_down_tok_u<BITS, 1, DBG>(a, hq, hsc, dbg);
+    case 2: return launch_down_tok_u<BITS, 2, DBG>(a, hq, hsc, dbg);
+    case 3: return launch_down_tok_u<BITS, 3, DBG>(a, hq, hsc, dbg);
+    default: return launch_down_tok_u<BITS, 4, DBG>(a, hq, hsc, dbg);
+  }
 }
 
 // ---------------------------------------------------------------- host side
@@ -922,7 +969,8 @@ template <int BITS, int NPC, bool DBG>
 hipError_t launch_ffn(const DecodeArgs& a) {
   const moe_layer& L = *a.L;
   const int n = a.n, d = L.d_model, f = L.d_ff, k = L.top_k, E = L.n_experts;
-  const DecodeWs W = decode_ws_layout(n, k, d, f);
+  const bool shared = has_shared(L);  // only on the ids path (checked by the entry point)
+  const DecodeWs W = decode_ws_layout(n, k, d, f, shared);
   int* chunks = reinterpret_cast<int*>(a.ws + W.chunks);
   int* nchunks = reinterpret_cast<int*>(a.ws + W.nchunks);
   int8_t* xq = reinterpret_cast<int8_t*>(a.ws + W.xq);
@@ -978,28 +1026,36 @@ hipError_t launch_ffn(const DecodeArgs& a) {
       (P + NPC - 1) / NPC + std::min<long long>(E, P));
   const int cap = a.num_cus * 8;
   if (a.stages & MOE_DECODE_GATE_UP) {
-    const long long gu_items = max_chunks * (f / kGuRows);  // one workgroup per item
+    // one workgroup per item; the shared expert is one more chunk
+    const long long gu_items = (max_chunks + (shared ? 1 : 0)) * (f / kGuRows);
     const bool group = ids && a.logits;  // workgroup 0 writes the routing's grouping
     const int gu_grid = (int)std::max<long long>(1, gu_items + (group ? 1 : 0));
     const uint32_t* gsm = reinterpret_cast<const uint32_t*>(L.gate.scale_min);
     const uint32_t* usm = reinterpret_cast<const uint32_t*>(L.up.scale_min);
+    const uint32_t* sgc = shared ? L.shared_gate.codes : nullptr;
+    const uint32_t* sgs = shared ? reinterpret_cast<const uint32_t*>(L.shared_gate.scale_min) : nullptr;
+    const uint32_t* suc = shared ? L.shared_up.codes : nullptr;
+    const uint32_t* sus = shared ? reinterpret_cast<const uint32_t*>(L.shared_up.scale_min) : nullptr;
     if (ids)
       hipLaunchKernelGGL((k_gateup<BITS, NPC, DBG, true>), dim3(gu_grid), dim3(kGuThreads), 0,
                          a.stream, L.gate.codes, gsm, L.up.codes, usm, d, f, chunks, nchunks, xq,
                          xsc, hq, hsc, a.r->topk_ids, k, n * k, E,
-                         group ? a.r->expert_offsets : nullptr, a.r->pair_index, dbg);
+                         group ? a.r->expert_offsets : nullptr, a.r->pair_index, sgc, sgs, suc,
+                         sus, n, dbg);
     else
       hipLaunchKernelGGL((k_gateup<BITS, NPC, DBG, false>), dim3(gu_grid), dim3(kGuThreads), 0,
                          a.stream, L.gate.codes, gsm, L.up.codes, usm, d, f, chunks, nchunks, xq,
-                         xsc, hq, hsc, a.r->topk_ids, k, n * k, E, nullptr, nullptr, dbg);
+                         xsc, hq, hsc, a.r->topk_ids, k, n * k, E, nullptr, nullptr, nullptr,
+                         nullptr, nullptr, nullptr, n, dbg);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   // down and combine together for a small window: the token-major kernel does both
   const int nbf = f / 32, dt_u = (nbf + 7) / 8;
+  const int ke = k + (shared ? 1 : 0);  // slots per token
   const bool token_major = (a.stages & MOE_DECODE_DOWN) && (a.stages & MOE_DECODE_COMBINE) &&
-                           n <= kDtMaxTokens && k <= kDtMaxK && nbf <= kDtMaxBlocks &&
-                           (k + 1) / 2 <= kDtSlots / dt_u;
+                           n <= kDtMaxTokens && ke <= kDtMaxK && nbf <= kDtMaxBlocks &&
+                           (ke + 1) / 2 <= kDtSlotsShared / dt_u;
   if (token_major) return launch_down_tok<BITS, DBG>(a, hq, hsc, dbg, dt_u);
   if (a.stages & MOE_DECODE_DOWN) {
     const long long dn_items = max_chunks * ((d + kWave - 1) / kWave);

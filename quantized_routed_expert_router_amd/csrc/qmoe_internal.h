@@ -107,21 +107,25 @@ __host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~(size
 constexpr int kMaxChunkPairs = 8;
 constexpr int kChunkInts = 32;
 
+// Whether the layer carries a shared expert (moe_layer.shared_*).
+inline bool has_shared(const moe_layer& L) { return L.shared_gate.codes != nullptr; }
+
+// Pairs Q = n*k, plus n with a shared expert (token t's shared pair is n*k + t).
 struct DecodeWs {
-  size_t chunks;   // int [n*k][kChunkInts] work records
+  size_t chunks;   // int [Q][kChunkInts] work records
   size_t nchunks;  // int  [1]
   size_t xq;       // int8 [n][d]  permuted activation codes
   size_t xsc;      // double2 [n][d/32]   (scale, scale*sum of codes)
-  size_t hq;       // int8 [n*k][f] permuted hidden codes
-  size_t hsc;      // double2 [n*k][f/32]
-  size_t y;        // double [n*k][d]
+  size_t hq;       // int8 [Q][f] permuted hidden codes
+  size_t hsc;      // double2 [Q][f/32]
+  size_t y;        // double [Q][d]
   size_t total;
 };
 
-inline DecodeWs decode_ws_layout(int n, int k, int d, int f) {
+inline DecodeWs decode_ws_layout(int n, int k, int d, int f, bool shared) {
   DecodeWs L;
   size_t o = 0;
-  const size_t P = (size_t)n * k;
+  const size_t P = (size_t)n * k + (shared ? (size_t)n : 0);
   L.chunks = o;
   o = align256(o + sizeof(int) * kChunkInts * (P + 1));
   L.nchunks = o;

@@ -47,7 +47,8 @@ class _QMatrix(ctypes.Structure):
 class _Layer(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
-                ("gate", _QMatrix), ("up", _QMatrix), ("down", _QMatrix)]
+                ("gate", _QMatrix), ("up", _QMatrix), ("down", _QMatrix),
+                ("shared_gate", _QMatrix), ("shared_up", _QMatrix), ("shared_down", _QMatrix)]
 
 
 class _Routing(ctypes.Structure):
@@ -127,6 +128,8 @@ class QMatrix:
 
 @dataclass
 class Layer:
+    """One MoE layer: E routed experts, and optionally one always-active shared expert
+    (`shared` = its (gate, up, down), one expert each in the routed experts' format)."""
     d_model: int
     d_ff: int
     n_experts: int
@@ -134,10 +137,16 @@ class Layer:
     gate: QMatrix
     up: QMatrix
     down: QMatrix
+    shared: tuple[QMatrix, QMatrix, QMatrix] | None = None
 
     def _struct(self) -> _Layer:
+        sh = [m._struct() for m in self.shared] if self.shared else [_QMatrix()] * 3
         return _Layer(self.d_model, self.d_ff, self.n_experts, self.top_k, self.gate._struct(),
-                      self.up._struct(), self.down._struct())
+                      self.up._struct(), self.down._struct(), *sh)
+
+    def pairs(self, n: int) -> int:
+        """Pair slots of an n-token window: n*k routed, plus n shared (pair n*k + t)."""
+        return n * self.top_k + (n if self.shared else 0)
 
 
 @dataclass
@@ -191,8 +200,8 @@ def workspace(layer: Layer, n_tokens: int, prefill: bool = False, device="cuda")
 
 
 def debug_buffers(layer: Layer, n: int, device="cuda") -> dict:
-    d, f, k = layer.d_model, layer.d_ff, layer.top_k
-    P = n * k
+    d, f = layer.d_model, layer.d_ff
+    P = layer.pairs(n)
     z = lambda shape, dt: torch.zeros(shape, dtype=dt, device=device)  # noqa: E731
     return dict(xq=z((n, d), torch.int8), xs=z((n, d // 32), torch.float32),
                 gate_dots=z((P, f, d // 32), torch.int32), up_dots=z((P, f, d // 32), torch.int32),

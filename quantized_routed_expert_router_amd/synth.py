@@ -34,6 +34,7 @@ LIB = os.path.join(PKG_DIR, "libqmoe_synth.so")
 
 # tensor ids of the counter-based streams
 T_GATE, T_UP, T_DOWN, T_X, T_LOGITS, T_PERM = 1, 2, 3, 4, 5, 6
+T_SHARED_GATE, T_SHARED_UP, T_SHARED_DOWN = 7, 8, 9  # the always-active shared expert
 
 SIGMA_W = 0.02
 ZIPF_S = 1.1
@@ -221,6 +222,17 @@ def host_layer(w: Workload, layer: int, experts=None, nthreads: int = 0):
     u = fill_matrix_host(empty_matrix(w.E, w.f, w.d, w.bits), w.seed, layer, T_UP, experts,
                          nthreads=nthreads)
     dn = fill_matrix_host(empty_matrix(w.E, w.d, w.f, w.bits), w.seed, layer, T_DOWN, experts,
+                          nthreads=nthreads)
+    return g, u, dn
+
+
+def host_shared(w: Workload, layer: int, nthreads: int = 0):
+    """(gate, up, down) HostMatrix of the layer's shared expert (one expert, E = 1)."""
+    g = fill_matrix_host(empty_matrix(1, w.f, w.d, w.bits), w.seed, layer, T_SHARED_GATE,
+                         nthreads=nthreads)
+    u = fill_matrix_host(empty_matrix(1, w.f, w.d, w.bits), w.seed, layer, T_SHARED_UP,
+                         nthreads=nthreads)
+    dn = fill_matrix_host(empty_matrix(1, w.d, w.f, w.bits), w.seed, layer, T_SHARED_DOWN,
                           nthreads=nthreads)
     return g, u, dn
 

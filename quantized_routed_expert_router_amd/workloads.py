@@ -26,12 +26,21 @@ def device_matrix(w: synth.Workload, layer: int, tensor: int, rows: int, cols: i
     return qmoe.QMatrix(codes, sm, rows, cols, w.bits)
 
 
-def device_layer(w: synth.Workload, layer: int, device="cuda") -> qmoe.Layer:
-    """All E experts of one layer instance generated on the GPU."""
+def device_layer(w: synth.Workload, layer: int, device="cuda", shared: bool = False) -> qmoe.Layer:
+    """All E experts of one layer instance generated on the GPU (and its shared expert)."""
     return qmoe.Layer(w.d, w.f, w.E, w.k,
                       device_matrix(w, layer, synth.T_GATE, w.f, w.d, device),
                       device_matrix(w, layer, synth.T_UP, w.f, w.d, device),
-                      device_matrix(w, layer, synth.T_DOWN, w.d, w.f, device))
+                      device_matrix(w, layer, synth.T_DOWN, w.d, w.f, device),
+                      device_shared(w, layer, device) if shared else None)
+
+
+def device_shared(w: synth.Workload, layer: int, device="cuda"):
+    """(gate, up, down) of the layer's shared expert (one expert) generated on the GPU."""
+    one = synth.Workload(w.name, w.d, w.f, 1, w.k, w.n, w.bits, w.logits, seed=w.seed)
+    return (device_matrix(one, layer, synth.T_SHARED_GATE, w.f, w.d, device),
+            device_matrix(one, layer, synth.T_SHARED_UP, w.f, w.d, device),
+            device_matrix(one, layer, synth.T_SHARED_DOWN, w.d, w.f, device))
 
 
 def matrix_from_host(m: synth.HostMatrix, device="cuda") -> qmoe.QMatrix:
@@ -41,10 +50,12 @@ def matrix_from_host(m: synth.HostMatrix, device="cuda") -> qmoe.QMatrix:
 
 
 def layer_from_host(gate: synth.HostMatrix, up: synth.HostMatrix, down: synth.HostMatrix, k: int,
-                    device="cuda") -> qmoe.Layer:
+                    device="cuda", shared=None) -> qmoe.Layer:
+    """Layer from host matrices; `shared`: optional (gate, up, down) HostMatrix, E = 1."""
     E = gate.codes.shape[0]
+    sh = None if shared is None else tuple(matrix_from_host(m, device) for m in shared)
     return qmoe.Layer(gate.cols, gate.rows, E, k, matrix_from_host(gate, device),
-                      matrix_from_host(up, device), matrix_from_host(down, device))
+                      matrix_from_host(up, device), matrix_from_host(down, device), sh)
 
 
 def matrix_to_host(m: qmoe.QMatrix, E: int) -> synth.HostMatrix:

@@ -53,14 +53,16 @@ def check_routing(lg: np.ndarray, k: int, routing: qmoe.Routing):
     return ids_o, w_o
 
 
-def compare_decode_traces(dbg: dict, tr: dict, layer_host, ids: np.ndarray, bits: int):
+def compare_decode_traces(dbg: dict, tr: dict, layer_host, ids: np.ndarray, bits: int,
+                          shared_down=None):
     """Bit-exact checks of the integer intermediates; near-exact float intermediates.
 
     h is a binary64 sum on both sides rounded to fp32, so it agrees except where the two
     summation orders straddle an fp32 rounding boundary; an h code may then legitimately
     differ. Where h agrees, the codes must agree; everywhere, the GPU codes must be the
     quantization of the GPU's own h, and the GPU down dots must be the exact dots of the
-    GPU's codes.
+    GPU's codes. With a shared expert (`shared_down` its down HostMatrix), pairs n*k + t
+    are token t's shared pairs.
     """
     g_h, u_h, d_h = layer_host
     k = ids.shape[1]
@@ -88,10 +90,12 @@ def compare_decode_traces(dbg: dict, tr: dict, layer_host, ids: np.ndarray, bits
     if "down_dots" in dbg:
         dd = dbg["down_dots"].cpu().numpy()
         Qd = unpack_codes(d_h.codes, bits)
+        Qs = None if shared_down is None else unpack_codes(shared_down.codes, bits)[0]
         d, f = d_h.rows, d_h.cols
+        P = ids.size
         for p in range(hq.shape[0]):
-            e = ids.ravel()[p]
-            ref = np.einsum("rbi,bi->rb", Qd[e].reshape(d, f // 32, 32),
+            W = Qd[ids.ravel()[p]] if p < P else Qs
+            ref = np.einsum("rbi,bi->rb", W.reshape(d, f // 32, 32),
                             hq[p].astype(np.int64).reshape(f // 32, 32))
             assert np.array_equal(dd[p], ref), f"down dots pair {p}"
     return frac_diff

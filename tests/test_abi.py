@@ -188,3 +188,47 @@ def test_layer_decode_argument_checks():
     assert qmoe.lib.moe_layer_decode(ctypes.byref(L), FAKE + 0x900000, FAKE + 0x600000, 4,
                                      ctypes.byref(r), FAKE + 0x700000, FAKE + 0x800000, 1 << 30,
                                      None, None) == UNSUPPORTED
+
+
+def _with_shared(L, bits=4, base=FAKE + 0x20000000):
+    d, f = L.d_model, L.d_ff
+    L.shared_gate = _mat(f, d, bits, codes=base, sm=base + 0x1000000)
+    L.shared_up = _mat(f, d, bits, codes=base + 0x2000000, sm=base + 0x3000000)
+    L.shared_down = _mat(d, f, bits, codes=base + 0x4000000, sm=base + 0x5000000)
+    return L
+
+
+def test_shared_expert_argument_checks():
+    # a shared expert is validated like the routed matrices, and the decode entry points take
+    # it only on their small-window path; every call here is rejected before launch
+    L = _with_shared(_layer())
+    L.shared_up = _mat(100, 256, 4)                                      # wrong rows
+    assert _decode(L) == INVALID
+    L = _with_shared(_layer())
+    L.shared_down = _mat(256, 128, 2)                                    # other bit width
+    assert _decode(L) == INVALID
+    L = _with_shared(_layer())
+    L.shared_gate = _mat(128, 256, 4, codes=FAKE + 4)                    # codes misaligned
+    assert _decode(L) == INVALID
+    assert _decode(_with_shared(_layer()), n=9) == UNSUPPORTED           # window above 8
+    assert _decode(_with_shared(_layer(E=512, k=10)), n=7) == UNSUPPORTED  # 70 pairs
+    assert _decode(_with_shared(_layer(E=512, k=16)), n=1) == UNSUPPORTED  # 17 slots a token
+    assert _decode(_with_shared(_layer(f=2048)), n=1) == UNSUPPORTED     # d_ff above 1024
+    assert _decode(_with_shared(_layer()), n=0, x=0, res=0, ws=0, ws_bytes=0) == OK
+    # the down stage without the combine (expert-major down) has no shared slot
+    r = _routing()
+    st = lambda stages: qmoe.lib.moe_expert_ffn_decode_stages(  # noqa: E731
+        ctypes.byref(_with_shared(_layer())), FAKE + 0x600000, 4, ctypes.byref(r),
+        FAKE + 0x700000, FAKE + 0x800000, 1 << 30, None, stages, None)
+    assert st(qmoe.DECODE_DOWN) == UNSUPPORTED
+    assert st(qmoe.DECODE_COMBINE) == UNSUPPORTED
+    assert st(qmoe.DECODE_PREP | qmoe.DECODE_GATE_UP | qmoe.DECODE_DOWN) == UNSUPPORTED
+    # the prefill entry points have no shared expert
+    assert _prefill(_with_shared(_layer())) == UNSUPPORTED
+    # the workspace holds n more pairs
+    a = qmoe.lib.moe_ffn_workspace_bytes(ctypes.byref(_layer(d=2048, f=768, E=512, k=10)), 4, 0)
+    b = qmoe.lib.moe_ffn_workspace_bytes(
+        ctypes.byref(_with_shared(_layer(d=2048, f=768, E=512, k=10))), 4, 0)
+    assert b >= a + 4 * (768 + 8 * 2048)
+    need = b
+    assert _decode(_with_shared(_layer(d=2048, f=768, E=512, k=10)), ws_bytes=need - 1) == WS_SMALL
