@@ -51,6 +51,7 @@ def lib():
         vp, i32 = ctypes.c_void_p, ctypes.c_int
         L.orc_route.argtypes = [vp, i32, i32, i32, vp, vp]
         L.orc_group.argtypes = [vp, i32, i32, i32, vp, vp]
+        L.orc_router_logits.argtypes = [vp, vp, i32, i32, i32, vp]
         L.orc_quant_act.argtypes = [vp, ctypes.c_int64, vp, vp]
         L.orc_quant_act.restype = None
         L.orc_weight.argtypes = [ctypes.POINTER(_Matrix), i32, i32, i32]
@@ -104,6 +105,19 @@ def route(logits: np.ndarray, k: int):
     if lib().orc_route(_p(logits), n, E, k, _p(ids), _p(w)) != 0:
         raise ValueError("orc_route: bad arguments")
     return ids, w
+
+
+def router_logits(W_bf16: np.ndarray, x: np.ndarray) -> np.ndarray:
+    """Router logits [n, E] fp32 of x [n, d] against bf16 rows W_bf16 [E, d] (uint16)."""
+    W = _c(W_bf16, np.uint16)
+    x = _c(x, np.float32)
+    n, d = x.shape
+    E = W.shape[0]
+    assert W.shape == (E, d)
+    out = np.zeros((n, E), np.float32)
+    if lib().orc_router_logits(_p(W), _p(x), n, d, E, _p(out)) != 0:
+        raise ValueError("orc_router_logits: bad arguments")
+    return out
 
 
 def group(ids: np.ndarray, E: int):

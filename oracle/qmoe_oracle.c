@@ -26,6 +26,11 @@
  *   combine  - routing-weighted sum of the k expert outputs added into the residual
  *              (same page, "Doorbell handshake": combine expert outputs, write back
  *              the residual).
+ *   router   - the router's logits of a token: the dot product of its MoE input x with
+ *              each expert's router row (the router runs on the GPU per the memory table
+ *              of "Architecture overview"; its weight precision is not given by the pages:
+ *              rows are bf16 here, x fp32, each product exact in binary64, the sum over
+ *              the model dimension in binary64, rounded once to binary32);
  *   shared   - optionally one always-active shared expert of the routed experts' shape
  *              and quantization, run for every token and added with weight 1 after the
  *              routed slots (reading of the model table's "10+1" active experts per
@@ -177,6 +182,25 @@ int orc_route(const float* logits, int n, int E, int k, int32_t* ids, float* w) 
   }
   free(taken);
   free(ex);
+  return 0;
+}
+
+/* ---- router: logits[t][e] = sum_c x[t][c] * W[e][c] ----------------------------- */
+
+/* W: bf16 bit patterns, [E][d] row-major (row e holds expert e's router weights).
+ * Each product bf16 x fp32 is exact in binary64; the sum runs over c in increasing order
+ * in binary64 and is rounded to binary32 once. Returns 0, or 1 on bad arguments. */
+int orc_router_logits(const uint16_t* W, const float* x, int n, int d, int E, float* logits) {
+  if (n < 0 || d < 1 || E < 1) return 1;
+  for (int t = 0; t < n; ++t) {
+    const float* xt = x + (size_t)t * d;
+    for (int e = 0; e < E; ++e) {
+      const uint16_t* we = W + (size_t)e * d;
+      double acc = 0.0;
+      for (int c = 0; c < d; ++c) acc += bf16_to_double(we[c]) * (double)xt[c];
+      logits[(size_t)t * E + e] = (float)acc;
+    }
+  }
   return 0;
 }
 

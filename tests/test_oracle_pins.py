@@ -76,6 +76,52 @@ def test_route_k1_and_k_equals_E():
 
 # ------------------------------------------------------------------ group
 
+# ---- router projection: logits[t][e] = sum_c x[t][c] * W[e][c], bf16 rows, fp32 x
+
+def test_router_logits_exact_integer_case():
+    # small integers: every product and partial sum is an exact integer, so any order of
+    # summation gives the same value; E != d catches a transposed operand
+    rng = np.random.default_rng(11)
+    n, d, E = 5, 96, 37
+    Wi = rng.integers(-8, 9, (E, d))
+    xi = rng.integers(-50, 51, (n, d))
+    W = synth.to_bf16_bits(Wi.astype(np.float32))
+    out = O.router_logits(W, xi.astype(np.float32))
+    assert np.array_equal(out, (xi @ Wi.T).astype(np.float32))
+
+
+def test_router_logits_one_hot_rows_pick_columns():
+    rng = np.random.default_rng(12)
+    n, d, E = 3, 64, 40
+    cols = rng.permutation(d)[:E]
+    Wf = np.zeros((E, d), np.float32)
+    Wf[np.arange(E), cols] = 1.0
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    out = O.router_logits(synth.to_bf16_bits(Wf), x)
+    assert np.array_equal(out, x[:, cols])
+
+
+def test_router_logits_bf16_hand_cases():
+    # 0x3f80 = 1, 0xc040 = -3, 0x8000 = -0, 0x0001 = 2^-133 (smallest bf16 subnormal)
+    W = np.array([[0x3F80, 0], [0xC040, 0], [0x8000, 0], [0x0001, 0]], np.uint16)
+    x = np.array([[2.0 ** 100, 7.0]], np.float32)
+    out = O.router_logits(W, x)
+    assert out.tolist() == [[2.0 ** 100, -3.0 * 2.0 ** 100, 0.0, 2.0 ** -33]]
+
+
+def test_router_logits_random_vs_dense_fp64():
+    rng = np.random.default_rng(13)
+    n, d, E = 4, 2048, 64
+    W = synth.to_bf16_bits((rng.standard_normal((E, d)) / np.sqrt(d)).astype(np.float32))
+    x = rng.standard_normal((n, d)).astype(np.float32)
+    out = O.router_logits(W, x)
+    ref = (x.astype(np.float64) @ bf16_to_f64(W).T).astype(np.float32)
+    np.testing.assert_array_max_ulp(out, ref, maxulp=1)
+    # exact symmetries: a power-of-two scale and a sign flip commute with every rounding
+    assert np.array_equal(O.router_logits(W, 4.0 * x), 4.0 * out)
+    assert np.array_equal(O.router_logits(W, -x), -out)
+
+
 def test_group_is_stable_counting_sort():
     rng = np.random.default_rng(4)
     for n, k, E in [(5, 3, 7), (64, 10, 512), (1, 2, 8), (0, 2, 8)]:
