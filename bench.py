@@ -55,6 +55,11 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true",
                     help="--config 4: skip the HIP-graph replay of the 48-layer step")
+    ap.add_argument("--experts", type=int, default=512, choices=[512, 256],
+                    help="experts per layer (256: the pruned Coder model, still top-10)")
+    ap.add_argument("--router", action="store_true",
+                    help="--config 2 or 4: each layer projects its own router logits from x "
+                         "(bf16 router rows) instead of taking the workload's logits")
     ap.add_argument("--shared", action="store_true",
                     help="--config 2 or 4: layers with one always-active shared expert")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -78,12 +83,14 @@ class Step:
         self.rout_s = routing._struct()
         self.routing = routing
         self.lg, self.x, self.res, self.ws = lg, x, res, ws
-        self.n, self.E = lg.shape
+        self.n, self.E = x.shape[0], layer.n_experts
         self.k = layer.top_k
+        # no logits: the layer projects them from x with its router rows
+        self.lg_ptr = None if lg is None else lg.data_ptr()
 
     def layer(self, stream, stages):
         rc = self.q.lib.moe_layer_decode_stages(
-            ctypes.byref(self.layer_s), self.lg.data_ptr(), self.x.data_ptr(), self.n,
+            ctypes.byref(self.layer_s), self.lg_ptr, self.x.data_ptr(), self.n,
             ctypes.byref(self.rout_s), self.res.data_ptr(), self.ws.data_ptr(), self.ws.numel(),
             None, stages, stream)
         assert rc == 0, rc
@@ -222,21 +229,26 @@ def measured_traffic(profile_path):
 def bench_decode(args, torch, q, synth, workloads):
     import numpy as np
 
-    w = synth.config(args.config, args.T)
+    w = synth.config(args.config, args.T, args.experts)
     shared = args.shared and args.config == 2
+    router = args.router and args.config == 2
     if shared:
         w.name += "_shared1"
+    if router:
+        w.name += "_router"
+    # the headline line: configuration 2 as the workload defines it
+    primary = args.config == 2 and not shared and not router and args.experts == 512
     L = args.instances or (10 if args.config == 2 else 3)
     log(f"workload {w.name}: generating {L} layer instances on the GPU")
     t0 = time.perf_counter()
     steps, inputs = [], []
     for i in range(L):
         # one workspace per instance: stages can be replayed
-        ws = q.workspace(_shape_layer(q, w, shared), w.n)
-        layer = workloads.device_layer(w, i, shared=shared)
+        ws = q.workspace(_shape_layer(q, w, shared, router), w.n)
+        layer = workloads.device_layer(w, i, shared=shared, router=router)
         lg, x = synth.layer_inputs(w, i)
         inputs.append((lg, x))
-        lg_d = torch.from_numpy(lg).cuda()
+        lg_d = None if router else torch.from_numpy(lg).cuda()
         x_d = torch.from_numpy(x).cuda()
         routing = q.Routing.empty(w.n, w.E, w.k)
         steps.append(Step(q, layer, lg_d, x_d, x_d.clone(), routing, ws))
@@ -279,14 +291,14 @@ def bench_decode(args, torch, q, synth, workloads):
     stage_us["gate_up_back_to_back"] = round(gu_ms / len(order) * 1e3, 2)
     mean_touched = float(np.mean([touched[i] for i in order]))
     rec = {
-        "metric": METRIC if args.config == 2 else f"{METRIC} [supplementary: {w.name}]",
+        "metric": METRIC if primary else f"{METRIC} [supplementary: {w.name}]",
         "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(total_ms / len(order), 5),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
         "data": "synthetic",
         "config": {"workload": w.name, "d_model": w.d, "d_ff": w.f, "experts": w.E,
                    "top_k": w.k, "tokens_per_step": w.n, "weight_bits": w.bits,
-                   "layer_instances": L, "shared_expert": shared,
+                   "layer_instances": L, "shared_expert": shared, "router_projection": router,
                    "step": "moe_layer_decode (routing + expert FFN: x quant, gate/up, SwiGLU, "
                            "h quant, down, combine)"},
         "tokens_per_s": round(tok_s, 1),
@@ -297,17 +309,16 @@ def bench_decode(args, torch, q, synth, workloads):
         "roofline": {"bound": "hbm", "kernel": "k_gateup (gate/up + SwiGLU + h quant)",
                      "achieved": round(gu_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_ach / HBM_PEAK_GBS, 4),
-                     "traffic": (measured_traffic(TRAFFIC_PROFILE)
-                                 if args.config == 2 and not shared else None),
+                     "traffic": measured_traffic(TRAFFIC_PROFILE) if primary else None,
                      "bytes_per_launch": round(float(np.mean([gu_bytes[i] for i in order])), 1)},
     }
-    if args.config == 2 and not shared and not args.no_cpu_baseline:
+    if primary and not args.no_cpu_baseline:
         log("CPU oracle baseline ...")
         rec["cpu_baseline"] = cpu_baseline(w, inputs, args.cpu_seconds)
     return rec
 
 
-def _shape_layer(q, w, shared=False):
+def _shape_layer(q, w, shared=False, router=False):
     """A layer description with the right sizes for workspace queries (no weights)."""
     import torch
 
@@ -315,25 +326,29 @@ def _shape_layer(q, w, shared=False):
     dummy16 = torch.empty(16, dtype=torch.int16, device="cuda")
     mk = lambda r, c: q.QMatrix(dummy, dummy16, r, c, w.bits)  # noqa: E731
     sh = (mk(w.f, w.d), mk(w.f, w.d), mk(w.d, w.f)) if shared else None
-    return q.Layer(w.d, w.f, w.E, w.k, mk(w.f, w.d), mk(w.f, w.d), mk(w.d, w.f), sh)
+    rt = torch.empty((w.E, w.d), dtype=torch.int16, device="cuda") if router else None
+    return q.Layer(w.d, w.f, w.E, w.k, mk(w.f, w.d), mk(w.f, w.d), mk(w.d, w.f), sh, rt)
 
 
 def bench_chain(args, torch, q, synth, workloads):
     import numpy as np
 
-    w = synth.config(4)
-    shared = args.shared
+    w = synth.config(4, experts=args.experts)
+    shared, router = args.shared, args.router
     if shared:
         w.name += "_shared1"
+    if router:
+        w.name += "_router"
     log(f"workload {w.name}: generating {w.layers} layers on the GPU")
     t0 = time.perf_counter()
-    ws = q.workspace(_shape_layer(q, w, shared), w.n)
+    ws = q.workspace(_shape_layer(q, w, shared, router), w.n)
     x0 = torch.from_numpy(synth.activations(w.seed, 0, w.n, w.d)).cuda()
     res = x0.clone()
     steps = []
     for l_ in range(w.layers):
-        layer = workloads.device_layer(w, l_, shared=shared)
-        lg = torch.from_numpy(synth.logits(w.seed, l_, w.n, w.E, w.logits)).cuda()
+        layer = workloads.device_layer(w, l_, shared=shared, router=router)
+        lg = (None if router else
+              torch.from_numpy(synth.logits(w.seed, l_, w.n, w.E, w.logits)).cuda())
         routing = q.Routing.empty(w.n, w.E, w.k)
         steps.append(Step(q, layer, lg, res, res, routing, ws))  # x is the residual stream
     torch.cuda.synchronize()
@@ -352,14 +367,17 @@ def bench_chain(args, torch, q, synth, workloads):
     n_chain = len(order) // w.layers
     sec = total_ms * 1e-3
     value = chain_bytes * n_chain / sec / 1e9
-    graph = None if args.no_graph else chain_graph(torch, steps, n_chain, chain_bytes, w)
+    per_layer = 4 if router else 3  # (router projection,) route+prep, gate/up, down+combine
+    graph = (None if args.no_graph else
+             chain_graph(torch, steps, n_chain, chain_bytes, w, per_layer))
     return {
         "metric": f"{METRIC} [supplementary: {w.name}]", "value": round(value, 2), "unit": "GB/s",
         "n_gpus": 1, "steps": n_chain, "warmup": 1, "ms_per_step": round(total_ms / n_chain, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "i8",
         "data": "synthetic",
         "config": {"workload": w.name, "layers": w.layers, "tokens_per_step": w.n,
-                   "shared_expert": shared, "step": "48 x moe_layer_decode, residual chained"},
+                   "shared_expert": shared, "router_projection": router,
+                   "step": "48 x moe_layer_decode, residual chained"},
         "tokens_per_s": round(n_chain * w.n / sec, 1),
         "pct_of_hbm_peak": round(100.0 * value / HBM_PEAK_GBS, 2),
         "expert_bytes_per_step": chain_bytes,
@@ -371,8 +389,8 @@ def bench_chain(args, torch, q, synth, workloads):
     }
 
 
-def chain_graph(torch, steps, replays, chain_bytes, w):
-    """The 48-layer step captured once as a HIP graph (144 kernel launches) and replayed
+def chain_graph(torch, steps, replays, chain_bytes, w, per_layer=3):
+    """The 48-layer step captured once as a HIP graph (3 or 4 launches per layer) and replayed
     back to back: no host launch cost per layer and no spin kernel needed. The launches
     use no memset and no allocation, so the captured step is the eager one."""
     stream = torch.cuda.Stream()
@@ -395,7 +413,7 @@ def chain_graph(torch, steps, replays, chain_bytes, w):
     ms = start.elapsed_time(end) / replays
     return {"ms_per_step": round(ms, 4), "value_GBs": round(chain_bytes / (ms * 1e-3) / 1e9, 2),
             "tokens_per_s": round(w.n / (ms * 1e-3), 1), "replays": replays,
-            "kernels_per_step": 3 * len(steps)}
+            "kernels_per_step": per_layer * len(steps)}
 
 
 class PrefillStep:
@@ -448,7 +466,7 @@ def bench_prefill(args, torch, q, synth, workloads):
     """8192-token prefill chunk: route + bf16 matrix-core expert FFN per step."""
     import numpy as np
 
-    w = synth.config(5)
+    w = synth.config(5, experts=args.experts)
     L = args.instances or 2
     log(f"workload {w.name}: generating {L} layer instances on the GPU")
     steps = []

@@ -99,6 +99,12 @@ typedef struct {
    * the down and combine stages issued together; otherwise, and by the prefill entry
    * points, MOE_ERR_UNSUPPORTED. */
   moe_qmatrix shared_gate, shared_up, shared_down;
+  /* Optional router weights, for moe_layer_decode called without logits: bf16 bit
+   * patterns, [E][d] row-major (row e holds expert e's weights), 16-byte aligned.
+   * logits[t][e] = sum_c x[t][c] * router_w[e][c], each product exact and the sum in
+   * binary64, rounded once to fp32 (the engine explainer's memory table keeps the router
+   * on the GPU; the pages give no precision for its weights). NULL: none. */
+  const uint16_t* router_w;
 } moe_layer;
 
 /* Routing record of n tokens (all device memory), written by moe_route and read by the
@@ -127,7 +133,9 @@ typedef struct {
  *   h fp32 [n*k][f]                               SwiGLU output, the value quantized
  *   hq int8 [n*k][f], hs fp32 [n*k][f/32]         hidden codes and block scales
  *   down_dots int32 [n*k][d][f/32]                exact per-block integer dots
- *   y fp32 [n*k][d]                               expert output of each pair */
+ *   y fp32 [n*k][d]                               expert output of each pair
+ *   logits fp32 [n][E]                            router logits (moe_layer_decode
+ *                                                 projecting with router_w only) */
 typedef struct {
   int8_t* xq;
   float* xs;
@@ -140,6 +148,7 @@ typedef struct {
   float* hs;
   int32_t* down_dots;
   float* y;
+  float* logits;
 } moe_debug;
 
 /* Human-readable name of a status code (static storage). */
@@ -198,9 +207,12 @@ moe_status moe_expert_ffn_decode_stages(const moe_layer* L, const float* x, int 
  * kernel of the layer. The router hands expert ids and weights to the expert pass
  * (Strata engine explainer, m.lqnn.cn/news/264700, "Doorbell handshake": routing ends
  * the first half of a layer, combine and residual write-back end the second). logits:
- * device fp32 [n][E]; r receives the routing exactly as moe_route writes it; all other
- * arguments, limits and errors as moe_expert_ffn_decode, plus MOE_ERR_INVALID_ARGUMENT
- * for NULL logits when n > 0. n == 0 only writes zero expert offsets. */
+ * device fp32 [n][E], or NULL when the layer has router weights (L->router_w): the
+ * layer then projects x onto the router rows first (one more launch in the PREP stage;
+ * the logits go to the workspace, and to dbg->logits when given). r receives the
+ * routing exactly as moe_route writes it for those logits; all other arguments, limits
+ * and errors as moe_expert_ffn_decode, plus MOE_ERR_INVALID_ARGUMENT for NULL logits
+ * without router weights when n > 0. n == 0 only writes zero expert offsets. */
 moe_status moe_layer_decode(const moe_layer* L, const float* logits, const float* x,
                             int n_tokens, const moe_routing* r, float* residual, void* ws,
                             size_t ws_bytes, const moe_debug* dbg, void* stream);

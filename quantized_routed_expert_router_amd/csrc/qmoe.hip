@@ -54,6 +54,7 @@ moe_status check_layer(const moe_layer* L) {
   moe_status s = check_matrix(L->gate, f, d, bits);
   if (s == MOE_OK) s = check_matrix(L->up, f, d, bits);
   if (s == MOE_OK) s = check_matrix(L->down, d, f, bits);
+  if (s == MOE_OK && L->router_w && !aligned(L->router_w, 16)) s = MOE_ERR_INVALID_ARGUMENT;
   if (s == MOE_OK && has_shared(*L)) {
     s = check_matrix(L->shared_gate, f, d, bits);
     if (s == MOE_OK) s = check_matrix(L->shared_up, f, d, bits);
@@ -79,9 +80,9 @@ moe_status check_routing(const moe_routing* r) {
   return MOE_OK;
 }
 
-moe_status decode_entry(const moe_layer* L, const float* logits, const float* x, int n_tokens,
-                        const moe_routing* r, float* residual, void* ws, size_t ws_bytes,
-                        const moe_debug* dbg, unsigned stages, void* stream) {
+moe_status decode_entry(const moe_layer* L, const float* logits, bool project, const float* x,
+                        int n_tokens, const moe_routing* r, float* residual, void* ws,
+                        size_t ws_bytes, const moe_debug* dbg, unsigned stages, void* stream) {
   if (stages == 0 || (stages & ~MOE_DECODE_ALL)) return MOE_ERR_INVALID_ARGUMENT;
   moe_status s = check_layer(L);
   if (s != MOE_OK) return s;
@@ -97,18 +98,19 @@ moe_status decode_entry(const moe_layer* L, const float* logits, const float* x,
   const size_t act_bytes = (size_t)n_tokens * L->d_model * sizeof(float);
   if (x != residual && overlaps(x, act_bytes, residual, act_bytes))
     return MOE_ERR_INVALID_ARGUMENT;
-  const size_t need =
-      decode_ws_layout(n_tokens, L->top_k, L->d_model, L->d_ff, has_shared(*L)).total;
+  const size_t need = decode_ws_layout(n_tokens, L->top_k, L->d_model, L->d_ff, has_shared(*L),
+                                       L->router_w ? L->n_experts : 0)
+                          .total;
   if (ws_bytes < need) return MOE_ERR_WORKSPACE_TOO_SMALL;
   if (overlaps(ws, need, residual, act_bytes) || overlaps(ws, need, x, act_bytes))
     return MOE_ERR_INVALID_ARGUMENT;
   DecodeDebug dd{};
   if (dbg) {
-    dd = DecodeDebug{dbg->xq, dbg->xs, dbg->gate_dots, dbg->up_dots, dbg->g,
-                     dbg->u,  dbg->h,  dbg->hq,        dbg->hs,      dbg->down_dots, dbg->y};
+    dd = DecodeDebug{dbg->xq, dbg->xs, dbg->gate_dots, dbg->up_dots,  dbg->g, dbg->u,
+                     dbg->h,  dbg->hq, dbg->hs,        dbg->down_dots, dbg->y, dbg->logits};
   }
-  DecodeArgs a{L, logits, x, n_tokens, r, residual, (char*)ws, dbg ? &dd : nullptr,
-               (hipStream_t)stream, device_cu_count(), stages};
+  DecodeArgs a{L,        logits, project, x, n_tokens, r, residual, (char*)ws,
+               dbg ? &dd : nullptr, (hipStream_t)stream, device_cu_count(), stages};
   const hipError_t err = launch_decode(a);
   return err == hipSuccess ? MOE_OK : MOE_ERR_HIP;
 }
@@ -170,7 +172,9 @@ size_t moe_ffn_workspace_bytes(const moe_layer* L, int n_tokens, int prefill) {
     if (E < 1 || E > MOE_MAX_EXPERTS) return 0;
     return prefill_ws_layout(n_tokens, k, d, f, E).total;
   }
-  return decode_ws_layout(n_tokens, k, d, f, has_shared(*L)).total;
+  const int E = L->n_experts;
+  if (L->router_w && (E < 1 || E > MOE_MAX_EXPERTS)) return 0;
+  return decode_ws_layout(n_tokens, k, d, f, has_shared(*L), L->router_w ? E : 0).total;
 }
 
 moe_status moe_expert_ffn_decode(const moe_layer* L, const float* x, int n_tokens,
@@ -184,7 +188,8 @@ moe_status moe_expert_ffn_decode_stages(const moe_layer* L, const float* x, int 
                                         const moe_routing* r, float* residual, void* ws,
                                         size_t ws_bytes, const moe_debug* dbg, unsigned stages,
                                         void* stream) {
-  return decode_entry(L, nullptr, x, n_tokens, r, residual, ws, ws_bytes, dbg, stages, stream);
+  return decode_entry(L, nullptr, false, x, n_tokens, r, residual, ws, ws_bytes, dbg, stages,
+                      stream);
 }
 
 moe_status moe_layer_decode(const moe_layer* L, const float* logits, const float* x,
@@ -198,7 +203,9 @@ moe_status moe_layer_decode_stages(const moe_layer* L, const float* logits, cons
                                    int n_tokens, const moe_routing* r, float* residual, void* ws,
                                    size_t ws_bytes, const moe_debug* dbg, unsigned stages,
                                    void* stream) {
-  if (n_tokens > 0 && !logits) return MOE_ERR_INVALID_ARGUMENT;
+  // without logits the layer projects its own from the router weights
+  const bool project = !logits && L && L->router_w;
+  if (n_tokens > 0 && !logits && !project) return MOE_ERR_INVALID_ARGUMENT;
   if (n_tokens == 0) {
     // no tokens: the routing still reports empty expert groups
     moe_status s = check_layer(L);
@@ -207,7 +214,8 @@ moe_status moe_layer_decode_stages(const moe_layer* L, const float* logits, cons
     if (!(stages & MOE_DECODE_PREP)) return MOE_OK;
     return moe_route(logits, 0, L->n_experts, L->top_k, r, nullptr, 0, stream);
   }
-  return decode_entry(L, logits, x, n_tokens, r, residual, ws, ws_bytes, dbg, stages, stream);
+  return decode_entry(L, logits, project, x, n_tokens, r, residual, ws, ws_bytes, dbg, stages,
+                      stream);
 }
 
 moe_status moe_expert_ffn_prefill(const moe_layer* L, const uint16_t* x_bf16, int n_tokens,

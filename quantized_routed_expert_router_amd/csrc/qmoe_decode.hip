@@ -212,6 +212,122 @@ __global__ __launch_bounds__(kPrepThreads) void k_route_prep(
   quant_x_block<BITS>(x, d, gid / nbd, gid % nbd, xq, xsc, dbg_xq, dbg_xs);
 }
 
+// ---------------------------------------------------------------- router projection
+
+// logits[t][e] = sum_c x[t][c] * W[e][c], W bf16 [E][d], x fp32 [n][d] (the layer's router;
+// the engine explainer keeps it on the GPU, "Architecture overview"). It is a launch of its
+// own ahead of k_route_prep: the top-k of a token needs all E logits, which come from many
+// workgroups, and a hand-off between workgroups inside one launch needs write-through
+// stores, an arrival counter and write-through loads, a chain of memory round trips of
+// the order of the 1.5 us kernel boundary.
+//
+// One workgroup per expert. The reduction axis is cut into passes of 512 columns, and wave
+// q of the workgroup takes passes q, q + 4, ...; lane l of a pass owns columns 8l .. 8l+7
+// of it and loads them straight from memory (router row and x: no other wave of the
+// workgroup needs them). Tokens go in groups of kRtTok, their four sums interleaved.
+// Every product (bf16 times fp32) is exact in binary64; a lane sums its columns in
+// increasing order, a DPP reduction gathers the 64 lane sums into lane 63, and the four
+// waves' sums are added in wave order and rounded to fp32 once.
+constexpr int kRtWaves = 4;
+constexpr int kRtThreads = kRtWaves * kWave;
+constexpr int kRtTok = 4;
+constexpr int kRtPass = 8 * kWave;  // columns per pass
+
+// Sum of a binary64 value over the wave, in lane 63: row shifts by 1, 2, 4 and 8 (lanes
+// without a source add 0), then row 0's total into row 1 and row 2's into row 3
+// (row_bcast:15), then rows 0-1's total into rows 2-3 (row_bcast:31). The order is fixed.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+  uint64_t u;
+  __builtin_memcpy(&u, &v, 8);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)u, CTRL, ROW_MASK, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(u >> 32), CTRL, ROW_MASK, 0xF, false);
+  u = ((uint64_t)hi << 32) | lo;
+  double r;
+  __builtin_memcpy(&r, &u, 8);
+  return r;
+}
+
+__device__ __forceinline__ double wave_sum_f64_to_last(double v) {
+  v += dpp_f64<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_f64<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_f64<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_f64<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_f64<0x142, 0xA>(v);  // row_bcast:15
+  v += dpp_f64<0x143, 0xC>(v);  // row_bcast:31
+  return v;
+}
+
+__global__ __launch_bounds__(kRtThreads) void k_router_logits(
+    const uint16_t* __restrict__ W, const float* __restrict__ x, int n, int d, int E,
+    float* __restrict__ logits, float* __restrict__ dbg_logits) {
+  __shared__ double red[kRtWaves][kRtTok];
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  typedef uint32_t v4u __attribute__((ext_vector_type(4)));
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int e = blockIdx.x;
+  const uint16_t* __restrict__ wrow = W + (size_t)e * d;
+  const int npass = (d + kRtPass - 1) / kRtPass;
+  for (int t0 = 0; t0 < n; t0 += kRtTok) {
+    double acc[kRtTok];
+#pragma unroll
+    for (int tt = 0; tt < kRtTok; ++tt) acc[tt] = 0.0;
+    for (int p = wave; p < npass; p += kRtWaves) {
+      // columns past d: clamped (valid) loads whose terms are dropped by a select
+      const int c = p * kRtPass + 8 * lane;
+      const bool use = c < d;
+      const int cc = min(c, d - 8);
+      const v4u wv = *reinterpret_cast<const __attribute__((address_space(1))) v4u*>(
+          reinterpret_cast<uintptr_t>(wrow + cc));
+      v4f xa[kRtTok], xb[kRtTok];
+#pragma unroll
+      for (int tt = 0; tt < kRtTok; ++tt) {
+        const float* xr = x + (size_t)min(t0 + tt, n - 1) * d + cc;
+        xa[tt] = *reinterpret_cast<const __attribute__((address_space(1))) v4f*>(
+            reinterpret_cast<uintptr_t>(xr));
+        xb[tt] = *reinterpret_cast<const __attribute__((address_space(1))) v4f*>(
+            reinterpret_cast<uintptr_t>(xr + 4));
+      }
+      __builtin_amdgcn_sched_barrier(0);  // all nine requests go out before any arithmetic
+      double wd[8];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        wd[2 * i] = (double)__uint_as_float(wv[i] << 16);
+        wd[2 * i + 1] = (double)__uint_as_float(wv[i] & 0xffff0000u);
+      }
+      double s[kRtTok];
+#pragma unroll
+      for (int tt = 0; tt < kRtTok; ++tt) s[tt] = acc[tt];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+#pragma unroll
+        for (int tt = 0; tt < kRtTok; ++tt) {
+          const float xv = i < 4 ? xa[tt][i] : xb[tt][i - 4];
+          s[tt] = __builtin_fma(wd[i], (double)xv, s[tt]);
+        }
+      }
+#pragma unroll
+      for (int tt = 0; tt < kRtTok; ++tt) acc[tt] = use ? s[tt] : acc[tt];
+    }
+#pragma unroll
+    for (int tt = 0; tt < kRtTok; ++tt) {
+      const double v = wave_sum_f64_to_last(acc[tt]);
+      if (lane == kWave - 1) red[wave][tt] = v;
+    }
+    __syncthreads();
+    if (tid < kRtTok && t0 + tid < n) {
+      double v = red[0][tid];
+#pragma unroll
+      for (int q = 1; q < kRtWaves; ++q) v += red[q][tid];  // wave order
+      const float lf = (float)v;
+      logits[(size_t)(t0 + tid) * E + e] = lf;
+      if (dbg_logits) dbg_logits[(size_t)(t0 + tid) * E + e] = lf;
+    }
+    __syncthreads();  // red is reused by the next token group
+  }
+}
+
 // ---------------------------------------------------------------- streaming block loads
 
 // One packed block (16 B at 4 bits, 8 B at 2 bits) through a buffer resource.
@@ -970,7 +1086,7 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   const moe_layer& L = *a.L;
   const int n = a.n, d = L.d_model, f = L.d_ff, k = L.top_k, E = L.n_experts;
   const bool shared = has_shared(L);  // only on the ids path (checked by the entry point)
-  const DecodeWs W = decode_ws_layout(n, k, d, f, shared);
+  const DecodeWs W = decode_ws_layout(n, k, d, f, shared, L.router_w ? E : 0);
   int* chunks = reinterpret_cast<int*>(a.ws + W.chunks);
   int* nchunks = reinterpret_cast<int*>(a.ws + W.nchunks);
   int8_t* xq = reinterpret_cast<int8_t*>(a.ws + W.xq);
@@ -986,9 +1102,18 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   // chunks straight from the expert ids (see k_gateup); with logits, the gate/up stage also
   // writes the routing's grouping
   const bool ids = n <= NPC && (long long)n * k <= kWave;
+  // logits to route from: the caller's, or the router projection's in the workspace
+  const float* logits = a.project ? reinterpret_cast<const float*>(a.ws + W.logits) : a.logits;
   if (a.stages & MOE_DECODE_PREP) {
+    if (a.project) {
+      hipLaunchKernelGGL(k_router_logits, dim3(E), dim3(kRtThreads),
+                         0, a.stream, L.router_w, a.x, n, d, E,
+                         reinterpret_cast<float*>(a.ws + W.logits), DBG ? dbg.logits : nullptr);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
     const int prep_blocks = 1 + (n * nbd + kPrepThreads - 1) / kPrepThreads;
-    if (a.logits && n <= kFusedMaxTokens) {
+    if (logits && n <= kFusedMaxTokens) {
       const int kpl = (E + kWave - 1) / kWave;
 #define QMOE_RP(G)                                                                        \
   (kpl <= 1   ? k_route_prep<BITS, 1, G>                                                  \
@@ -998,16 +1123,16 @@ hipError_t launch_ffn(const DecodeArgs& a) {
               : k_route_prep<BITS, 16, G>)
       auto kern = ids ? QMOE_RP(false) : QMOE_RP(true);
 #undef QMOE_RP
-      hipLaunchKernelGGL(kern, dim3(prep_blocks), dim3(kPrepThreads), 0, a.stream, a.logits, a.x,
+      hipLaunchKernelGGL(kern, dim3(prep_blocks), dim3(kPrepThreads), 0, a.stream, logits, a.x,
                          n, d, E, k, NPC, a.r->topk_ids, a.r->topk_w, a.r->expert_offsets,
                          a.r->pair_index, chunks, nchunks, xq, xsc, DBG ? dbg.xq : nullptr,
                          DBG ? dbg.xs : nullptr);
     } else {
-      if (a.logits) {
+      if (logits) {
         // the histograms of a multi-workgroup grouping live in the pair-output region,
         // which is only written later (it holds at least 256 bytes per pair, the
         // histograms at most 2 bytes per pair plus 4 KB)
-        err = launch_route(a.logits, n, E, k, a.r, a.ws + W.y, a.stream);
+        err = launch_route(logits, n, E, k, a.r, a.ws + W.y, a.stream);
         if (err != hipSuccess) return err;
       }
       hipLaunchKernelGGL(k_prep<BITS>, dim3(prep_blocks), dim3(kPrepThreads), 0, a.stream, a.x,
@@ -1028,7 +1153,7 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   if (a.stages & MOE_DECODE_GATE_UP) {
     // one workgroup per item; the shared expert is one more chunk
     const long long gu_items = (max_chunks + (shared ? 1 : 0)) * (f / kGuRows);
-    const bool group = ids && a.logits;  // workgroup 0 writes the routing's grouping
+    const bool group = ids && logits;  // workgroup 0 writes the routing's grouping
     const int gu_grid = (int)std::max<long long>(1, gu_items + (group ? 1 : 0));
     const uint32_t* gsm = reinterpret_cast<const uint32_t*>(L.gate.scale_min);
     const uint32_t* usm = reinterpret_cast<const uint32_t*>(L.up.scale_min);

@@ -119,10 +119,12 @@ struct DecodeWs {
   size_t hq;       // int8 [Q][f] permuted hidden codes
   size_t hsc;      // double2 [Q][f/32]
   size_t y;        // double [Q][d]
+  size_t logits;   // float [n][E] router logits (a layer with router weights), else empty
   size_t total;
 };
 
-inline DecodeWs decode_ws_layout(int n, int k, int d, int f, bool shared) {
+// router_E: E for a layer with router weights (its logits are projected into ws), else 0.
+inline DecodeWs decode_ws_layout(int n, int k, int d, int f, bool shared, int router_E) {
   DecodeWs L;
   size_t o = 0;
   const size_t P = (size_t)n * k + (shared ? (size_t)n : 0);
@@ -140,6 +142,8 @@ inline DecodeWs decode_ws_layout(int n, int k, int d, int f, bool shared) {
   o = align256(o + 16 * P * (f / 32));
   L.y = o;
   o = align256(o + 8 * P * d);
+  L.logits = o;
+  o = align256(o + 4 * (size_t)n * (size_t)router_E);
   L.total = o;
   return L;
 }
@@ -208,11 +212,13 @@ struct DecodeDebug {
   float* hs;
   int32_t* down_dots;
   float* y;
+  float* logits;
 };
 
 struct DecodeArgs {
   const moe_layer* L;
   const float* logits;  // non-null: route inside the prep stage (moe_layer_decode)
+  bool project;         // route from logits = x . router_w^T, projected into ws first
   const float* x;
   int n;
   const moe_routing* r;

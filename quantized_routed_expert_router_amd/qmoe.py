@@ -48,7 +48,8 @@ class _Layer(ctypes.Structure):
     _fields_ = [("d_model", ctypes.c_int32), ("d_ff", ctypes.c_int32),
                 ("n_experts", ctypes.c_int32), ("top_k", ctypes.c_int32),
                 ("gate", _QMatrix), ("up", _QMatrix), ("down", _QMatrix),
-                ("shared_gate", _QMatrix), ("shared_up", _QMatrix), ("shared_down", _QMatrix)]
+                ("shared_gate", _QMatrix), ("shared_up", _QMatrix), ("shared_down", _QMatrix),
+                ("router_w", ctypes.c_void_p)]
 
 
 class _Routing(ctypes.Structure):
@@ -56,7 +57,8 @@ class _Routing(ctypes.Structure):
                 ("expert_offsets", ctypes.c_void_p), ("pair_index", ctypes.c_void_p)]
 
 
-DEBUG_FIELDS = ("xq", "xs", "gate_dots", "up_dots", "g", "u", "h", "hq", "hs", "down_dots", "y")
+DEBUG_FIELDS = ("xq", "xs", "gate_dots", "up_dots", "g", "u", "h", "hq", "hs", "down_dots", "y",
+                "logits")
 
 
 class _Debug(ctypes.Structure):
@@ -128,8 +130,10 @@ class QMatrix:
 
 @dataclass
 class Layer:
-    """One MoE layer: E routed experts, and optionally one always-active shared expert
-    (`shared` = its (gate, up, down), one expert each in the routed experts' format)."""
+    """One MoE layer: E routed experts, optionally one always-active shared expert
+    (`shared` = its (gate, up, down), one expert each in the routed experts' format) and
+    optionally the router's weights (`router`: bf16 bits [E][d] in a 2-byte tensor), which
+    let layer_decode project its own logits."""
     d_model: int
     d_ff: int
     n_experts: int
@@ -138,11 +142,17 @@ class Layer:
     up: QMatrix
     down: QMatrix
     shared: tuple[QMatrix, QMatrix, QMatrix] | None = None
+    router: torch.Tensor | None = None
 
     def _struct(self) -> _Layer:
         sh = [m._struct() for m in self.shared] if self.shared else [_QMatrix()] * 3
+        rw = None
+        if self.router is not None:
+            assert self.router.element_size() == 2 and self.router.is_contiguous()
+            assert tuple(self.router.shape) == (self.n_experts, self.d_model)
+            rw = self.router.data_ptr()
         return _Layer(self.d_model, self.d_ff, self.n_experts, self.top_k, self.gate._struct(),
-                      self.up._struct(), self.down._struct(), *sh)
+                      self.up._struct(), self.down._struct(), *sh, rw)
 
     def pairs(self, n: int) -> int:
         """Pair slots of an n-token window: n*k routed, plus n shared (pair n*k + t)."""
@@ -207,7 +217,8 @@ def debug_buffers(layer: Layer, n: int, device="cuda") -> dict:
                 gate_dots=z((P, f, d // 32), torch.int32), up_dots=z((P, f, d // 32), torch.int32),
                 g=z((P, f), torch.float32), u=z((P, f), torch.float32), h=z((P, f), torch.float32),
                 hq=z((P, f), torch.int8), hs=z((P, f // 32), torch.float32),
-                down_dots=z((P, d, f // 32), torch.int32), y=z((P, d), torch.float32))
+                down_dots=z((P, d, f // 32), torch.int32), y=z((P, d), torch.float32),
+                logits=z((n, layer.n_experts), torch.float32) if layer.router is not None else None)
 
 
 def ffn_decode(layer: Layer, x: torch.Tensor, routing: Routing, residual: torch.Tensor,
@@ -235,11 +246,12 @@ def ffn_decode(layer: Layer, x: torch.Tensor, routing: Routing, residual: torch.
         raise MoeError(fn, rc)
 
 
-def layer_decode(layer: Layer, logits: torch.Tensor, x: torch.Tensor, residual: torch.Tensor,
-                 routing: Routing | None = None, ws: torch.Tensor | None = None,
-                 debug: dict | None = None, stream=None, stages: int | None = None) -> Routing:
-    """moe_layer_decode: route `logits` and run the decode expert FFN (residual in place).
-    Returns the routing it wrote."""
+def layer_decode(layer: Layer, logits: torch.Tensor | None, x: torch.Tensor,
+                 residual: torch.Tensor, routing: Routing | None = None,
+                 ws: torch.Tensor | None = None, debug: dict | None = None, stream=None,
+                 stages: int | None = None) -> Routing:
+    """moe_layer_decode: route `logits` (None: the layer's router projects them from x) and
+    run the decode expert FFN (residual in place). Returns the routing it wrote."""
     n = x.shape[0]
     if routing is None:
         routing = Routing.empty(n, layer.n_experts, layer.top_k, x.device)

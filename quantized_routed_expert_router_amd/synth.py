@@ -35,6 +35,7 @@ LIB = os.path.join(PKG_DIR, "libqmoe_synth.so")
 # tensor ids of the counter-based streams
 T_GATE, T_UP, T_DOWN, T_X, T_LOGITS, T_PERM = 1, 2, 3, 4, 5, 6
 T_SHARED_GATE, T_SHARED_UP, T_SHARED_DOWN = 7, 8, 9  # the always-active shared expert
+T_ROUTER = 10  # router weights
 
 SIGMA_W = 0.02
 ZIPF_S = 1.1
@@ -193,7 +194,19 @@ class Workload:
     extra: dict = field(default_factory=dict)
 
 
-def config(cfg: int, T: int = 4) -> Workload:
+def config(cfg: int, T: int = 4, experts: int | None = None) -> Workload:
+    """Workload `cfg`; `experts` replaces the expert count of configurations 2-5 (256: the
+    pruned "Coder" model, 256 of every layer's 512 experts kept, still 10 active)."""
+    w = _config(cfg, T)
+    if experts is not None and experts != w.E:
+        if cfg == 1:
+            raise ValueError("the expert count of configuration 1 is fixed")
+        w.name = w.name.replace(f"_e{w.E}_", f"_e{experts}_")
+        w.E = experts
+    return w
+
+
+def _config(cfg: int, T: int) -> Workload:
     if cfg == 1:
         return Workload("tiny_d256_f128_e8_top2_t1", 256, 128, 8, 2, 1, 4, "normal")
     if cfg == 2:
@@ -235,6 +248,12 @@ def host_shared(w: Workload, layer: int, nthreads: int = 0):
     dn = fill_matrix_host(empty_matrix(1, w.d, w.f, w.bits), w.seed, layer, T_SHARED_DOWN,
                           nthreads=nthreads)
     return g, u, dn
+
+
+def host_router(w: Workload, layer: int) -> np.ndarray:
+    """Router weights of the layer: bf16 bits [E][d] of N(0, 1/d) values, so that the
+    logits of N(0, 1) inputs are about N(0, 1)."""
+    return to_bf16_bits(normal(w.seed, T_ROUTER, layer, (w.E, w.d), sigma=1.0 / math.sqrt(w.d)))
 
 
 def layer_inputs(w: Workload, layer: int):

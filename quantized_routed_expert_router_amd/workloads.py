@@ -26,13 +26,21 @@ def device_matrix(w: synth.Workload, layer: int, tensor: int, rows: int, cols: i
     return qmoe.QMatrix(codes, sm, rows, cols, w.bits)
 
 
-def device_layer(w: synth.Workload, layer: int, device="cuda", shared: bool = False) -> qmoe.Layer:
-    """All E experts of one layer instance generated on the GPU (and its shared expert)."""
+def device_router(w: synth.Workload, layer: int, device="cuda") -> torch.Tensor:
+    """The layer's router weights (bf16 bits [E][d], int16 storage) in device memory."""
+    return torch.from_numpy(synth.host_router(w, layer).view(np.int16)).to(device)
+
+
+def device_layer(w: synth.Workload, layer: int, device="cuda", shared: bool = False,
+                 router: bool = False) -> qmoe.Layer:
+    """All E experts of one layer instance generated on the GPU (and optionally its shared
+    expert and router weights)."""
     return qmoe.Layer(w.d, w.f, w.E, w.k,
                       device_matrix(w, layer, synth.T_GATE, w.f, w.d, device),
                       device_matrix(w, layer, synth.T_UP, w.f, w.d, device),
                       device_matrix(w, layer, synth.T_DOWN, w.d, w.f, device),
-                      device_shared(w, layer, device) if shared else None)
+                      device_shared(w, layer, device) if shared else None,
+                      device_router(w, layer, device) if router else None)
 
 
 def device_shared(w: synth.Workload, layer: int, device="cuda"):

@@ -232,3 +232,24 @@ def test_shared_expert_argument_checks():
     assert b >= a + 4 * (768 + 8 * 2048)
     need = b
     assert _decode(_with_shared(_layer(d=2048, f=768, E=512, k=10)), ws_bytes=need - 1) == WS_SMALL
+
+
+def test_router_argument_checks():
+    r = _routing()
+    call = lambda L, logits=None, n=4: qmoe.lib.moe_layer_decode(  # noqa: E731
+        ctypes.byref(L), logits, FAKE + 0x600000, n, ctypes.byref(r), FAKE + 0x700000,
+        FAKE + 0x800000, 1 << 30, None, None)
+    assert call(_layer()) == INVALID                        # no logits and no router rows
+    L = _layer()
+    L.router_w = FAKE + 0x30000008                          # router rows not 16-byte aligned
+    assert call(L, FAKE + 0x900000) == INVALID
+    # the workspace holds the projected logits
+    base = _layer(d=2048, f=768, E=512, k=10)
+    withr = _layer(d=2048, f=768, E=512, k=10)
+    withr.router_w = FAKE + 0x30000000
+    a = qmoe.lib.moe_ffn_workspace_bytes(ctypes.byref(base), 4, 0)
+    b = qmoe.lib.moe_ffn_workspace_bytes(ctypes.byref(withr), 4, 0)
+    assert b >= a + 4 * 512 * 4
+    assert qmoe.lib.moe_layer_decode(ctypes.byref(withr), None, FAKE + 0x600000, 4,
+                                     ctypes.byref(r), FAKE + 0x700000, FAKE + 0x1000000, b - 1,
+                                     None, None) == WS_SMALL

@@ -270,6 +270,21 @@ def test_decode_max_tokens_sampled(cfg2_layer):
     assert_output_tolerance(out[tokens] - x[tokens], out_o - x[tokens], what="moe delta")
 
 
+@pytest.mark.parametrize("bits,T", [(4, 4), (2, 4), (4, 1)])
+def test_decode_pruned_256_experts(bits, T):
+    # the pruned model: 256 experts per layer, still top-10, at the full layer shape
+    w = synth.config(2, experts=256)
+    w = synth.Workload(w.name, w.d, w.f, w.E, w.k, T, bits, w.logits)
+    layer = workloads.device_layer(w, 3)
+    lg, x = synth.layer_inputs(w, 3)
+    ids, _ = O.route(lg, w.k)
+    experts = np.unique(ids)
+    host = synth.host_layer(w, 3, experts=experts)
+    device_layer_matches_host(layer, host, experts[::5], w.E)
+    _decode_parity(w, host, lg, x, layer=layer, dots=(bits == 4 and T == 4))
+    out, _ = _layer_vs_two_calls(w, layer, lg, x)
+
+
 @pytest.mark.parametrize("T", [1, 4])
 def test_decode_config3_2bit_batched(T):
     w = synth.config(3, T)
