@@ -158,6 +158,17 @@ def test_decode_small_shapes(E, d, f, k, n, bits):
     _decode_parity(w, host, lg, x, residual=res)
 
 
+@pytest.mark.parametrize("E,d,f,k,n,bits,dots", [
+    (2, 8192, 8192, 1, 2, 4, False),  # the largest d and f: several gate/up groups, f > 1024
+                                      # takes the expert-major down and the combine launch
+    (3, 8192, 1024, 2, 3, 2, True),   # the largest f of the token-major down, largest d
+    (3, 512, 1056, 2, 2, 4, True),    # one block past it: expert-major down
+])
+def test_decode_largest_dimensions(E, d, f, k, n, bits, dots):
+    w, host, lg, x = _small(E, d, f, k, n, bits, seed=11)
+    _decode_parity(w, host, lg, x, dots=dots)
+
+
 def test_decode_x_aliases_residual():
     w, host, lg, x = _small(8, 128, 64, 2, 3, 4, seed=2)
     layer = workloads.layer_from_host(*host, w.k)

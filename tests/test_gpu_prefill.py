@@ -69,6 +69,14 @@ def test_prefill_small_shapes(E, d, f, k, n, bits):
     _small_parity(E, d, f, k, n, bits)
 
 
+@pytest.mark.parametrize("E,d,f,k,n,bits", [
+    (2, 8192, 8192, 1, 2, 4),    # the largest d and f
+    (3, 8192, 512, 2, 100, 2),   # the largest d over a ragged chunk
+])
+def test_prefill_largest_dimensions(E, d, f, k, n, bits):
+    _small_parity(E, d, f, k, n, bits, seed=12)
+
+
 def test_prefill_skewed_routing():
     # one expert takes most of the pairs (Zipf-biased logits, few experts)
     _small_parity(12, 256, 128, 3, 1000, 4, logits="zipf", seed=3)
