@@ -1,31 +1,38 @@
-// Decode-window expert FFN: the hot path of the routed-expert layer for T <= 5 tokens.
+// Decode-window expert FFN: the hot path of the routed-expert layer for small batches
+// (the T <= 5 verify window of speculative decoding, and batches of windows).
 //
 // The pages' engine computes cached experts for the whole verify window in one grouped
 // kernel (Strata engine explainer, m.lqnn.cn/news/264700, section "Expert cache") and
 // its CPU kernels quantize each activation vector to int8 once and reuse it over many
-// weight rows with 4-wide int8 dot products (section "CPU expert pool"). Here:
+// weight rows with 4-wide int8 dot products (section "CPU expert pool"). Kernels here:
 //
-//   k_prep      one lane per (token, 32-block): int8 block quantization of x, stored in
-//               a byte order matched to the packed weight nibbles; block 0 of the grid
-//               turns the expert offsets into a work list of (expert, pair range) chunks.
-//   k_gateup    one lane per weight row, 64 rows per wavefront, the four waves of a
-//               workgroup split the reduction blocks. Each lane streams its row's packed
-//               codes (16 B per block at 4 bits: one block column of 64 rows is 1 KB
-//               contiguous) and scale/min words, and forms exact int32 block dots with
-//               v_dot4 against activation words that are wave-uniform (scalar loads).
-//               Block terms (scale*xs)*dot and min*(xs*sum) are exact in binary64, so the
-//               row sums round only in the additions. The workgroup then applies SwiGLU
-//               and quantizes h per 32 rows (two halves of a wave) to int8.
-//   k_down      the same streaming scheme over the down projection's d rows.
-//   k_combine   residual[t] += sum_j w[t][j] * y[t*k+j] in slot order, binary64. It stays a
-//               launch of its own: folding it into k_down through a last-arriver counter
-//               needs the pair outputs to cross XCDs, either through device-scope fences
-//               (an L2 writeback per workgroup) or through write-through stores and loads,
-//               and both put a chain of memory round trips on the last workgroup that costs
-//               more than this small launch.
+//   k_router_logits  (optional) logits = x . W_r^T from bf16 router rows, binary64 sums.
+//   k_route_prep     top-k routing of up to 64 tokens by one workgroup (one wave per
+//                    token), fused with the int8 block quantization of x by the other
+//                    workgroups; for larger windows it also groups the pairs and builds
+//                    the work list. k_prep does the quantization and the work list after
+//                    a separate routing call.
+//   k_gateup         one workgroup per (chunk of pairs of one expert, 32 rows of f): the
+//                    gate and up rows of the item stream through raw buffer loads (all
+//                    blocks of a lane at once), exact int32 block dots with v_dot4 against
+//                    activation codes staged in LDS, binary64 block terms, then SwiGLU and
+//                    the int8 quantization of the item's 32-row block of h. For small
+//                    windows the chunks come straight from the expert ids and workgroup 0
+//                    writes the routing's grouping.
+//   k_down_tok       small windows: the down projection by token, with the routing-
+//                    weighted combine into the residual folded in (no pair outputs leave
+//                    the workgroup).
+//   k_down, k_combine  larger windows: the down projection by expert chunk, then the
+//                    slot-order combine in a launch of its own. Folding the combine into
+//                    k_down through a last-arriver counter needs the pair outputs to cross
+//                    XCDs, through device-scope fences (an L2 writeback per workgroup) or
+//                    write-through stores and loads, and both put a chain of memory round
+//                    trips on the last workgroup that costs more than this small launch.
 //
-// Every expert's weights are read once per chunk of up to NPC pairs; at n <= NPC tokens
-// (the T = 4 window) every touched expert is read exactly once per call.
+// Block terms (scale*xs)*dot and min*(xs*sum) are exact in binary64, so row sums round
+// only in the additions. Every expert's weights are read once per chunk of up to NPC
+// pairs; at n <= NPC tokens (the T = 4 window) every touched expert is read exactly once
+// per call.
 #include <algorithm>
 
 #include "qmoe_route_dev.h"

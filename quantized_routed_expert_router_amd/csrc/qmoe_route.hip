@@ -6,13 +6,14 @@
 // handshake" section, and grouping by expert feeds a grouped expert kernel ("Expert
 // cache" section).
 //
-// One wavefront selects for one token: lane l holds the logits of experts l, l+64, ...
-// as 64-bit keys (order-preserving bits of the logit, then the complement of the expert
-// id so that equal logits favour the lower id); k rounds of a wave max-reduction pick
-// the slots in order. Weights are computed in binary64 and summed in slot order.
-// Grouping is a stable counting sort done by one workgroup: per-wave histograms in LDS,
-// a scan, and an in-order scatter where lanes holding the same expert are ranked with
-// ballots over the bits of the expert id.
+// One wavefront selects for one token (wave_topk): lane l holds the logits of experts
+// l, l+64, ... as order-preserving bits; a threshold found bit by bit with ballots leaves
+// the candidates, which are ranked by (logit desc, id asc) from registers. Weights are
+// computed in binary64 and summed in slot order. Grouping is a stable counting sort: by
+// one workgroup up to 4096 pairs (per-wave histograms in LDS, a scan, and an in-order
+// scatter where lanes holding the same expert are ranked with ballots over the bits of
+// the expert id), and beyond that by many workgroups over chunks of 2048 pairs, each
+// writing an expert histogram to the workspace.
 #include "qmoe_route_dev.h"
 
 namespace qmoe {
