@@ -114,3 +114,48 @@ def test_router_full_layer_shape(E, T):
     x = synth.activations(0, 40 + T, T, w.d)
     same = _run(w, layer, x, layer_id=5)
     assert same >= 0.99  # equal to the bit nearly always
+
+
+def test_router_with_shared_expert():
+    # both optional parts at once: logits projected from x, then the routed experts and the
+    # shared expert (weight 1, after the routed slots)
+    w = synth.Workload("router_shared", 256, 128, 32, 4, 3, 4, "normal", seed=14)
+    host = synth.host_layer(w, 0)
+    sh = synth.host_shared(w, 0)
+    layer = workloads.layer_from_host(*host, w.k, shared=sh)
+    layer.router = workloads.device_router(w, 0)
+    x = synth.activations(14, 0, w.n, w.d)
+    x_d = to_dev(x)
+    dbg = qmoe.debug_buffers(layer, w.n)
+    res = x_d.clone()
+    r = qmoe.layer_decode(layer, None, x_d, res, debug=dbg)
+    torch.cuda.synchronize()
+    lg_gpu = dbg["logits"].cpu().numpy()
+    _check_logits(lg_gpu, O.router_logits(layer.router.cpu().numpy().view(np.uint16), x))
+    ids, wt = check_routing(lg_gpu, w.k, r)
+    out_o, _ = O.ffn_decode(*(omat(h) for h in host), w.E, x, ids, wt, x,
+                            shared=tuple(omat(h) for h in sh))
+    assert_output_tolerance(res.cpu().numpy(), out_o)
+    assert_output_tolerance(res.cpu().numpy() - x, out_o - x, what="moe delta")
+
+
+def test_router_layer_in_graph_replays():
+    # the projecting layer captured in a HIP graph: every replay equals the eager call
+    w, host, layer, x = _small_layer(64, 256, 128, 6, 4, 4, seed=15)
+    x_d = to_dev(x)
+    ws = qmoe.workspace(layer, w.n)
+    r = qmoe.Routing.empty(w.n, w.E, w.k)
+    ref = x_d.clone()
+    qmoe.layer_decode(layer, None, x_d, ref, routing=r, ws=ws)
+    torch.cuda.synchronize()
+    res = x_d.clone()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        qmoe.layer_decode(layer, None, x_d, res, routing=r, ws=ws)
+    for _ in range(3):
+        res.copy_(x_d)
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(res, ref)
