@@ -163,6 +163,8 @@ def test_decode_small_shapes(E, d, f, k, n, bits):
                                       # takes the expert-major down and the combine launch
     (3, 8192, 1024, 2, 3, 2, True),   # the largest f of the token-major down, largest d
     (3, 512, 1056, 2, 2, 4, True),    # one block past it: expert-major down
+    (64, 256, 768, 12, 3, 4, True),   # 6 slot registers a lane half: the 18-block instance
+    (64, 256, 768, 13, 3, 2, True),   # 7: past the token-major limit, expert-major down
 ])
 def test_decode_largest_dimensions(E, d, f, k, n, bits, dots):
     w, host, lg, x = _small(E, d, f, k, n, bits, seed=11)
