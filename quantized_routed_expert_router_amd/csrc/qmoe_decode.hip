@@ -12,16 +12,18 @@
 //                    workgroups; for larger windows it also groups the pairs and builds
 //                    the work list. k_prep does the quantization and the work list after
 //                    a separate routing call.
-//   k_gateup         one workgroup per (chunk of pairs of one expert, 32 rows of f): the
-//                    gate and up rows of the item stream through raw buffer loads (all
-//                    blocks of a lane at once), exact int32 block dots with v_dot4 against
-//                    activation codes staged in LDS, binary64 block terms, then SwiGLU and
-//                    the int8 quantization of the item's 32-row block of h. For small
-//                    windows the chunks come straight from the expert ids and workgroup 0
-//                    writes the routing's grouping.
-//   k_down_tok       small windows: the down projection by token, with the routing-
-//                    weighted combine into the residual folded in (no pair outputs leave
-//                    the workgroup).
+//   k_gateup         one workgroup per (chunk of pairs of one expert, 16 or 32 rows of
+//                    f): the gate and up rows of the item stream through raw buffer loads
+//                    (all blocks of a lane at once), exact int32 block dots with v_dot4
+//                    against activation codes staged in LDS, binary64 block terms, then
+//                    SwiGLU; 32-row items also quantize their block of h to int8, 16-row
+//                    items (small windows) leave h in fp32. For small windows the chunks
+//                    come straight from the expert ids and workgroup 0 writes the
+//                    routing's grouping.
+//   k_down_tok       small windows: the int8 quantization of the token's h, the down
+//                    projection by token, and the routing-weighted combine into the
+//                    residual (no pair outputs leave the workgroup).
+//   k_hquant         the h quantization alone, when a small window's down runs by expert.
 //   k_down, k_combine  larger windows: the down projection by expert chunk, then the
 //                    slot-order combine in a launch of its own. Folding the combine into
 //                    k_down through a last-arriver counter needs the pair outputs to cross
@@ -407,31 +409,40 @@ __device__ __forceinline__ int quant_half_wave(float h, float& scale, int& sum) 
 
 // ---------------------------------------------------------------- gate/up + SwiGLU + h quant
 
-// A workgroup of WAVES waves takes one item = (chunk of pairs of one expert, 32 rows of f):
-// exactly one 32-row block of h, so the int8 quantization of h closes inside the
-// workgroup. The first half of the waves streams the gate matrix and the second half the
-// up matrix. The reduction axis is cut into WAVES parts, two a wave: lane l of wave w owns
-// row l%32 and part ke = 2*(w % (WAVES/2)) + l/32, and reads blocks ke, ke+WAVES, ... in
-// groups of 64 blocks (kUnroll = 64/WAVES a lane). All loads of a group are issued at once
-// (the whole reduction axis at d = 2048), so every weight byte of the item is in flight
-// after one memory latency, and the dots of a block start as soon as that block lands. The
-// chunk's activation codes and scales are staged in LDS per group and read back with
+// A workgroup of WAVES waves takes one item = (chunk of pairs of one expert, ROWS rows of
+// f). The first half of the waves streams the gate matrix and the second half the up
+// matrix. The reduction axis is cut into parts, 64/ROWS a wave: lane l of wave w owns row
+// l%ROWS and part ke = (64/ROWS)*(w % (WAVES/2)) + l/ROWS, and reads blocks ke, ke+kSplit,
+// ... in groups of 64 blocks. All loads of a group are issued at once (the whole reduction
+// axis at d = 2048), so every weight byte of the item is in flight after one memory
+// latency, and the dots of a block start as soon as that block lands. The chunk's
+// activation codes and scales are staged in LDS per group and read back with
 // half-wave-uniform addresses.
 //
-// Eight waves (two workgroups a CU, 16 waves) serve the decode window, whose 500-odd items
-// fit one round of workgroups; four waves (three workgroups a CU, 12 waves, twice the
-// loads in flight a lane) serve the batched path, whose thousands of items run in many
-// rounds: the gate/up launch measured 4-8% faster there and 6% slower on the window.
-constexpr int kGuRows = 32;   // rows of f per item
+// Two shapes:
+// * ROWS = 16, 4 waves (the decode window, ahead of the token-major down): 40 KB of
+//   weights an item, five workgroups a CU, so the ~1000 items of a T=4 window run in one
+//   round; the 16 rows are half of an h block, so h leaves in fp32 and the down kernel
+//   quantizes it. (Reading the same bytes as 1056 workgroups of 40 KB instead of 528 of
+//   80 KB measured 10% faster in a plain read probe.)
+// * ROWS = 32 (the work-list path and the expert-major down): one item is exactly one
+//   32-row block of h, so the int8 quantization of h closes inside the workgroup. Four
+//   waves (three workgroups a CU, 16 blocks a lane) serve the batched work list, whose
+//   thousands of items run in many rounds: 4-8% faster there than eight waves.
+constexpr int kGuRows = 32;   // rows of an h block
 constexpr int kGuGroup = 64;  // blocks per group
-template <int WAVES>
+template <int WAVES, int ROWS>
 struct GuShape {
   static constexpr int kThreads = WAVES * kWave;
-  static constexpr int kKWaves = WAVES / 2;             // waves per matrix
-  static constexpr int kSplit = WAVES;                  // reduction-axis parts
-  static constexpr int kUnroll = kGuGroup / WAVES;      // blocks per lane per group
-  static constexpr int kWavesPerEu = WAVES == 8 ? 4 : 3;  // the register budget
+  static constexpr int kKWaves = WAVES / 2;          // waves per matrix
+  static constexpr int kPW = kWave / ROWS;           // reduction-axis parts a wave
+  static constexpr int kSplit = kKWaves * kPW;       // reduction-axis parts
+  static constexpr int kUnroll = kGuGroup / kSplit;  // blocks per lane per group
 };
+// register budget (waves a SIMD): five 16-row workgroups a CU where the registers allow
+constexpr int gu_waves_per_eu(int waves, int rows, int npc, bool dbg) {
+  return rows == 16 ? (npc <= 4 && !dbg ? 5 : 4) : waves == 8 ? 4 : 3;
+}
 
 // Activation staging straight into LDS with global_load_lds_dwordx4: each wave-level load
 // writes 64 consecutive 16-byte entries of s_act[j][bb][part] (part 0/1: the two halves of
@@ -553,9 +564,9 @@ __device__ __forceinline__ IdsChunk<NPC> chunk_from_ids(const int32_t* __restric
   return ch;
 }
 
-template <int BITS, int NPC, int WAVES, bool DBG, bool IDS>
-__global__ __launch_bounds__(GuShape<WAVES>::kThreads) __attribute__((
-    amdgpu_waves_per_eu(GuShape<WAVES>::kWavesPerEu))) void k_gateup(
+template <int BITS, int NPC, int WAVES, int ROWS, bool DBG, bool IDS>
+__global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
+    amdgpu_waves_per_eu(gu_waves_per_eu(WAVES, ROWS, NPC, DBG)))) void k_gateup(
     const uint32_t* __restrict__ gcodes, const uint32_t* __restrict__ gsm,
     const uint32_t* __restrict__ ucodes, const uint32_t* __restrict__ usm, int d, int f,
     const int* __restrict__ chunks, const int* __restrict__ nchunks, const int8_t* __restrict__ xq,
@@ -563,20 +574,21 @@ __global__ __launch_bounds__(GuShape<WAVES>::kThreads) __attribute__((
     const int32_t* __restrict__ topk_ids, int k, int P, int E, int32_t* __restrict__ offsets,
     int32_t* __restrict__ pair_index, const uint32_t* __restrict__ sgcodes,
     const uint32_t* __restrict__ sgsm, const uint32_t* __restrict__ sucodes,
-    const uint32_t* __restrict__ susm, int n, DecodeDebug dbg) {
-  using S = GuShape<WAVES>;
-  __shared__ double red[WAVES][NPC][kGuRows];
+    const uint32_t* __restrict__ susm, int n, float* __restrict__ hf, DecodeDebug dbg) {
+  using S = GuShape<WAVES, ROWS>;
+  static_assert(ROWS == 16 || ROWS == 32, "item rows");
+  __shared__ double red[WAVES][NPC][ROWS];
   __shared__ int4 s_act_raw[ActLds<NPC, kGuGroup, S::kThreads>::kPadded];
   __shared__ uint32_t s_bits[kExpertWords];
   int4 (*s_act)[kGuGroup][3] = reinterpret_cast<int4 (*)[kGuGroup][3]>(s_act_raw);
   const int nbd = d / 32, nbf = f / 32;
-  const int ntiles = f / kGuRows;
+  const int ntiles = f / ROWS;
   const int tid = threadIdx.x;
   const int lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int mat = wave / S::kKWaves;  // 0: gate, 1: up
-  const int ke = 2 * (wave % S::kKWaves) + lane / kGuRows;  // reduction-axis part
-  const int rl = lane % kGuRows;
+  const int ke = S::kPW * (wave % S::kKWaves) + lane / ROWS;  // reduction-axis part
+  const int rl = lane % ROWS;
   // One item per workgroup: the grid covers the largest possible item count and the
   // workgroups past the live count exit. (A loop over items would make the compiler's wait
   // counts conservative at its head: the first weight requests would wait for the
@@ -657,7 +669,7 @@ __global__ __launch_bounds__(GuShape<WAVES>::kThreads) __attribute__((
   const int nitems = nch * ntiles;
   if (item < nitems) {
     const int tile = item % ntiles;
-    const int r = tile * kGuRows + rl;
+    const int r = tile * ROWS + rl;
     double acc[NPC];
 #pragma unroll
     for (int j = 0; j < NPC; ++j) acc[j] = 0.0;
@@ -722,21 +734,53 @@ __global__ __launch_bounds__(GuShape<WAVES>::kThreads) __attribute__((
         asm volatile("" ::"v"(smw[u]));
       }
     }
-    // the two reduction halves of a row sit in lanes l and l+32
+    // the reduction parts of a row sit in lanes l, l+ROWS, ... (every lane of the row ends
+    // with the same sum: fp addition commutes)
 #pragma unroll
     for (int j = 0; j < NPC; ++j) {
-      const double o = __shfl_xor(acc[j], kGuRows);
-      acc[j] = lane < kGuRows ? acc[j] + o : o + acc[j];
+#pragma unroll
+      for (int m = ROWS; m < kWave; m *= 2) {
+        const double o = __shfl_xor(acc[j], m);
+        acc[j] = (lane & m) ? o + acc[j] : acc[j] + o;
+      }
     }
-    if (lane < kGuRows) {
+    if (lane < ROWS) {
 #pragma unroll
       for (int j = 0; j < NPC; ++j)
         if (j < np) red[wave][j][rl] = acc[j];
     }
     __syncthreads();
-    if (wave == 0) {
+    if (ROWS == 16 && wave == 0) {
+      // lane l takes pair slots l/16, l/16 + 4, ... at row l%16; h leaves in fp32
+      const int js = lane / ROWS;
+#pragma unroll
+      for (int jj = 0; jj < (NPC + S::kPW - 1) / S::kPW; ++jj) {
+        const int j = S::kPW * jj + js;
+        if (j < np) {
+          // sums over the waves of each matrix, in wave order
+          double g = red[0][j][rl], u = red[S::kKWaves][j][rl];
+#pragma unroll
+          for (int w2 = 1; w2 < S::kKWaves; ++w2) {
+            g += red[w2][j][rl];
+            u += red[S::kKWaves + w2][j][rl];
+          }
+          const double silu = g / (1.0 + exp(-g));
+          const float h = (float)(silu * u);
+          int pj = pid[0];
+#pragma unroll
+          for (int j2 = 1; j2 < NPC; ++j2) pj = j == j2 ? pid[j2] : pj;
+          hf[(size_t)pj * f + r] = h;
+          if (DBG) {
+            if (dbg.g) dbg.g[(size_t)pj * f + r] = (float)g;
+            if (dbg.u) dbg.u[(size_t)pj * f + r] = (float)u;
+            if (dbg.h) dbg.h[(size_t)pj * f + r] = h;
+          }
+        }
+      }
+    }
+    if (ROWS == 32 && wave == 0) {
       // lanes 0..31 take even pair slots, lanes 32..63 odd ones; each half quantizes the
-      // 32 rows of its pair
+      // 32 rows of its pair (and with hf given also stores h in fp32)
       const int hh = lane / kGuRows;
 #pragma unroll
       for (int jj = 0; jj < (NPC + 1) / 2; ++jj) {
@@ -759,6 +803,7 @@ __global__ __launch_bounds__(GuShape<WAVES>::kThreads) __attribute__((
 #pragma unroll
           for (int j2 = 1; j2 < NPC; ++j2) pj = j == j2 ? pid[j2] : pj;
           hq[(size_t)pj * f + 32 * tile + act_byte_pos<BITS>(rl)] = (int8_t)q;
+          if (hf) hf[(size_t)pj * f + r] = h;
           if (rl == 0) hsc[(size_t)pj * nbf + tile] = make_double2((double)scale, (double)scale * qsum);
           if (DBG) {
             if (dbg.g) dbg.g[(size_t)pj * f + r] = (float)g;
@@ -911,10 +956,12 @@ __global__ __launch_bounds__(kThreads) void k_combine(const double* __restrict__
 // the token, for blocks w, w+8, ... of f.
 //
 // Order of requests: the experts of the lane's pairs, the token's residual values and its
-// h codes and scales go out first; then all U*I weight blocks of the lane (the whole token
-// at f = 768, k = 10), then the routing weights (scalar loads, needed only at the end). The wave waits only for the h loads
-// before writing them to LDS and meeting the barrier, and each block's dots start as
-// soon as that block has landed. The 8 waves' partial sums meet in LDS.
+// h (fp32) go out first; then all U*I weight blocks of the lane (the whole token at
+// f = 768, k = 10), then the routing weights (scalar loads, needed only at the end). The
+// wave waits only for the h loads, quantizes h block by block into LDS (every workgroup
+// of the token does this for itself, while its weights are in flight) and meets the
+// barrier; each block's dots start as soon as that block has landed. The 8 waves' partial
+// sums meet in LDS.
 constexpr int kDtRows = 32;
 constexpr int kDtWaves = 8;
 constexpr int kDtThreads = kDtWaves * kWave;
@@ -930,8 +977,8 @@ template <int BITS, int U, int I, bool SH, bool DBG>
 __global__ __launch_bounds__(kDtThreads) void k_down_tok(
     const uint32_t* __restrict__ dcodes, const uint32_t* __restrict__ dsm, int d, int f, int k,
     int n, const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w,
-    const int8_t* __restrict__ hq, const double2* __restrict__ hsc, float* residual,
-    const uint32_t* __restrict__ sdcodes, const uint32_t* __restrict__ sdsm, DecodeDebug dbg) {
+    const float* __restrict__ hf, float* residual, const uint32_t* __restrict__ sdcodes,
+    const uint32_t* __restrict__ sdsm, DecodeDebug dbg) {
   // slots j < k: the routed pairs t*k + j; with SH, slot k: the shared expert, pair n*k + t,
   // weight 1. I slots per lane half (lane half h takes j = h, h+2, ...). Without SH every
   // shared-slot select folds away.
@@ -962,23 +1009,20 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
   const bool epi = wave == 0 && lane < kDtRows;
   const float res0 = residual[(size_t)t * d + (epi ? row : rt * kDtRows)];
 
-  // h of the token into registers: entry (j, b) = 32 code bytes, then (scale, scale*sum);
-  // entries past the end repeat the last one. They are written to LDS after the weight
-  // requests, so the compiler's own wait for them leaves the weight loads in flight.
-  typedef int v4i __attribute__((ext_vector_type(4)));
-  v4i stg[kDtStage / kDtThreads];
+  // h of the token in fp32 into registers: thread q takes block q of the token's ke*nbf
+  // (<= 512) blocks, slot j = q / nbf and rows 32b .. 32b+31 with b = q % nbf; threads past
+  // the end read the last block again, never used. The block is quantized after the
+  // weight requests, so the compiler's own wait for it leaves the weight loads in flight.
+  const int nblk = ke * nbf;
+  typedef float v4f __attribute__((ext_vector_type(4)));
+  v4f hv[8];
   {
-    const int total = ke * nbf * 3;
+    const int q = min(tid, nblk - 1);
+    const int j = q / nbf, b = q - j * nbf;
+    const uintptr_t src = reinterpret_cast<uintptr_t>(hf + pair_of(j) * f + 32 * b);
 #pragma unroll
-    for (int it = 0; it < kDtStage / kDtThreads; ++it) {
-      const int idx = min(it * kDtThreads + tid, total - 1);
-      const int jb = idx / 3, part = idx % 3;
-      const int j = jb / nbf, b = jb % nbf;
-      const size_t p = pair_of(j);
-      const uintptr_t src = part < 2 ? reinterpret_cast<uintptr_t>(hq + p * f + 32 * b + 16 * part)
-                                     : reinterpret_cast<uintptr_t>(hsc + p * nbf + b);
-      stg[it] = *reinterpret_cast<const __attribute__((address_space(1))) v4i*>(src);
-    }
+    for (int i = 0; i < 8; ++i)
+      hv[i] = reinterpret_cast<const __attribute__((address_space(1))) v4f*>(src)[i];
   }
   __builtin_amdgcn_sched_barrier(0);
 
@@ -1014,9 +1058,42 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
   for (int j = 0; j < kDtMaxK; ++j)
     sw[j] = __int_as_float(
         load_uniform(reinterpret_cast<const int*>(topk_w) + (size_t)t * k + min(j, k - 1)));
+  // int8 quantization of the thread's block (the arithmetic of the gate/up epilogue of
+  // 32-row items, in registers): LDS entry q = the 32 codes at their dot4 byte positions,
+  // then (scale, scale*sum). Entries past ke*nbf stay unwritten; the blocks that would read
+  // them are dropped below. (Every workgroup of the token quantizes all of its blocks.)
+  if (tid < nblk) {
+    float v[32];
 #pragma unroll
-  for (int it = 0; it < kDtStage / kDtThreads; ++it)
-    reinterpret_cast<v4i*>(s_act)[it * kDtThreads + tid] = stg[it];
+    for (int i = 0; i < 8; ++i) {
+      v[4 * i] = hv[i].x;
+      v[4 * i + 1] = hv[i].y;
+      v[4 * i + 2] = hv[i].z;
+      v[4 * i + 3] = hv[i].w;
+    }
+    int qc[32];
+    const float scale = quant_block32(v, qc);
+    int sum = 0;
+    uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+    for (int i = 0; i < 32; ++i) {
+      sum += qc[i];
+      const int pos = act_byte_pos<BITS>(i);
+      words[pos / 4] |= ((uint32_t)qc[i] & 0xffu) << (8 * (pos % 4));
+    }
+    s_act[3 * tid] = make_int4((int)words[0], (int)words[1], (int)words[2], (int)words[3]);
+    s_act[3 * tid + 1] = make_int4((int)words[4], (int)words[5], (int)words[6], (int)words[7]);
+    reinterpret_cast<double2*>(s_act)[3 * tid + 2] =
+        make_double2((double)scale, (double)scale * (double)sum);
+    if (DBG && rt == 0) {  // one workgroup per token reports the codes
+      const int j = tid / nbf, b = tid - j * nbf;
+      if (dbg.hq) {
+#pragma unroll
+        for (int i = 0; i < 32; ++i) dbg.hq[pair_of(j) * f + 32 * b + i] = (int8_t)qc[i];
+      }
+      if (dbg.hs) dbg.hs[pair_of(j) * nbf + b] = scale;
+    }
+  }
   __syncthreads();
 
   // Every block is computed and the unused ones (past ke or nbf) are dropped by a select:
@@ -1063,11 +1140,33 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
   }
 }
 
+// h quantization for the expert-major down after 16-row gate/up items (which leave h in
+// fp32 only): one half-wave per (pair, 32-row block), the arithmetic of the gate/up
+// epilogue.
+constexpr int kHqThreads = 256;
+template <int BITS, bool DBG>
+__global__ __launch_bounds__(kHqThreads) void k_hquant(const float* __restrict__ hf, int Q, int f,
+                                                       int8_t* __restrict__ hq,
+                                                       double2* __restrict__ hsc, DecodeDebug dbg) {
+  const int nbf = f / 32;
+  const int blk = (blockIdx.x * kHqThreads + (int)threadIdx.x) / 32, hl = threadIdx.x % 32;
+  if (blk >= Q * nbf) return;  // whole half-waves leave together
+  const int p = blk / nbf, b = blk - p * nbf;
+  float scale;
+  int qsum;
+  const int c = quant_half_wave(hf[(size_t)p * f + 32 * b + hl], scale, qsum);
+  hq[(size_t)p * f + 32 * b + act_byte_pos<BITS>(hl)] = (int8_t)c;
+  if (hl == 0) hsc[(size_t)p * nbf + b] = make_double2((double)scale, (double)scale * qsum);
+  if (DBG) {
+    if (dbg.hq) dbg.hq[(size_t)p * f + 32 * b + hl] = (int8_t)c;
+    if (dbg.hs && hl == 0) dbg.hs[(size_t)p * nbf + b] = scale;
+  }
+}
+
 // Slots per lane half: kDtSlots / U weight blocks in flight per lane, or kDtSlotsShared / U
 // when the window needs one more slot than that (a shared expert).
 template <int BITS, int U, bool DBG>
-hipError_t launch_down_tok_u(const DecodeArgs& a, const int8_t* hq, const double2* hsc,
-                             const DecodeDebug& dbg) {
+hipError_t launch_down_tok_u(const DecodeArgs& a, const float* hf, const DecodeDebug& dbg) {
   const moe_layer& L = *a.L;
   const int d = L.d_model, f = L.d_ff, k = L.top_k, n = a.n;
   const int per = (d / kDtRows + 7) / 8;
@@ -1082,18 +1181,17 @@ hipError_t launch_down_tok_u(const DecodeArgs& a, const int8_t* hq, const double
               : (ke + 1) / 2 <= I1 ? k_down_tok<BITS, U, I1, false, DBG>
                                       : k_down_tok<BITS, U, I2, false, DBG>;
   hipLaunchKernelGGL(kern, grid, block, 0, a.stream, L.down.codes, sm, d, f, k, n,
-                     a.r->topk_ids, a.r->topk_w, hq, hsc, a.residual, sdc, sds, dbg);
+                     a.r->topk_ids, a.r->topk_w, hf, a.residual, sdc, sds, dbg);
   return hipGetLastError();
 }
 
 template <int BITS, bool DBG>
-hipError_t launch_down_tok(const DecodeArgs& a, const int8_t* hq, const double2* hsc,
-                           const DecodeDebug& dbg, int U) {
+hipError_t launch_down_tok(const DecodeArgs& a, const float* hf, const DecodeDebug& dbg, int U) {
   switch (U) {
-    case 1: return launch_down_tok_u<BITS, 1, DBG>(a, hq, hsc, dbg);
-    case 2: return launch_down_tok_u<BITS, 2, DBG>(a, hq, hsc, dbg);
-    case 3: return launch_down_tok_u<BITS, 3, DBG>(a, hq, hsc, dbg);
-    default: return launch_down_tok_u<BITS, 4, DBG>(a, hq, hsc, dbg);
+    case 1: return launch_down_tok_u<BITS, 1, DBG>(a, hf, dbg);
+    case 2: return launch_down_tok_u<BITS, 2, DBG>(a, hf, dbg);
+    case 3: return launch_down_tok_u<BITS, 3, DBG>(a, hf, dbg);
+    default: return launch_down_tok_u<BITS, 4, DBG>(a, hf, dbg);
   }
 }
 
@@ -1112,6 +1210,7 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   int8_t* hq = reinterpret_cast<int8_t*>(a.ws + W.hq);
   double2* hsc = reinterpret_cast<double2*>(a.ws + W.hsc);
   double* y = reinterpret_cast<double*>(a.ws + W.y);
+  float* hf = reinterpret_cast<float*>(a.ws + W.hf);
   DecodeDebug dbg{};
   if (DBG) dbg = *a.dbg;
 
@@ -1168,9 +1267,19 @@ hipError_t launch_ffn(const DecodeArgs& a) {
       std::min<long long>(P, (long long)E * ((n + NPC - 1) / NPC)),
       (P + NPC - 1) / NPC + std::min<long long>(E, P));
   const int cap = a.num_cus * 8;
+  // The token-major down (down and combine in one kernel) takes windows of up to 16 tokens
+  // and 16 slots a token, d_ff up to 1024, and as many slots as its lanes hold. It reads h
+  // in fp32 and quantizes it itself; the expert-major down reads the codes.
+  const int nbf = f / 32, dt_u = (nbf + 7) / 8;
+  const int ke = k + (shared ? 1 : 0);  // slots per token
+  const bool dt_shape = n <= kDtMaxTokens && ke <= kDtMaxK && nbf <= kDtMaxBlocks &&
+                        (ke + 1) / 2 <= kDtSlotsShared / dt_u;
+  // 16-row gate/up items for the ids path of such a window: h leaves in fp32 only, and an
+  // expert-major down (down and combine in separate calls) quantizes it first
+  const bool h16 = ids && dt_shape;
   if (a.stages & MOE_DECODE_GATE_UP) {
     // one workgroup per item; the shared expert is one more chunk
-    const long long gu_items = (max_chunks + (shared ? 1 : 0)) * (f / kGuRows);
+    const long long gu_items = (max_chunks + (shared ? 1 : 0)) * (f / (h16 ? 16 : kGuRows));
     const bool group = ids && logits;  // workgroup 0 writes the routing's grouping
     const int gu_grid = (int)std::max<long long>(1, gu_items + (group ? 1 : 0));
     const uint32_t* gsm = reinterpret_cast<const uint32_t*>(L.gate.scale_min);
@@ -1179,30 +1288,42 @@ hipError_t launch_ffn(const DecodeArgs& a) {
     const uint32_t* sgs = shared ? reinterpret_cast<const uint32_t*>(L.shared_gate.scale_min) : nullptr;
     const uint32_t* suc = shared ? L.shared_up.codes : nullptr;
     const uint32_t* sus = shared ? reinterpret_cast<const uint32_t*>(L.shared_up.scale_min) : nullptr;
-    if (ids)
-      hipLaunchKernelGGL((k_gateup<BITS, NPC, 8, DBG, true>), dim3(gu_grid),
-                         dim3(GuShape<8>::kThreads), 0,
+    if (h16)
+      hipLaunchKernelGGL((k_gateup<BITS, NPC, 4, 16, DBG, true>), dim3(gu_grid),
+                         dim3(GuShape<4, 16>::kThreads), 0,
                          a.stream, L.gate.codes, gsm, L.up.codes, usm, d, f, chunks, nchunks, xq,
                          xsc, hq, hsc, a.r->topk_ids, k, n * k, E,
                          group ? a.r->expert_offsets : nullptr, a.r->pair_index, sgc, sgs, suc,
-                         sus, n, dbg);
+                         sus, n, hf, dbg);
+    else if (ids)
+      hipLaunchKernelGGL((k_gateup<BITS, NPC, 8, 32, DBG, true>), dim3(gu_grid),
+                         dim3(GuShape<8, 32>::kThreads), 0,
+                         a.stream, L.gate.codes, gsm, L.up.codes, usm, d, f, chunks, nchunks, xq,
+                         xsc, hq, hsc, a.r->topk_ids, k, n * k, E,
+                         group ? a.r->expert_offsets : nullptr, a.r->pair_index, sgc, sgs, suc,
+                         sus, n, nullptr, dbg);
     else
-      hipLaunchKernelGGL((k_gateup<BITS, NPC, 4, DBG, false>), dim3(gu_grid),
-                         dim3(GuShape<4>::kThreads), 0,
+      hipLaunchKernelGGL((k_gateup<BITS, NPC, 4, 32, DBG, false>), dim3(gu_grid),
+                         dim3(GuShape<4, 32>::kThreads), 0,
                          a.stream, L.gate.codes, gsm, L.up.codes, usm, d, f, chunks, nchunks, xq,
                          xsc, hq, hsc, a.r->topk_ids, k, n * k, E, nullptr, nullptr, nullptr,
-                         nullptr, nullptr, nullptr, n, dbg);
+                         nullptr, nullptr, nullptr, n, dt_shape ? hf : nullptr, dbg);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   // down and combine together for a small window: the token-major kernel does both
-  const int nbf = f / 32, dt_u = (nbf + 7) / 8;
-  const int ke = k + (shared ? 1 : 0);  // slots per token
-  const bool token_major = (a.stages & MOE_DECODE_DOWN) && (a.stages & MOE_DECODE_COMBINE) &&
-                           n <= kDtMaxTokens && ke <= kDtMaxK && nbf <= kDtMaxBlocks &&
-                           (ke + 1) / 2 <= kDtSlotsShared / dt_u;
-  if (token_major) return launch_down_tok<BITS, DBG>(a, hq, hsc, dbg, dt_u);
+  const bool token_major =
+      (a.stages & MOE_DECODE_DOWN) && (a.stages & MOE_DECODE_COMBINE) && dt_shape;
+  if (token_major) return launch_down_tok<BITS, DBG>(a, hf, dbg, dt_u);
   if (a.stages & MOE_DECODE_DOWN) {
+    if (h16) {
+      const long long hblocks = (P + (shared ? n : 0)) * nbf;
+      hipLaunchKernelGGL((k_hquant<BITS, DBG>), dim3((int)((hblocks * 32 + kHqThreads - 1) / kHqThreads)),
+                         dim3(kHqThreads), 0, a.stream, hf, (int)(P + (shared ? n : 0)), f, hq,
+                         hsc, dbg);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
     const long long dn_items = max_chunks * ((d + kWave - 1) / kWave);
     const int dn_grid = (int)std::max<long long>(1, std::min<long long>(dn_items, cap));
     hipLaunchKernelGGL((k_down<BITS, NPC, DBG>), dim3(dn_grid), dim3(kDnThreads), 0, a.stream,

@@ -118,6 +118,7 @@ struct DecodeWs {
   size_t xsc;      // double2 [n][d/32]   (scale, scale*sum of codes)
   size_t hq;       // int8 [Q][f] permuted hidden codes
   size_t hsc;      // double2 [Q][f/32]
+  size_t hf;       // float [Q][f] h before quantization (read by the token-major down)
   size_t y;        // double [Q][d]
   size_t logits;   // float [n][E] router logits (a layer with router weights), else empty
   size_t total;
@@ -140,6 +141,8 @@ inline DecodeWs decode_ws_layout(int n, int k, int d, int f, bool shared, int ro
   o = align256(o + P * f);
   L.hsc = o;
   o = align256(o + 16 * P * (f / 32));
+  L.hf = o;
+  o = align256(o + 4 * P * f);
   L.y = o;
   o = align256(o + 8 * P * d);
   L.logits = o;

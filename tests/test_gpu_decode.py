@@ -404,3 +404,28 @@ def test_decode_separate_down_and_combine_stages(bits):
         outs.append(out)
     # the two paths sum the pair outputs in different orders: equal to the last ulps
     np.testing.assert_allclose(outs[0], outs[1], rtol=1e-6, atol=1e-7)
+
+
+@pytest.mark.parametrize("E,d,f,k,n,bits", [
+    (32, 256, 128, 6, 4, 4),   # 16-row gate/up items (h in fp32), then the h quantization kernel
+    (16, 128, 96, 3, 5, 2),    # eight-pair chunks, 2-bit
+])
+def test_decode_separate_stages_debug_trace(E, d, f, k, n, bits):
+    # with down and combine issued separately after a small window's gate/up (which leaves
+    # h in fp32), a quantization launch of its own writes the codes the expert-major down
+    # reads: every intermediate still matches the oracle's trace
+    w, host, lg, x = _small(E, d, f, k, n, bits, seed=11)
+    layer = workloads.layer_from_host(*host, w.k)
+    routing = qmoe.route(to_dev(lg), w.k)
+    ids, wt = check_routing(lg, w.k, routing)
+    dbg = qmoe.debug_buffers(layer, n)
+    res = to_dev(x)
+    ws = qmoe.workspace(layer, n)
+    for st in (qmoe.DECODE_PREP, qmoe.DECODE_GATE_UP, qmoe.DECODE_DOWN, qmoe.DECODE_COMBINE):
+        qmoe.ffn_decode(layer, to_dev(x), routing, res, ws=ws, stages=st, debug=dbg)
+    torch.cuda.synchronize()
+    out_o, tr = O.ffn_decode(*(omat(h) for h in host), w.E, x, ids, wt, x, trace=True)
+    compare_decode_traces(dbg, tr, host, ids, bits)
+    np.testing.assert_allclose(dbg["y"].cpu().numpy(), tr["y"].astype(np.float32), rtol=1e-6,
+                               atol=1e-7)
+    assert_output_tolerance(res.cpu().numpy(), out_o)
