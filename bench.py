@@ -306,7 +306,7 @@ def bench_decode(args, torch, q, synth, workloads):
         "expert_bytes_per_step": round(float(np.mean([step_bytes[i] for i in order])), 1),
         "touched_experts_per_step": round(mean_touched, 2),
         "stage_us": stage_us,
-        "roofline": {"bound": "hbm", "kernel": "k_gateup (gate/up + SwiGLU + h quant)",
+        "roofline": {"bound": "hbm", "kernel": "k_gateup (gate/up + SwiGLU)",
                      "achieved": round(gu_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_ach / HBM_PEAK_GBS, 4),
                      "traffic": measured_traffic(TRAFFIC_PROFILE) if primary else None,

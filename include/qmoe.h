@@ -186,8 +186,10 @@ moe_status moe_expert_ffn_decode(const moe_layer* L, const float* x, int n_token
 
 /* Stages of moe_expert_ffn_decode, as bits of `stages` below. */
 #define MOE_DECODE_PREP 1u     /* int8 quantization of x and the per-expert work list     */
-#define MOE_DECODE_GATE_UP 2u  /* gate/up projections, SwiGLU, int8 quantization of h      */
-#define MOE_DECODE_DOWN 4u     /* down projection of every token-expert pair               */
+#define MOE_DECODE_GATE_UP 2u  /* gate/up projections, SwiGLU (and for large windows the
+                                  int8 quantization of h)                                 */
+#define MOE_DECODE_DOWN 4u     /* (for small windows the int8 quantization of h) down
+                                  projection of every token-expert pair                   */
 #define MOE_DECODE_COMBINE 8u  /* routing-weighted combine into the residual              */
 #define MOE_DECODE_ALL 15u
 

@@ -609,6 +609,11 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
       }
       --item;
     }
+    // 16-row items: the two halves of a 32-row block share the 128-byte lines of their
+    // scale/min words, so they run on one XCD (one L2): workgroups are dealt to the 8 XCDs
+    // in turn, and items 2m and 2m+1 of every 16 go to workgroups 8 apart (a bijection on
+    // each run of 16; the grid is a multiple of 16)
+    if (ROWS == 16) item = (item & ~15) | ((item & 7) << 1) | ((item >> 3) & 1);
     // wave 0 derives the chunk and hands it to the others through LDS (a derivation in
     // every wave costs more: all waves of all workgroups would read the same ids). The
     // weight pointers are fetched first, during the derivation (a pointer used on one side
@@ -1281,7 +1286,8 @@ hipError_t launch_ffn(const DecodeArgs& a) {
     // one workgroup per item; the shared expert is one more chunk
     const long long gu_items = (max_chunks + (shared ? 1 : 0)) * (f / (h16 ? 16 : kGuRows));
     const bool group = ids && logits;  // workgroup 0 writes the routing's grouping
-    const int gu_grid = (int)std::max<long long>(1, gu_items + (group ? 1 : 0));
+    const long long gu_run = h16 ? (gu_items + 15) / 16 * 16 : gu_items;  // see k_gateup
+    const int gu_grid = (int)std::max<long long>(1, gu_run + (group ? 1 : 0));
     const uint32_t* gsm = reinterpret_cast<const uint32_t*>(L.gate.scale_min);
     const uint32_t* usm = reinterpret_cast<const uint32_t*>(L.up.scale_min);
     const uint32_t* sgc = shared ? L.shared_gate.codes : nullptr;
