@@ -1129,18 +1129,26 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
     red[wave][j < ke ? j : kDtMaxK][r] = acc[i];  // unconditional: see above
   }
   __syncthreads();
+  // Each (slot, row) output sums its 8 wave partials in wave order, one per thread
+  // (ke*32 <= 512: all at once), into LDS over the staged h, which nobody reads any more;
+  // then 32 lanes combine the slots in slot order. (A 32-lane loop over both took 0.9 µs
+  // of dependent adds.)
+  double(*ys)[kDtRows] = reinterpret_cast<double(*)[kDtRows]>(s_act);
+  static_assert(sizeof(double) * kDtMaxK * kDtRows <= sizeof(int4) * kDtStage, "ys fits");
+  if (tid < ke * kDtRows) {
+    const int j = tid / kDtRows, rr = tid % kDtRows;
+    double y = red[0][j][rr];
+#pragma unroll
+    for (int w2 = 1; w2 < kDtWaves; ++w2) y += red[w2][j][rr];  // wave order
+    ys[j][rr] = y;
+    if (DBG && dbg.y) dbg.y[pair_of(j) * d + rt * kDtRows + rr] = (float)y;
+  }
+  __syncthreads();
   if (epi) {
     double tot = 0.0;
 #pragma unroll
-    for (int j = 0; j < kDtMaxK; ++j) {  // slot order, the shared expert last
-      if (j < ke) {
-        double y = red[0][j][r];
-#pragma unroll
-        for (int w2 = 1; w2 < kDtWaves; ++w2) y += red[w2][j][r];  // wave order
-        if (DBG && dbg.y) dbg.y[pair_of(j) * d + row] = (float)y;
-        tot += (SH && j >= k ? 1.0 : (double)sw[j]) * y;
-      }
-    }
+    for (int j = 0; j < kDtMaxK; ++j)  // slot order, the shared expert last
+      if (j < ke) tot += (SH && j >= k ? 1.0 : (double)sw[j]) * ys[j][r];
     residual[(size_t)t * d + row] = (float)((double)res0 + tot);
   }
 }
