@@ -978,7 +978,7 @@ constexpr int kDtSlotsShared = 18;  // the same with one more slot (a shared exp
 constexpr int kDtStage = kDtMaxK * kDtMaxBlocks * 3;  // 16-byte LDS entries of h
 static_assert(kDtStage % kDtThreads == 0, "staging is whole wave-level loads");
 
-template <int BITS, int U, int I, bool SH, bool DBG>
+template <int BITS, int U, int I, bool SH, bool EQ, bool DBG>
 __global__ __launch_bounds__(kDtThreads) void k_down_tok(
     const uint32_t* __restrict__ dcodes, const uint32_t* __restrict__ dsm, int d, int f, int k,
     int n, const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w,
@@ -1029,6 +1029,48 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
     for (int i = 0; i < 8; ++i)
       hv[i] = reinterpret_cast<const __attribute__((address_space(1))) v4f*>(src)[i];
   }
+  // int8 quantization of the thread's block (the arithmetic of the gate/up epilogue of
+  // 32-row items, in registers): LDS entry q = the 32 codes at their dot4 byte positions,
+  // then (scale, scale*sum). Entries past ke*nbf stay unwritten; the blocks that would read
+  // them are dropped below. (Every workgroup of the token quantizes all of its blocks.)
+  // With EQ (grids of more workgroups than CUs) it runs before the weight requests, so its
+  // registers are free while they are in flight and two workgroups fit a CU; otherwise
+  // after them, where its wait for h leaves the weights in flight.
+  auto quant_h = [&]() {
+    if (tid < nblk) {
+      float v[32];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[4 * i] = hv[i].x;
+        v[4 * i + 1] = hv[i].y;
+        v[4 * i + 2] = hv[i].z;
+        v[4 * i + 3] = hv[i].w;
+      }
+      int qc[32];
+      const float scale = quant_block32(v, qc);
+      int sum = 0;
+      uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        sum += qc[i];
+        const int pos = act_byte_pos<BITS>(i);
+        words[pos / 4] |= ((uint32_t)qc[i] & 0xffu) << (8 * (pos % 4));
+      }
+      s_act[3 * tid] = make_int4((int)words[0], (int)words[1], (int)words[2], (int)words[3]);
+      s_act[3 * tid + 1] = make_int4((int)words[4], (int)words[5], (int)words[6], (int)words[7]);
+      reinterpret_cast<double2*>(s_act)[3 * tid + 2] =
+          make_double2((double)scale, (double)scale * (double)sum);
+      if (DBG && rt == 0) {  // one workgroup per token reports the codes
+        const int j = tid / nbf, b = tid - j * nbf;
+        if (dbg.hq) {
+#pragma unroll
+          for (int i = 0; i < 32; ++i) dbg.hq[pair_of(j) * f + 32 * b + i] = (int8_t)qc[i];
+        }
+        if (dbg.hs) dbg.hs[pair_of(j) * nbf + b] = scale;
+      }
+    }
+  };
+  if (EQ) quant_h();
   __builtin_amdgcn_sched_barrier(0);
 
   // all weight blocks of this lane (past ke or nbf: a valid block, never used)
@@ -1063,42 +1105,7 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
   for (int j = 0; j < kDtMaxK; ++j)
     sw[j] = __int_as_float(
         load_uniform(reinterpret_cast<const int*>(topk_w) + (size_t)t * k + min(j, k - 1)));
-  // int8 quantization of the thread's block (the arithmetic of the gate/up epilogue of
-  // 32-row items, in registers): LDS entry q = the 32 codes at their dot4 byte positions,
-  // then (scale, scale*sum). Entries past ke*nbf stay unwritten; the blocks that would read
-  // them are dropped below. (Every workgroup of the token quantizes all of its blocks.)
-  if (tid < nblk) {
-    float v[32];
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      v[4 * i] = hv[i].x;
-      v[4 * i + 1] = hv[i].y;
-      v[4 * i + 2] = hv[i].z;
-      v[4 * i + 3] = hv[i].w;
-    }
-    int qc[32];
-    const float scale = quant_block32(v, qc);
-    int sum = 0;
-    uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      sum += qc[i];
-      const int pos = act_byte_pos<BITS>(i);
-      words[pos / 4] |= ((uint32_t)qc[i] & 0xffu) << (8 * (pos % 4));
-    }
-    s_act[3 * tid] = make_int4((int)words[0], (int)words[1], (int)words[2], (int)words[3]);
-    s_act[3 * tid + 1] = make_int4((int)words[4], (int)words[5], (int)words[6], (int)words[7]);
-    reinterpret_cast<double2*>(s_act)[3 * tid + 2] =
-        make_double2((double)scale, (double)scale * (double)sum);
-    if (DBG && rt == 0) {  // one workgroup per token reports the codes
-      const int j = tid / nbf, b = tid - j * nbf;
-      if (dbg.hq) {
-#pragma unroll
-        for (int i = 0; i < 32; ++i) dbg.hq[pair_of(j) * f + 32 * b + i] = (int8_t)qc[i];
-      }
-      if (dbg.hs) dbg.hs[pair_of(j) * nbf + b] = scale;
-    }
-  }
+  if (!EQ) quant_h();
   __syncthreads();
 
   // Every block is computed and the unused ones (past ke or nbf) are dropped by a select:
@@ -1190,9 +1197,14 @@ hipError_t launch_down_tok_u(const DecodeArgs& a, const float* hf, const DecodeD
   const uint32_t* sds = shared ? reinterpret_cast<const uint32_t*>(L.shared_down.scale_min) : nullptr;
   constexpr int I1 = kDtSlots / U, I2 = kDtSlotsShared / U;
   const int ke = k + (shared ? 1 : 0);
-  auto kern = shared                  ? k_down_tok<BITS, U, I2, true, DBG>
-              : (ke + 1) / 2 <= I1 ? k_down_tok<BITS, U, I1, false, DBG>
-                                      : k_down_tok<BITS, U, I2, false, DBG>;
+  // more workgroups than CUs: quantize h early, so that two fit a CU
+  const bool eq = (int)grid.x > a.num_cus;
+#define QMOE_DT(EQ)                                                                       \
+  (shared                 ? k_down_tok<BITS, U, I2, true, EQ, DBG>                        \
+   : (ke + 1) / 2 <= I1 ? k_down_tok<BITS, U, I1, false, EQ, DBG>                         \
+                          : k_down_tok<BITS, U, I2, false, EQ, DBG>)
+  auto kern = eq ? QMOE_DT(true) : QMOE_DT(false);
+#undef QMOE_DT
   hipLaunchKernelGGL(kern, grid, block, 0, a.stream, L.down.codes, sm, d, f, k, n,
                      a.r->topk_ids, a.r->topk_w, hf, a.residual, sdc, sds, dbg);
   return hipGetLastError();

@@ -429,3 +429,14 @@ def test_decode_separate_stages_debug_trace(E, d, f, k, n, bits):
     np.testing.assert_allclose(dbg["y"].cpu().numpy(), tr["y"].astype(np.float32), rtol=1e-6,
                                atol=1e-7)
     assert_output_tolerance(res.cpu().numpy(), out_o)
+
+
+@pytest.mark.parametrize("E,d,f,k,n,bits", [
+    (16, 4096, 128, 4, 3, 4),   # 8*16*3 = 384 down workgroups: h quantized before the weights
+    (12, 8192, 96, 3, 2, 2),    # 512 down workgroups, 2-bit
+])
+def test_decode_down_grid_past_one_round(E, d, f, k, n, bits):
+    # a token-major down grid with more workgroups than CUs takes the instance that
+    # quantizes h before requesting its weights (fewer registers: two workgroups a CU)
+    w, host, lg, x = _small(E, d, f, k, n, bits, seed=13)
+    _decode_parity(w, host, lg, x)
