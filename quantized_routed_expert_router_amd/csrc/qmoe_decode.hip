@@ -952,13 +952,14 @@ __global__ __launch_bounds__(kThreads) void k_combine(const double* __restrict__
 // ---------------------------------------------------------------- down + combine, token-major
 //
 // For small windows the down projection is organised by token instead of by expert: a
-// workgroup owns (token t, 32 rows of d), computes those rows of the down outputs of all
-// k pairs of t and applies the routing-weighted combine itself (slot order, binary64), so
-// the pair outputs never leave the workgroup and the combine needs no launch of its own.
-// An expert shared by several tokens of the window is read once per token; the row tiles
-// are laid out so that all tokens of one row tile run on one XCD, whose L2 then serves
-// the repeats. Lane l of wave w owns row l%32 and the experts j = l/32, l/32 + 2, ... of
-// the token, for blocks w, w+8, ... of f.
+// workgroup owns (token t, R rows of d; R = 32, or 8 and 16 for one and two tokens),
+// computes those rows of the down outputs of all k pairs of t and applies the routing-
+// weighted combine itself (slot order, binary64), so the pair outputs never leave the
+// workgroup and the combine needs no launch of its own. An expert shared by several
+// tokens of the window is read once per token; the row tiles are laid out so that all
+// tokens of one row tile run on one XCD, whose L2 then serves the repeats. Lane l of wave
+// w owns row l%R and the experts j = l/R, l/R + 64/R, ... of the token, for blocks w,
+// w+8, ... of f.
 //
 // Order of requests: the experts of the lane's pairs, the token's residual values and its
 // h (fp32) go out first; then all U*I weight blocks of the lane (the whole token at
@@ -967,7 +968,6 @@ __global__ __launch_bounds__(kThreads) void k_combine(const double* __restrict__
 // of the token does this for itself, while its weights are in flight) and meets the
 // barrier; each block's dots start as soon as that block has landed. The 8 waves' partial
 // sums meet in LDS.
-constexpr int kDtRows = 32;
 constexpr int kDtWaves = 8;
 constexpr int kDtThreads = kDtWaves * kWave;
 constexpr int kDtMaxK = 16;       // top-k handled by this path
@@ -978,27 +978,29 @@ constexpr int kDtSlotsShared = 18;  // the same with one more slot (a shared exp
 constexpr int kDtStage = kDtMaxK * kDtMaxBlocks * 3;  // 16-byte LDS entries of h
 static_assert(kDtStage % kDtThreads == 0, "staging is whole wave-level loads");
 
-template <int BITS, int U, int I, bool SH, bool EQ, bool DBG>
+template <int BITS, int U, int I, bool SH, bool EQ, bool DBG, int R>
 __global__ __launch_bounds__(kDtThreads) void k_down_tok(
     const uint32_t* __restrict__ dcodes, const uint32_t* __restrict__ dsm, int d, int f, int k,
     int n, const int32_t* __restrict__ topk_ids, const float* __restrict__ topk_w,
     const float* __restrict__ hf, float* residual, const uint32_t* __restrict__ sdcodes,
     const uint32_t* __restrict__ sdsm, DecodeDebug dbg) {
   // slots j < k: the routed pairs t*k + j; with SH, slot k: the shared expert, pair n*k + t,
-  // weight 1. I slots per lane half (lane half h takes j = h, h+2, ...). Without SH every
-  // shared-slot select folds away.
+  // weight 1. R rows a workgroup; lane group h = lane / R takes slots j = h, h + G, ... (G =
+  // 64/R groups, I slots a lane). Without SH every shared-slot select folds away.
+  static_assert(R == 8 || R == 16 || R == 32, "row tile");
+  constexpr int G = kWave / R;
   const int ke = SH ? k + 1 : k;
   __shared__ int4 s_act[kDtStage];
-  __shared__ double red[kDtWaves][kDtMaxK + 1][kDtRows];  // slot kDtMaxK: unused pairs
-  const int nbf = f / 32, nrt = d / kDtRows;
+  __shared__ double red[kDtWaves][kDtMaxK + 1][R];  // slot kDtMaxK: unused pairs
+  const int nbf = f / 32, nrt = d / R;
   const int per = (nrt + 7) / 8;  // row tiles per XCD
   const int xcd = blockIdx.x % 8, slot = blockIdx.x / 8;
   const int rt = xcd * per + slot / n, t = slot % n;
   if (slot >= per * n || rt >= nrt) return;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
-  const int r = lane % kDtRows, h = lane / kDtRows;
-  const int row = rt * kDtRows + r;
+  const int r = lane % R, h = lane / R;
+  const int row = rt * R + r;
   const int P = n * k;
   auto pair_of = [&](int j) { return SH && j >= k ? (size_t)P + t : (size_t)t * k + j; };
 
@@ -1007,12 +1009,12 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
   int eid[I];
 #pragma unroll
   for (int i = 0; i < I; ++i) {
-    const int j = min(h + 2 * i, ke - 1);
+    const int j = min(h + G * i, ke - 1);
     const int id = topk_ids[(size_t)t * k + min(j, k - 1)];
     eid[i] = SH && j >= k ? -1 : id;
   }
-  const bool epi = wave == 0 && lane < kDtRows;
-  const float res0 = residual[(size_t)t * d + (epi ? row : rt * kDtRows)];
+  const bool epi = wave == 0 && lane < R;
+  const float res0 = residual[(size_t)t * d + (epi ? row : rt * R)];
 
   // h of the token in fp32 into registers: thread q takes block q of the token's ke*nbf
   // (<= 512) blocks, slot j = q / nbf and rows 32b .. 32b+31 with b = q % nbf; threads past
@@ -1115,7 +1117,7 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
 #pragma unroll
   for (int i = 0; i < I; ++i) {
     acc[i] = 0.0;
-    const int j = h + 2 * i;
+    const int j = h + G * i;
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int b = wave + 8 * u;
@@ -1137,18 +1139,18 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
   }
   __syncthreads();
   // Each (slot, row) output sums its 8 wave partials in wave order, one per thread
-  // (ke*32 <= 512: all at once), into LDS over the staged h, which nobody reads any more;
-  // then 32 lanes combine the slots in slot order. (A 32-lane loop over both took 0.9 µs
+  // (ke*R <= 512: all at once), into LDS over the staged h, which nobody reads any more;
+  // then R lanes combine the slots in slot order. (A 32-lane loop over both took 0.9 µs
   // of dependent adds.)
-  double(*ys)[kDtRows] = reinterpret_cast<double(*)[kDtRows]>(s_act);
-  static_assert(sizeof(double) * kDtMaxK * kDtRows <= sizeof(int4) * kDtStage, "ys fits");
-  if (tid < ke * kDtRows) {
-    const int j = tid / kDtRows, rr = tid % kDtRows;
+  double(*ys)[R] = reinterpret_cast<double(*)[R]>(s_act);
+  static_assert(sizeof(double) * kDtMaxK * R <= sizeof(int4) * kDtStage, "ys fits");
+  if (tid < ke * R) {
+    const int j = tid / R, rr = tid % R;
     double y = red[0][j][rr];
 #pragma unroll
     for (int w2 = 1; w2 < kDtWaves; ++w2) y += red[w2][j][rr];  // wave order
     ys[j][rr] = y;
-    if (DBG && dbg.y) dbg.y[pair_of(j) * d + rt * kDtRows + rr] = (float)y;
+    if (DBG && dbg.y) dbg.y[pair_of(j) * d + rt * R + rr] = (float)y;
   }
   __syncthreads();
   if (epi) {
@@ -1183,13 +1185,19 @@ __global__ __launch_bounds__(kHqThreads) void k_hquant(const float* __restrict__
   }
 }
 
-// Slots per lane half: kDtSlots / U weight blocks in flight per lane, or kDtSlotsShared / U
-// when the window needs one more slot than that (a shared expert).
+// Row tile: 32 rows a workgroup, or 8 and 16 for one- and two-token windows, which would
+// otherwise fill only a quarter or half of the CUs (64 and 128 workgroups at d = 2048).
+// Slots a lane: with 32 rows, kDtSlots / U weight blocks in flight per lane, or
+// kDtSlotsShared / U when the window needs one more slot than that (a shared expert); with
+// 16 and 8 rows, 4 and 2 slots (at most 16 slots a token).
+inline int down_tok_rows(int n) { return n == 1 ? 8 : n == 2 ? 16 : 32; }
+
 template <int BITS, int U, bool DBG>
 hipError_t launch_down_tok_u(const DecodeArgs& a, const float* hf, const DecodeDebug& dbg) {
   const moe_layer& L = *a.L;
   const int d = L.d_model, f = L.d_ff, k = L.top_k, n = a.n;
-  const int per = (d / kDtRows + 7) / 8;
+  const int R = down_tok_rows(n);
+  const int per = (d / R + 7) / 8;
   const dim3 grid(8 * per * n), block(kDtThreads);
   const uint32_t* sm = reinterpret_cast<const uint32_t*>(L.down.scale_min);
   const bool shared = has_shared(L);
@@ -1200,9 +1208,13 @@ hipError_t launch_down_tok_u(const DecodeArgs& a, const float* hf, const DecodeD
   // more workgroups than CUs: quantize h early, so that two fit a CU
   const bool eq = (int)grid.x > a.num_cus;
 #define QMOE_DT(EQ)                                                                       \
-  (shared                 ? k_down_tok<BITS, U, I2, true, EQ, DBG>                        \
-   : (ke + 1) / 2 <= I1 ? k_down_tok<BITS, U, I1, false, EQ, DBG>                         \
-                          : k_down_tok<BITS, U, I2, false, EQ, DBG>)
+  (R == 8    ? (shared ? k_down_tok<BITS, U, 2, true, EQ, DBG, 8>                          \
+                       : k_down_tok<BITS, U, 2, false, EQ, DBG, 8>)                        \
+   : R == 16 ? (shared ? k_down_tok<BITS, U, 4, true, EQ, DBG, 16>                         \
+                       : k_down_tok<BITS, U, 4, false, EQ, DBG, 16>)                       \
+   : shared  ? k_down_tok<BITS, U, I2, true, EQ, DBG, 32>                                  \
+   : (ke + 1) / 2 <= I1 ? k_down_tok<BITS, U, I1, false, EQ, DBG, 32>                      \
+                        : k_down_tok<BITS, U, I2, false, EQ, DBG, 32>)
   auto kern = eq ? QMOE_DT(true) : QMOE_DT(false);
 #undef QMOE_DT
   hipLaunchKernelGGL(kern, grid, block, 0, a.stream, L.down.codes, sm, d, f, k, n,
