@@ -47,14 +47,22 @@ constexpr int kThreads = 256;
 
 // ---------------------------------------------------------------- int8 block quantizer
 
-// Quantize one 32-value block held as v[32]: returns scale; q receives codes.
+// Quantize one 32-value block held as v[32]: returns scale; q receives codes. The block
+// maximum of |v| is taken over the bit patterns as unsigned integers (which order
+// non-negative floats like their values) in a tree, so it is exact and its dependent
+// chain is 5 steps instead of 32.
 __device__ __forceinline__ float quant_block32(const float (&v)[32], int (&q)[32]) {
-  float amax = 0.0f;
+  uint32_t m[16];
 #pragma unroll
-  for (int i = 0; i < 32; ++i) {
-    const float a = fabsf(v[i]);
-    amax = a > amax ? a : amax;
+  for (int i = 0; i < 16; ++i) {
+    const uint32_t a = __float_as_uint(fabsf(v[2 * i])), b = __float_as_uint(fabsf(v[2 * i + 1]));
+    m[i] = a > b ? a : b;
   }
+#pragma unroll
+  for (int w = 8; w >= 1; w /= 2)
+#pragma unroll
+    for (int i = 0; i < w; ++i) m[i] = m[i] > m[i + w] ? m[i] : m[i + w];
+  const float amax = __uint_as_float(m[0]);
   if (amax == 0.0f) {
 #pragma unroll
     for (int i = 0; i < 32; ++i) q[i] = 0;
@@ -70,6 +78,18 @@ __device__ __forceinline__ float quant_block32(const float (&v)[32], int (&q)[32
     q[i] = (int)t;
   }
   return scale;
+}
+
+// Sum of the 32 codes of a block, in a tree (exact in int32).
+__device__ __forceinline__ int code_sum32(const int (&q)[32]) {
+  int s[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) s[i] = q[2 * i] + q[2 * i + 1];
+#pragma unroll
+  for (int w = 8; w >= 1; w /= 2)
+#pragma unroll
+    for (int i = 0; i < w; ++i) s[i] += s[i + w];
+  return s[0];
 }
 
 // ---------------------------------------------------------------- prep: x quant + work list
@@ -96,9 +116,7 @@ __device__ __forceinline__ void quant_x_block(const float* __restrict__ x, int d
   }
   int q[32];
   const float scale = quant_block32(v, q);
-  int sum = 0;
-#pragma unroll
-  for (int i = 0; i < 32; ++i) sum += q[i];
+  const int sum = code_sum32(q);
   uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
   for (int i = 0; i < 32; ++i) {
@@ -1050,11 +1068,10 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
       }
       int qc[32];
       const float scale = quant_block32(v, qc);
-      int sum = 0;
+      const int sum = code_sum32(qc);
       uint32_t words[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 #pragma unroll
       for (int i = 0; i < 32; ++i) {
-        sum += qc[i];
         const int pos = act_byte_pos<BITS>(i);
         words[pos / 4] |= ((uint32_t)qc[i] & 0xffu) << (8 * (pos % 4));
       }
