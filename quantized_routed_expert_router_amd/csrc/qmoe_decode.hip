@@ -993,8 +993,8 @@ constexpr int kDtMaxBlocks = 32;  // f/32 handled by this path
 constexpr int kDtMaxTokens = 16;  // window tokens handled by this path
 constexpr int kDtSlots = 16;      // weight blocks in flight per lane
 constexpr int kDtSlotsShared = 18;  // the same with one more slot (a shared expert)
-constexpr int kDtStage = kDtMaxK * kDtMaxBlocks * 3;  // 16-byte LDS entries of h
-static_assert(kDtStage % kDtThreads == 0, "staging is whole wave-level loads");
+constexpr int kDtStage = kDtMaxK * kDtMaxBlocks * 3;  // 16-byte LDS entries of quantized h
+static_assert(kDtMaxK * kDtMaxBlocks <= kDtThreads, "one h block per thread");
 
 template <int BITS, int U, int I, bool SH, bool EQ, bool DBG, int R>
 __global__ __launch_bounds__(kDtThreads) void k_down_tok(
