@@ -611,8 +611,7 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
   // workgroups past the live count exit. (A loop over items would make the compiler's wait
   // counts conservative at its head: the first weight requests would wait for the
   // activation staging.) Without IDS, scalar loads of a chunk's work record give expert,
-  // pair and token ids; the grid never exceeds max_chunks * ntiles, so the record is
-  // inside the work-list buffer.
+  // pair and token ids.
   int e, np, pid[NPC];
   RowSet<NPC> rows;
   int item = blockIdx.x, nch;
@@ -677,8 +676,11 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
   } else {
     // The record, the live chunk count and the weight pointers are fetched together: the
     // empty asm needs all of them, so no load is sunk behind the item test (which would
-    // chain two or three round trips before the first weight request).
-    const int* rec = chunks + (size_t)(item / ntiles) * kChunkInts;
+    // chain two or three round trips before the first weight request). 16-row items are
+    // permuted as above; the grid rounded up to 16 may pass the last record, so the index
+    // is clamped to the P+1 records of the work list (such items exit below).
+    if (ROWS == 16) item = (item & ~15) | ((item & 7) << 1) | ((item >> 3) & 1);
+    const int* rec = chunks + (size_t)min(item / ntiles, P) * kChunkInts;
     e = load_uniform(rec);
     np = load_uniform(rec + 2);
 #pragma unroll
@@ -1328,9 +1330,9 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   const int ke = k + (shared ? 1 : 0);  // slots per token
   const bool dt_shape = n <= kDtMaxTokens && ke <= kDtMaxK && nbf <= kDtMaxBlocks &&
                         (ke + 1) / 2 <= kDtSlotsShared / dt_u;
-  // 16-row gate/up items for the ids path of such a window: h leaves in fp32 only, and an
-  // expert-major down (down and combine in separate calls) quantizes it first
-  const bool h16 = ids && dt_shape;
+  // 16-row gate/up items for such a window: h leaves in fp32 only, and an expert-major
+  // down (down and combine in separate calls) quantizes it first
+  const bool h16 = dt_shape;
   if (a.stages & MOE_DECODE_GATE_UP) {
     // one workgroup per item; the shared expert is one more chunk
     const long long gu_items = (max_chunks + (shared ? 1 : 0)) * (f / (h16 ? 16 : kGuRows));
@@ -1343,7 +1345,7 @@ hipError_t launch_ffn(const DecodeArgs& a) {
     const uint32_t* sgs = shared ? reinterpret_cast<const uint32_t*>(L.shared_gate.scale_min) : nullptr;
     const uint32_t* suc = shared ? L.shared_up.codes : nullptr;
     const uint32_t* sus = shared ? reinterpret_cast<const uint32_t*>(L.shared_up.scale_min) : nullptr;
-    if (h16)
+    if (h16 && ids)
       hipLaunchKernelGGL((k_gateup<BITS, NPC, 4, 16, DBG, true>), dim3(gu_grid),
                          dim3(GuShape<4, 16>::kThreads), 0,
                          a.stream, L.gate.codes, gsm, L.up.codes, usm, d, f, chunks, nchunks, xq,
@@ -1357,12 +1359,18 @@ hipError_t launch_ffn(const DecodeArgs& a) {
                          xsc, hq, hsc, a.r->topk_ids, k, n * k, E,
                          group ? a.r->expert_offsets : nullptr, a.r->pair_index, sgc, sgs, suc,
                          sus, n, nullptr, dbg);
+    else if (h16)
+      hipLaunchKernelGGL((k_gateup<BITS, NPC, 4, 16, DBG, false>), dim3(gu_grid),
+                         dim3(GuShape<4, 16>::kThreads), 0,
+                         a.stream, L.gate.codes, gsm, L.up.codes, usm, d, f, chunks, nchunks, xq,
+                         xsc, hq, hsc, a.r->topk_ids, k, n * k, E, nullptr, nullptr, nullptr,
+                         nullptr, nullptr, nullptr, n, hf, dbg);
     else
       hipLaunchKernelGGL((k_gateup<BITS, NPC, 4, 32, DBG, false>), dim3(gu_grid),
                          dim3(GuShape<4, 32>::kThreads), 0,
                          a.stream, L.gate.codes, gsm, L.up.codes, usm, d, f, chunks, nchunks, xq,
                          xsc, hq, hsc, a.r->topk_ids, k, n * k, E, nullptr, nullptr, nullptr,
-                         nullptr, nullptr, nullptr, n, dt_shape ? hf : nullptr, dbg);
+                         nullptr, nullptr, nullptr, n, nullptr, dbg);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }

@@ -151,6 +151,8 @@ def test_decode_config1_tiny(bits):
     (8, 64, 64, 8, 3, 4),     # k = E: every expert
     (16, 128, 64, 1, 9, 4),   # k = 1: weights exactly 1
     (5, 64, 32, 2, 40, 2),    # many pairs per expert: several chunks per expert
+    (32, 256, 128, 10, 7, 4), # 70 pairs: work-list chunks, 16-row items, token-major down
+    (24, 96, 96, 12, 16, 2),  # 16 tokens (the token-major limit), 192 pairs, 2-bit
 ])
 def test_decode_small_shapes(E, d, f, k, n, bits):
     w, host, lg, x = _small(E, d, f, k, n, bits, seed=1)
@@ -409,6 +411,7 @@ def test_decode_separate_down_and_combine_stages(bits):
 @pytest.mark.parametrize("E,d,f,k,n,bits", [
     (32, 256, 128, 6, 4, 4),   # 16-row gate/up items (h in fp32), then the h quantization kernel
     (16, 128, 96, 3, 5, 2),    # eight-pair chunks, 2-bit
+    (32, 256, 128, 10, 7, 4),  # 70 pairs: chunks from the work list, 16-row items
 ])
 def test_decode_separate_stages_debug_trace(E, d, f, k, n, bits):
     # with down and combine issued separately after a small window's gate/up (which leaves
