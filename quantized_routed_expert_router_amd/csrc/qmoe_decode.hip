@@ -1379,6 +1379,16 @@ hipError_t launch_ffn(const DecodeArgs& a) {
       (a.stages & MOE_DECODE_DOWN) && (a.stages & MOE_DECODE_COMBINE) && dt_shape;
   if (token_major) return launch_down_tok<BITS, DBG>(a, hf, dbg, dt_u);
   if (a.stages & MOE_DECODE_DOWN) {
+    if (ids && logits) {
+      // with logits the ids path builds no work list (gate/up takes its chunks from the
+      // expert ids and writes the grouping): the expert-major down builds it from that
+      // grouping (block 0 of the prep kernel alone)
+      hipLaunchKernelGGL(k_prep<BITS>, dim3(1), dim3(kPrepThreads), 0, a.stream, a.x, n, d,
+                         a.r->expert_offsets, a.r->pair_index, E, k, NPC, chunks, nchunks, xq,
+                         xsc, nullptr, nullptr);
+      err = hipGetLastError();
+      if (err != hipSuccess) return err;
+    }
     if (h16) {
       const long long hblocks = (P + (shared ? n : 0)) * nbf;
       hipLaunchKernelGGL((k_hquant<BITS, DBG>), dim3((int)((hblocks * 32 + kHqThreads - 1) / kHqThreads)),

@@ -443,3 +443,24 @@ def test_decode_down_grid_past_one_round(E, d, f, k, n, bits):
     # quantizes h before requesting its weights (fewer registers: two workgroups a CU)
     w, host, lg, x = _small(E, d, f, k, n, bits, seed=13)
     _decode_parity(w, host, lg, x)
+
+
+@pytest.mark.parametrize("E,d,f,k,n,bits", [
+    (32, 256, 128, 6, 4, 4),   # chunks from the ids: the down stage builds the work list
+    (64, 128, 96, 8, 5, 2),    # eight-pair chunks from the ids
+])
+def test_layer_decode_separate_down_and_combine(E, d, f, k, n, bits):
+    # moe_layer_decode_stages with logits, down and combine issued separately: the
+    # expert-major down needs a work list, which the ids path does not build up front
+    w, host, lg, x = _small(E, d, f, k, n, bits, seed=17)
+    layer = workloads.layer_from_host(*host, w.k)
+    lg_d, x_d = to_dev(lg), to_dev(x)
+    ws = qmoe.workspace(layer, n)
+    res = x_d.clone()
+    r = qmoe.Routing.empty(n, w.E, w.k, "cuda")
+    for st in (qmoe.DECODE_PREP, qmoe.DECODE_GATE_UP, qmoe.DECODE_DOWN, qmoe.DECODE_COMBINE):
+        qmoe.layer_decode(layer, lg_d, x_d, res, routing=r, ws=ws, stages=st)
+    torch.cuda.synchronize()
+    ids, wt = check_routing(lg, w.k, r)
+    out_o, _ = O.ffn_decode(*(omat(h) for h in host), w.E, x, ids, wt, x)
+    assert_output_tolerance(res.cpu().numpy(), out_o)
