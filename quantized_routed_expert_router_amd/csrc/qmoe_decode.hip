@@ -34,7 +34,7 @@
 // Block terms (scale*xs)*dot and min*(xs*sum) are exact in binary64, so row sums round
 // only in the additions. Every expert's weights are read once per chunk of up to NPC
 // pairs; at n <= NPC tokens (the T = 4 window) every touched expert is read exactly once
-// per call.
+// per call, and up to 2*NPC tokens at most twice.
 #include <algorithm>
 
 #include "qmoe_route_dev.h"
@@ -536,16 +536,19 @@ __device__ __forceinline__ void wait_vmcnt() {
   __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
-// Chunks straight from the routing (IDS): for windows of n <= NPC tokens and P = n*k <= 64
-// pairs every expert's pairs form one chunk, so a workgroup derives its item's chunk from
-// the P expert ids instead of reading a work list (one wavefront does it). Lane p holds
-// ids[p] and sets bit ids[p] of an expert bitset in LDS (a wave's LDS operations complete
-// in order, so no barrier is needed); chunks are the experts present, in ascending id
-// order: a scan of the words' popcounts finds the word holding chunk c and a bit walk the
-// expert. The chunk's pairs are the lanes holding that expert, in pair order. This saves
-// the routing kernel its grouping and work list, which sit on the critical path there. With `offsets` given,
-// workgroup 0 writes the routing's expert offsets and pair index (the grouping) while the
-// other workgroups stream, and item i runs on workgroup i + 1.
+// Chunks straight from the routing (IDS): for windows of n <= 2*NPC tokens and P = n*k <=
+// 64 pairs, a workgroup derives its item's chunk from the P expert ids instead of reading
+// a work list (one wavefront does it). Lane p holds ids[p] and sets bit ids[p] of an expert
+// bitset in LDS (a wave's LDS operations complete in order, so no barrier is needed). An
+// expert with more than NPC pairs (possible when n > NPC) takes two chunks: its first NPC
+// pairs in pair order, then the rest; the lane that arrives as its (NPC+1)-th pair at an
+// LDS counter marks it in a second bitset. Chunks are the experts present in ascending id
+// order, each followed by its second chunk if marked: a scan of the words' chunk counts
+// finds the word holding chunk c and a walk over its bits the expert and part. The
+// chunk's pairs are the lanes holding that expert (a ballot). This saves the routing
+// kernel its grouping and work list, which sit on the critical path there. With `offsets`
+// given, workgroup 0 writes the routing's expert offsets and pair index (the grouping)
+// while the other workgroups stream, and item i runs on workgroup i + 1.
 constexpr int kExpertWords = MOE_MAX_EXPERTS / 32;
 static_assert(kExpertWords <= kWave, "one bitset word per lane");
 
@@ -555,25 +558,50 @@ struct IdsChunk {
   int pid[NPC];
 };
 
+// s_bits: 2*kExpertWords words of LDS; s_cnt: MOE_MAX_EXPERTS ints (used when split).
 template <int NPC>
 __device__ __forceinline__ IdsChunk<NPC> chunk_from_ids(const int32_t* __restrict__ topk_ids,
-                                                        int P, int c, int lane, uint32_t* s_bits) {
+                                                        int P, int c, int lane, uint32_t* s_bits,
+                                                        int* s_cnt, bool split) {
   const int idv = lane < P ? topk_ids[lane] : -1;
-  if (lane < kExpertWords) s_bits[lane] = 0u;
+  uint32_t* s_two = s_bits + kExpertWords;
+  if (lane < kExpertWords) {
+    s_bits[lane] = 0u;
+    s_two[lane] = 0u;
+  }
+  if (split && lane < P) s_cnt[idv] = 0;
   if (lane < P) atomicOr(&s_bits[idv >> 5], 1u << (idv & 31));
+  if (split && lane < P && atomicAdd(&s_cnt[idv], 1) == NPC)
+    atomicOr(&s_two[idv >> 5], 1u << (idv & 31));
   const uint32_t word = lane < kExpertWords ? s_bits[lane] : 0u;
-  const int cnt = __popc(word);
+  const uint32_t two = lane < kExpertWords ? s_two[lane] : 0u;
+  const int cnt = __popc(word) + __popc(two);  // chunks of the experts in this word
   const int incl = wave_inclusive_scan(cnt);
   IdsChunk<NPC> ch;
   ch.nch = __builtin_amdgcn_readlane(incl, kWave - 1);
   const uint64_t hit = __ballot(incl > c && incl - cnt <= c);  // the word holding chunk c
   const int w = hit ? __builtin_ctzll(hit) : 0;
   uint32_t wb = (uint32_t)__builtin_amdgcn_readlane((int)word, w);
-  const int skip = c - (__builtin_amdgcn_readlane(incl, w) - __builtin_amdgcn_readlane(cnt, w));
-  for (int i = 0; i < skip && wb; ++i) wb &= wb - 1;
-  ch.e = 32 * w + (wb ? __builtin_ctz(wb) : 0);
+  const uint32_t wb2 = (uint32_t)__builtin_amdgcn_readlane((int)two, w);
+  int skip = c - (__builtin_amdgcn_readlane(incl, w) - __builtin_amdgcn_readlane(cnt, w));
+  int bit = 0, part = 0;
+  while (wb) {  // experts of the word in ascending order, 1 or 2 chunks each
+    bit = __builtin_ctz(wb);
+    const int take = 1 + (int)((wb2 >> bit) & 1u);
+    if (skip < take) {
+      part = skip;
+      break;
+    }
+    skip -= take;
+    wb &= wb - 1;
+  }
+  ch.e = 32 * w + bit;  // past the last chunk: some expert present, never used
   uint64_t pm = __ballot(lane < P && idv == ch.e);
-  ch.np = __popcll(pm);
+  if (part) {
+#pragma unroll
+    for (int i = 0; i < NPC; ++i) pm &= pm - 1;
+  }
+  ch.np = min(__popcll(pm), NPC);
 #pragma unroll
   for (int j = 0; j < NPC; ++j) {  // slots past np repeat the last pair
     ch.pid[j] = pm ? __builtin_ctzll(pm) : (j ? ch.pid[j - 1] : 0);
@@ -597,7 +625,8 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
   static_assert(ROWS == 16 || ROWS == 32, "item rows");
   __shared__ double red[WAVES][NPC][ROWS];
   __shared__ int4 s_act_raw[ActLds<NPC, kGuGroup, S::kThreads>::kPadded];
-  __shared__ uint32_t s_bits[kExpertWords];
+  __shared__ uint32_t s_bits[2 * kExpertWords];
+  __shared__ int s_cnt[IDS ? MOE_MAX_EXPERTS : 1];
   int4 (*s_act)[kGuGroup][3] = reinterpret_cast<int4 (*)[kGuGroup][3]>(s_act_raw);
   const int nbd = d / 32, nbf = f / 32;
   const int ntiles = f / ROWS;
@@ -641,15 +670,17 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
                  "+s"(sgsm), "+s"(sucodes), "+s"(susm), "+s"(xq), "+s"(xsc), "+s"(kmul));
     __shared__ IdsChunk<NPC> s_ch;
     if (wave == 0) {
-      IdsChunk<NPC> c0 = chunk_from_ids<NPC>(topk_ids, P, item / ntiles, lane, s_bits);
-      if (sgcodes) {  // the shared expert: one chunk after the routed ones, all n tokens
-        if (item / ntiles == c0.nch) {
+      IdsChunk<NPC> c0 =
+          chunk_from_ids<NPC>(topk_ids, P, item / ntiles, lane, s_bits, s_cnt, n > NPC);
+      if (sgcodes) {  // the shared expert: chunks of NPC tokens after the routed ones
+        const int ns = (n + NPC - 1) / NPC, sc = item / ntiles - c0.nch;
+        if (sc >= 0 && sc < ns) {
           c0.e = -1;
-          c0.np = n;
+          c0.np = min(NPC, n - sc * NPC);
 #pragma unroll
-          for (int j = 0; j < NPC; ++j) c0.pid[j] = P + min(j, n - 1);
+          for (int j = 0; j < NPC; ++j) c0.pid[j] = P + sc * NPC + min(j, c0.np - 1);
         }
-        c0.nch += 1;
+        c0.nch += ns;
       }
       if (lane == 0) s_ch = c0;
     }
@@ -1274,7 +1305,7 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   hipError_t err = hipSuccess;
   // chunks straight from the expert ids (see k_gateup); with logits, the gate/up stage also
   // writes the routing's grouping
-  const bool ids = n <= NPC && (long long)n * k <= kWave;
+  const bool ids = n <= 2 * NPC && (long long)n * k <= kWave;
   // logits to route from: the caller's, or the router projection's in the workspace
   const float* logits = a.project ? reinterpret_cast<const float*>(a.ws + W.logits) : a.logits;
   if (a.stages & MOE_DECODE_PREP) {
@@ -1335,7 +1366,8 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   const bool h16 = dt_shape;
   if (a.stages & MOE_DECODE_GATE_UP) {
     // one workgroup per item; the shared expert is one more chunk
-    const long long gu_items = (max_chunks + (shared ? 1 : 0)) * (f / (h16 ? 16 : kGuRows));
+    const long long gu_items =
+        (max_chunks + (shared ? (n + NPC - 1) / NPC : 0)) * (f / (h16 ? 16 : kGuRows));
     const bool group = ids && logits;  // workgroup 0 writes the routing's grouping
     const long long gu_run = h16 ? (gu_items + 15) / 16 * 16 : gu_items;  // see k_gateup
     const int gu_grid = (int)std::max<long long>(1, gu_run + (group ? 1 : 0));
@@ -1415,7 +1447,10 @@ hipError_t launch_ffn(const DecodeArgs& a) {
 
 template <int BITS, bool DBG>
 hipError_t launch_bits(const DecodeArgs& a) {
-  if (a.n <= 4) return launch_ffn<BITS, 4, DBG>(a);
+  // chunks of 4 pairs (95 registers: five 16-row gate/up workgroups a CU) up to 8 tokens
+  // while the ids path applies (an expert then takes at most two chunks)
+  if (a.n <= 4 || (a.n <= 8 && (long long)a.n * a.L->top_k <= kWave))
+    return launch_ffn<BITS, 4, DBG>(a);
   return launch_ffn<BITS, 8, DBG>(a);
 }
 

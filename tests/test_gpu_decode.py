@@ -152,6 +152,8 @@ def test_decode_config1_tiny(bits):
     (16, 128, 64, 1, 9, 4),   # k = 1: weights exactly 1
     (5, 64, 32, 2, 40, 2),    # many pairs per expert: several chunks per expert
     (32, 256, 128, 10, 7, 4), # 70 pairs: work-list chunks, 16-row items, token-major down
+    (6, 128, 96, 5, 6, 4),    # experts with 5-6 of 6 tokens: two chunks from the ids
+    (5, 64, 64, 4, 8, 2),     # 8 tokens on 5 experts: two 4-pair chunks per expert
     (24, 96, 96, 12, 16, 2),  # 16 tokens (the token-major limit), 192 pairs, 2-bit
 ])
 def test_decode_small_shapes(E, d, f, k, n, bits):
@@ -337,6 +339,7 @@ def _layer_vs_two_calls(w, host_or_layer, lg, x, logits_kind=None):
 @pytest.mark.parametrize("E,d,f,k,n,bits", [
     (8, 256, 128, 2, 1, 4),      # config 1 shape, one expert slot per lane
     (64, 128, 96, 8, 5, 2),      # T = 5 window
+    (6, 128, 64, 5, 8, 4),       # 8 tokens, 6 experts: chunks split in two, grouping in gate/up
     (1024, 64, 64, 64, 64, 4),   # largest fused batch: 4096 pairs, grouped by histograms
     (100, 96, 64, 3, 64, 4),     # E not a multiple of 64
     (16, 64, 64, 4, 65, 2),      # one token past the fused limit: separate routing kernels

@@ -57,6 +57,8 @@ def _parity(w, host, sh, lg, x, layer=None, residual=None, dots=True):
     (16, 128, 64, 1, 8, 4),     # k = 1, the largest window (8 tokens)
     (32, 128, 256, 15, 4, 2),   # 16 slots a token (15 routed + shared), 60 routed pairs
     (16, 64, 1024, 7, 2, 4),    # the largest d_ff (32 blocks), 8 slots a token
+    (6, 96, 64, 5, 6, 2),       # 6 tokens: split routed chunks and two shared chunks
+    (5, 128, 96, 4, 8, 4),      # 8 tokens: every expert and the shared one in two chunks
 ])
 def test_shared_small_shapes(E, d, f, k, n, bits):
     w, host, sh, lg, x = _case(E, d, f, k, n, bits, seed=3)
