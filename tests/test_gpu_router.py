@@ -97,6 +97,24 @@ def test_router_stages_match_one_call():
     assert torch.equal(res_a, res_b)
 
 
+def test_router_separate_down_and_combine_stages():
+    # projected logits, then down and combine as separate stages: the expert-major down
+    # builds its work list from the grouping the gate/up stage wrote; same result as the
+    # single call up to the combine's summation order
+    w, host, layer, x = _small_layer(64, 256, 128, 6, 4, 4, seed=10)
+    x_d = to_dev(x)
+    ws = qmoe.workspace(layer, w.n)
+    res_a = x_d.clone()
+    r_a = qmoe.layer_decode(layer, None, x_d, res_a, ws=ws)
+    res_b = x_d.clone()
+    r_b = qmoe.Routing.empty(w.n, w.E, w.k)
+    for st in (qmoe.DECODE_PREP, qmoe.DECODE_GATE_UP, qmoe.DECODE_DOWN, qmoe.DECODE_COMBINE):
+        qmoe.layer_decode(layer, None, x_d, res_b, routing=r_b, ws=ws, stages=st)
+    torch.cuda.synchronize()
+    assert torch.equal(r_a.topk_ids, r_b.topk_ids)
+    np.testing.assert_allclose(res_b.cpu().numpy(), res_a.cpu().numpy(), rtol=1e-6, atol=1e-7)
+
+
 def test_router_without_weights_needs_logits():
     w, host, layer, x = _small_layer(8, 64, 64, 2, 2, 4, seed=9)
     layer.router = None
