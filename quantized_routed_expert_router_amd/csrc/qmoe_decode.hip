@@ -437,16 +437,17 @@ __device__ __forceinline__ int quant_half_wave(float h, float& scale, int& sum) 
 // activation codes and scales are staged in LDS per group and read back with
 // half-wave-uniform addresses.
 //
-// Two shapes:
-// * ROWS = 16, 4 waves (the decode window, ahead of the token-major down): 40 KB of
-//   weights an item, five workgroups a CU, so the ~1000 items of a T=4 window run in one
-//   round; the 16 rows are half of an h block, so h leaves in fp32 and the down kernel
-//   quantizes it. (Reading the same bytes as 1056 workgroups of 40 KB instead of 528 of
-//   80 KB measured 10% faster in a plain read probe.)
-// * ROWS = 32 (the work-list path and the expert-major down): one item is exactly one
-//   32-row block of h, so the int8 quantization of h closes inside the workgroup. Four
-//   waves (three workgroups a CU, 16 blocks a lane) serve the batched work list, whose
-//   thousands of items run in many rounds: 4-8% faster there than eight waves.
+// Shapes:
+// * ROWS = 16, 4 waves (windows of up to 16 tokens, ahead of the token-major down): 40 KB
+//   of weights an item, five workgroups a CU (4-pair chunks), so the ~1000 items of a T=4
+//   window run in one round; the 16 rows are half of an h block, so h leaves in fp32 and
+//   the down kernel quantizes it. (Reading the same bytes as 1056 workgroups of 40 KB
+//   instead of 528 of 80 KB measured 10% faster in a plain read probe.)
+// * ROWS = 32 (ahead of the expert-major down): one item is exactly one 32-row block of
+//   h, so the int8 quantization of h closes inside the workgroup. Four waves (three
+//   workgroups a CU, 16 blocks a lane) serve the batched work list, whose thousands of
+//   items run in many rounds: 4-8% faster there than eight waves, which serve the ids
+//   path of windows too wide for the token-major down.
 constexpr int kGuRows = 32;   // rows of an h block
 constexpr int kGuGroup = 64;  // blocks per group
 template <int WAVES, int ROWS>
