@@ -52,6 +52,25 @@ def test_route_matches_stable_sort():
         assert np.all(np.diff(w, axis=1) <= 0)  # slot 0 the largest
 
 
+def test_route_weights_exact_binary64():
+    # the weights are one rounding of binary64 arithmetic: exponentials of l_j - l_0 (exact
+    # differences of binary32 logits), summed in slot order, divided, rounded to binary32
+    rng = np.random.default_rng(21)
+    for n, E, k in [(40, 512, 10), (30, 64, 8), (20, 16, 16), (25, 300, 3)]:
+        lg = (rng.standard_normal((n, E)) * rng.uniform(0.1, 6.0, (n, 1))).astype(np.float32)
+        ids, w = O.route(lg, k)
+        ref = np.argsort(-lg, axis=1, kind="stable")[:, :k]
+        assert np.array_equal(ids, ref)
+        sel = np.take_along_axis(lg, ref, axis=1).astype(np.float64)
+        ex = np.exp(sel - sel[:, :1])
+        for t in range(n):
+            tot = 0.0
+            for j in range(k):  # slot order, one binary64 add at a time
+                tot += float(ex[t, j])
+            ref_w = (ex[t] / tot).astype(np.float32)
+            np.testing.assert_array_max_ulp(w[t], ref_w, maxulp=0)
+
+
 def test_route_ties_and_signed_zero():
     with open(os.path.join(GOLDEN, "route_ties.json")) as fh:
         cases = json.load(fh)["cases"]
@@ -142,6 +161,48 @@ def test_quant_hand_cases():
         q, s = O.quant_act(x)
         assert q.tolist() == c["q"], c["name"]
         assert float(s[0]) == np.float32(c["scale"]), c["name"]
+
+
+def test_quant_rule_separating_cases():
+    # blocks whose codes under the stated rule (x times the correctly rounded binary32
+    # reciprocal 127/amax, rounded half to even) differ from those of x/scale, of exact
+    # rounding and of (x*127)/amax; expected codes derived with exact rational arithmetic
+    # by tests/golden/make_quant_rule_cases.py
+    with open(os.path.join(GOLDEN, "quant_rule_cases.json")) as fh:
+        cases = json.load(fh)["cases"]
+    assert len(cases) >= 4
+    for c in cases:
+        x = np.array(c["x"], np.float32)
+        amax = np.float32(np.abs(x).max())
+        # the stored reciprocal is IEEE binary32 division, as numpy performs it
+        assert np.float32(127) / amax == np.float32(c["inv_f32"]), c["name"]
+        assert amax / np.float32(127) == np.float32(c["scale"]), c["name"]
+        q, s = O.quant_act(x)
+        assert q.tolist() == c["q"], c["name"]
+        assert float(s[0]) == np.float32(c["scale"]), c["name"]
+        # each block tells the rule apart from x/scale
+        assert q.tolist() != c["q_div"], c["name"]
+    both = [c for c in cases if c["q"] != c["q_exact"] and c["q"] != c["q_mul127"]]
+    assert both, "some block separates the rule from exact rounding and (x*127)/amax"
+
+
+def test_planted_h_layer_reproduces_rule_cases():
+    # the layer used to put the rule cases through the GPU's h quantizers: its SwiGLU
+    # output is exactly the stored values, and the oracle's h codes are the stored codes
+    from quant_rule_layer import expected_h, planted_layer, planted_x
+
+    E, d, f, k, n = 3, 64, 128, 1, 2
+    for bits in (4, 2):
+        g, u, dn = planted_layer(E, d, f, bits)
+        x = planted_x(n, d)
+        ids = np.array([[0], [2]], np.int32)
+        w = np.ones((n, k), np.float32)
+        _, tr = O.ffn_decode(_M(g), _M(u), _M(dn), E, x, ids, w, x, trace=True)
+        h_ref, q_ref, s_ref = expected_h(f)
+        assert np.array_equal(tr["g"], np.full((n * k, f), 64.0))
+        assert np.array_equal(tr["h"], np.broadcast_to(h_ref, (n * k, f)))
+        assert np.array_equal(tr["hq"], np.broadcast_to(q_ref, (n * k, f)))
+        assert np.array_equal(tr["hs"], np.broadcast_to(s_ref, (n * k, f // 32)))
 
 
 def test_quant_properties():
@@ -436,6 +497,31 @@ def test_prefill_layer_vs_dense_bruteforce():
     y = tr["y"].reshape(n, k, d)
     ref_out = res.astype(np.float64) + np.einsum("tj,tjc->tc", w.astype(np.float64), y)
     np.testing.assert_array_max_ulp(out, ref_out.astype(np.float32), maxulp=1)
+
+
+def _bf16_rne_bits(v32: np.ndarray) -> np.ndarray:
+    """binary32 -> bfloat16 bits, round to nearest even (finite inputs)."""
+    u = np.asarray(v32, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_prefill_h_rounding_exact():
+    # h is bf16(fp32(silu(g) * u)) of the binary64 g and u: two roundings, binary64 to
+    # binary32 and binary32 to bfloat16 (half to even), both checked bit for bit
+    E, d, f, k, n = 6, 128, 96, 3, 9
+    g, u, dn = _layer(E, d, f, 2, seed=19)
+    rng = np.random.default_rng(19)
+    xb = synth.to_bf16_bits((rng.standard_normal((n, d)) * 4).astype(np.float32))
+    res = rng.standard_normal((n, d)).astype(np.float32)
+    ids, w = O.route(rng.standard_normal((n, E)).astype(np.float32), k)
+    _, tr = O.ffn_prefill(_M(g), _M(u), _M(dn), E, xb, ids, w, res, trace=True)
+    G, U = tr["g"], tr["u"]
+    silu = G / (1.0 + np.exp(-G))
+    h32 = (silu * U).astype(np.float32)
+    assert np.array_equal(tr["hb"], _bf16_rne_bits(h32))
+    # and the rounding is to nearest: truncation would differ on about half the values
+    trunc = (h32.view(np.uint32) >> 16).astype(np.uint16)
+    assert (trunc != tr["hb"]).mean() > 0.2
 
 
 # ------------------------------------------------------------------ byte accounting
