@@ -434,12 +434,21 @@ int orc_ffn_prefill(const orc_matrix* gate, const orc_matrix* up, const orc_matr
     const int e = ids[(size_t)t * k + j];
     const uint16_t* xt = x_bf16 + (size_t)t * d;
     uint16_t* hb = (uint16_t*)malloc(sizeof(uint16_t) * (size_t)f);
+    /* each weight is bf16(fp32(s*q + m)) as orc_weight_bf16 computes it; the block's
+     * scale and min are read once per 32 columns instead of once per column */
     for (int r = 0; r < f; ++r) {
       double g = 0.0, u = 0.0;
-      for (int c = 0; c < d; ++c) {
-        const double xv = bf16_to_double(xt[c]);
-        g += bf16_to_double(orc_weight_bf16(gate, e, r, c)) * xv;
-        u += bf16_to_double(orc_weight_bf16(up, e, r, c)) * xv;
+      for (int b = 0; b < d / 32; ++b) {
+        const float gs = (float)orc_scale(gate, e, r, b), gm = (float)orc_min(gate, e, r, b);
+        const float us = (float)orc_scale(up, e, r, b), um = (float)orc_min(up, e, r, b);
+        for (int i = 0; i < 32; ++i) {
+          const int c = 32 * b + i;
+          const double xv = bf16_to_double(xt[c]);
+          const float gw = gs * (float)orc_code(gate, e, r, c) + gm;
+          const float uw = us * (float)orc_code(up, e, r, c) + um;
+          g += bf16_to_double(bf16_rne(gw)) * xv;
+          u += bf16_to_double(bf16_rne(uw)) * xv;
+        }
       }
       const double silu = g / (1.0 + exp(-g));
       hb[r] = bf16_rne((float)(silu * u));
@@ -449,8 +458,14 @@ int orc_ffn_prefill(const orc_matrix* gate, const orc_matrix* up, const orc_matr
     }
     for (int c = 0; c < d; ++c) {
       double acc = 0.0;
-      for (int r = 0; r < f; ++r)
-        acc += bf16_to_double(orc_weight_bf16(down, e, c, r)) * bf16_to_double(hb[r]);
+      for (int b = 0; b < f / 32; ++b) {
+        const float ds = (float)orc_scale(down, e, c, b), dm = (float)orc_min(down, e, c, b);
+        for (int i = 0; i < 32; ++i) {
+          const int r = 32 * b + i;
+          const float dw = ds * (float)orc_code(down, e, c, r) + dm;
+          acc += bf16_to_double(bf16_rne(dw)) * bf16_to_double(hb[r]);
+        }
+      }
       y[(size_t)p * d + c] = acc;
       if (tr_y) tr_y[(size_t)p * d + c] = acc;
     }
