@@ -220,10 +220,11 @@ moe_status moe_layer_decode(const moe_layer* L, const float* logits, const float
                             size_t ws_bytes, const moe_debug* dbg, void* stream);
 
 /* moe_layer_decode split into stages like moe_expert_ffn_decode_stages; here
- * MOE_DECODE_PREP also performs the routing. For windows of n <= 8 tokens with n*k <= 64
+ * MOE_DECODE_PREP also performs the routing. For windows of n <= 16 tokens with n*k <= 64
  * pairs the expert pass takes its chunks straight from the expert ids: PREP then writes
  * r's topk_ids and topk_w, and MOE_DECODE_GATE_UP writes r's expert_offsets and
- * pair_index; r is complete once both stages have run (always, after the whole call). */
+ * pair_index; r is complete once both stages have run (always, after the whole call).
+ * Larger windows write all of r in PREP. */
 moe_status moe_layer_decode_stages(const moe_layer* L, const float* logits, const float* x,
                                    int n_tokens, const moe_routing* r, float* residual, void* ws,
                                    size_t ws_bytes, const moe_debug* dbg, unsigned stages,

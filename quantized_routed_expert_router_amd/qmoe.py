@@ -102,6 +102,45 @@ def _ptr(t) -> int | None:
     return None if t is None else t.data_ptr()
 
 
+class _Args:
+    """Checks of the tensors of one call before their pointers go to the library: first
+    each tensor's dtype, layout and extent (need), then that all of them sit on one GPU
+    (on_gpu). Raises ValueError."""
+
+    def __init__(self):
+        self.seen = []
+
+    def need(self, t, name: str, dtypes, shape=None, min_numel=None):
+        if not isinstance(t, torch.Tensor):
+            raise ValueError(f"{name}: expected a torch.Tensor, got {type(t).__name__}")
+        if t.dtype not in dtypes:
+            raise ValueError(f"{name}: dtype {t.dtype}, expected one of {dtypes}")
+        if not t.is_contiguous():
+            raise ValueError(f"{name}: must be contiguous")
+        if shape is not None and tuple(t.shape) != tuple(shape):
+            raise ValueError(f"{name}: shape {tuple(t.shape)}, expected {tuple(shape)}")
+        if min_numel is not None and t.numel() < min_numel:
+            raise ValueError(f"{name}: {t.numel()} elements, at least {min_numel} needed")
+        self.seen.append((name, t))
+
+    def on_gpu(self):
+        dev = None
+        for name, t in self.seen:
+            if not t.is_cuda:
+                raise ValueError(f"{name}: must be a GPU tensor (got device {t.device})")
+            if dev is None:
+                dev = t.device
+            elif t.device != dev:
+                raise ValueError(f"{name}: on {t.device}, the other arguments on {dev}")
+
+
+F32 = (torch.float32,)
+I32 = (torch.int32,)
+TWO_BYTE = (torch.int16, torch.bfloat16, torch.float16, torch.uint16)
+WORDS = (torch.int32, torch.uint32)
+BYTES = (torch.uint8, torch.int8)
+
+
 def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -122,6 +161,15 @@ class QMatrix:
     rows: int
     cols: int
     bits: int
+
+    def check(self, E: int, name: str, args: "_Args") -> None:
+        """Extents of E experts' codes and scale/min words (see the class docstring)."""
+        if self.bits not in (2, 4) or self.cols % 32 or self.rows <= 0:
+            raise ValueError(f"{name}: bad shape rows={self.rows} cols={self.cols} "
+                             f"bits={self.bits}")
+        blocks = E * (self.cols // 32) * self.rows
+        args.need(self.codes, f"{name}.codes", WORDS, min_numel=blocks * self.bits)
+        args.need(self.scale_min, f"{name}.scale_min", TWO_BYTE, min_numel=blocks * 2)
 
     def _struct(self) -> _QMatrix:
         return _QMatrix(self.codes.data_ptr(), self.scale_min.data_ptr(), self.rows, self.cols,
@@ -154,6 +202,26 @@ class Layer:
         return _Layer(self.d_model, self.d_ff, self.n_experts, self.top_k, self.gate._struct(),
                       self.up._struct(), self.down._struct(), *sh, rw)
 
+    def check(self, args: "_Args") -> None:
+        """Every matrix holds n_experts experts (the shared ones one) of the layer's shape;
+        the router rows are [n_experts, d_model] two-byte values."""
+        d, f = self.d_model, self.d_ff
+        for name, m, rows, cols, E in (("gate", self.gate, f, d, self.n_experts),
+                                        ("up", self.up, f, d, self.n_experts),
+                                        ("down", self.down, d, f, self.n_experts)):
+            if (m.rows, m.cols) != (rows, cols):
+                raise ValueError(f"{name}: {m.rows}x{m.cols}, expected {rows}x{cols}")
+            m.check(E, name, args)
+        if self.shared:
+            for name, m, rows, cols in (("shared_gate", self.shared[0], f, d),
+                                        ("shared_up", self.shared[1], f, d),
+                                        ("shared_down", self.shared[2], d, f)):
+                if (m.rows, m.cols) != (rows, cols):
+                    raise ValueError(f"{name}: {m.rows}x{m.cols}, expected {rows}x{cols}")
+                m.check(1, name, args)
+        if self.router is not None:
+            args.need(self.router, "router", TWO_BYTE, shape=(self.n_experts, d))
+
     def pairs(self, n: int) -> int:
         """Pair slots of an n-token window: n*k routed, plus n shared (pair n*k + t)."""
         return n * self.top_k + (n if self.shared else 0)
@@ -173,6 +241,12 @@ class Routing:
                        torch.empty(E + 1, dtype=torch.int32, device=device),
                        torch.empty(max(n * k, 1), dtype=torch.int32, device=device))
 
+    def check(self, n: int, E: int, k: int, args: "_Args") -> None:
+        args.need(self.topk_ids, "topk_ids", I32, min_numel=n * k)
+        args.need(self.topk_w, "topk_w", F32, min_numel=n * k)
+        args.need(self.expert_offsets, "expert_offsets", I32, min_numel=E + 1)
+        args.need(self.pair_index, "pair_index", I32, min_numel=n * k)
+
     def _struct(self) -> _Routing:
         return _Routing(self.topk_ids.data_ptr(), self.topk_w.data_ptr(),
                         self.expert_offsets.data_ptr(), self.pair_index.data_ptr())
@@ -186,11 +260,19 @@ def route_workspace(n: int, E: int, top_k: int, device="cuda") -> torch.Tensor |
 def route(logits: torch.Tensor, top_k: int, out: Routing | None = None, stream=None,
           ws: torch.Tensor | None = None) -> Routing:
     """moe_route: top-k experts, routing weights and expert grouping of `logits` [n, E]."""
+    if logits.dim() != 2:
+        raise ValueError(f"logits: expected [n, E], got shape {tuple(logits.shape)}")
     n, E = logits.shape
+    args = _Args()
+    args.need(logits, "logits", F32)
     if out is None:
         out = Routing.empty(n, E, top_k, logits.device)
     if ws is None:
         ws = route_workspace(n, E, top_k, logits.device)
+    out.check(n, E, top_k, args)
+    if ws is not None:
+        args.need(ws, "ws", BYTES)
+    args.on_gpu()
     st = out._struct()
     rc = lib.moe_route(_ptr(logits), n, E, top_k, ctypes.byref(st), _ptr(ws),
                        0 if ws is None else ws.numel(), _stream(stream))
@@ -221,12 +303,41 @@ def debug_buffers(layer: Layer, n: int, device="cuda") -> dict:
                 logits=z((n, layer.n_experts), torch.float32) if layer.router is not None else None)
 
 
+def _check_decode_args(layer: Layer, x, residual, routing: Routing, logits, ws, debug) -> int:
+    """Checks of a decode call's tensors; returns the token count."""
+    args = _Args()
+    layer.check(args)
+    if not isinstance(x, torch.Tensor) or x.dim() != 2:
+        raise ValueError(f"x: expected [n, d_model], got {getattr(x, 'shape', type(x))}")
+    n = x.shape[0]
+    args.need(x, "x", F32, shape=(n, layer.d_model))
+    args.need(residual, "residual", F32, shape=(n, layer.d_model))
+    if logits is not None:
+        args.need(logits, "logits", F32, shape=(n, layer.n_experts))
+    routing.check(n, layer.n_experts, layer.top_k, args)
+    if ws is not None:
+        args.need(ws, "ws", BYTES)
+    if debug is not None:
+        # each debug buffer given holds at least what debug_buffers allocates
+        ref = debug_buffers(layer, n, device="meta")
+        for key, t in debug.items():
+            if key not in DEBUG_FIELDS:
+                raise ValueError(f"debug: unknown buffer {key!r}")
+            if t is None:
+                continue
+            if ref[key] is None:
+                raise ValueError(f"debug[{key!r}]: this layer writes no such buffer")
+            args.need(t, f"debug[{key!r}]", (ref[key].dtype,), min_numel=ref[key].numel())
+    args.on_gpu()
+    return n
+
+
 def ffn_decode(layer: Layer, x: torch.Tensor, routing: Routing, residual: torch.Tensor,
                ws: torch.Tensor | None = None, debug: dict | None = None, stream=None,
                stages: int | None = None) -> None:
     """moe_expert_ffn_decode: residual += routing-weighted expert outputs (in place).
     With `stages` (DECODE_* bits) the call goes through moe_expert_ffn_decode_stages."""
-    n = x.shape[0]
+    n = _check_decode_args(layer, x, residual, routing, None, ws, debug)
     if ws is None:
         ws = workspace(layer, n, device=x.device)
     st, rs = layer._struct(), routing._struct()
@@ -255,6 +366,7 @@ def layer_decode(layer: Layer, logits: torch.Tensor | None, x: torch.Tensor,
     n = x.shape[0]
     if routing is None:
         routing = Routing.empty(n, layer.n_experts, layer.top_k, x.device)
+    _check_decode_args(layer, x, residual, routing, logits, ws, debug)
     if ws is None:
         ws = workspace(layer, n, device=x.device)
     st, rs = layer._struct(), routing._struct()
@@ -281,6 +393,14 @@ def ffn_prefill(layer: Layer, x_bf16: torch.Tensor, routing: Routing, residual: 
     x_bf16 holds bf16 bit patterns (any 2-byte dtype). With `stages` (PREFILL_* bits) the
     call goes through moe_expert_ffn_prefill_stages."""
     n = x_bf16.shape[0]
+    args = _Args()
+    layer.check(args)
+    args.need(x_bf16, "x_bf16", TWO_BYTE, shape=(n, layer.d_model))
+    args.need(residual, "residual", F32, shape=(n, layer.d_model))
+    routing.check(n, layer.n_experts, layer.top_k, args)
+    if ws is not None:
+        args.need(ws, "ws", BYTES)
+    args.on_gpu()
     if ws is None:
         ws = workspace(layer, n, prefill=True, device=x_bf16.device)
     st, rs = layer._struct(), routing._struct()

@@ -262,6 +262,37 @@ def test_decode_config2_t4_full_trace(cfg2_layer):
     _decode_parity(w, host, lg, x, layer=layer)
 
 
+@pytest.mark.parametrize("T", [4, 5])
+def test_decode_config2_outlier_blocks(cfg2_layer, T):
+    # the benchmarked call (moe_layer_decode, no debug buffers) on activation blocks with
+    # outliers: one value 100x the rest, a single non-zero value, all-zero blocks, a
+    # value 1000x, and (last token) an all-zero token, whose MoE update must be exactly 0
+    w, layer = cfg2_layer
+    w = synth.Workload(w.name, w.d, w.f, w.E, w.k, T, w.bits, w.logits)
+    lg, x = synth.layer_inputs(w, 40 + T)
+    x[0, 3 * 32 + 7] *= 100.0
+    x[0, 9 * 32:10 * 32] = 0.0
+    x[0, 9 * 32 + 31] = -2.5
+    x[1, 5 * 32:6 * 32] = 0.0
+    x[1, 17 * 32:19 * 32] = 0.0
+    x[1, 40 * 32 + 1] = 1000.0
+    x[2, ::32] *= 50.0                   # a spike at the start of every block
+    x[2, 31::32] = 0.0
+    x[T - 1, :] = 0.0                     # an all-zero token
+    res_in = synth.activations(0, 41, T, w.d)
+    res = to_dev(res_in)
+    r = qmoe.layer_decode(layer, to_dev(lg), to_dev(x), res)
+    torch.cuda.synchronize()
+    ids, wt = check_routing(lg, w.k, r)
+    host = synth.host_layer(synth.config(2), 0, experts=np.unique(ids))
+    out_o, _ = O.ffn_decode(*(omat(h) for h in host), w.E, x, ids, wt, res_in)
+    out = res.cpu().numpy()
+    assert_output_tolerance(out, out_o)
+    assert_output_tolerance(out - res_in, out_o - res_in, what="moe delta")
+    assert np.array_equal(out[T - 1], res_in[T - 1]), "an all-zero token adds exactly 0"
+    assert np.array_equal(out_o[T - 1], res_in[T - 1])
+
+
 @pytest.mark.parametrize("T", [1, 2, 3, 5])
 def test_decode_config2_window_sizes(cfg2_layer, T):
     w, layer = cfg2_layer
@@ -280,11 +311,11 @@ def test_decode_max_tokens_sampled(cfg2_layer):
     x = synth.activations(0, 21, n, w.d)
     routing, out, _ = run_decode(layer, lg, x, w.k)
     ids, wt = check_routing(lg, w.k, routing)
-    tokens = np.array([0, 1, 77, 255, 256, 400, 510, 511], np.int32)
-    host = synth.host_layer(synth.config(2), 0, experts=np.unique(ids[tokens]))
-    out_o, _ = O.ffn_decode(*(omat(h) for h in host), w.E, x, ids, wt, x, tokens=tokens)
-    assert_output_tolerance(out[tokens], out_o)
-    assert_output_tolerance(out[tokens] - x[tokens], out_o - x[tokens], what="moe delta")
+    # every token against the oracle (a few seconds of oracle time)
+    host = synth.host_layer(synth.config(2), 0, experts=np.unique(ids))
+    out_o, _ = O.ffn_decode(*(omat(h) for h in host), w.E, x, ids, wt, x)
+    assert_output_tolerance(out, out_o)
+    assert_output_tolerance(out - x, out_o - x, what="moe delta")
 
 
 @pytest.mark.parametrize("bits,T", [(4, 4), (2, 4), (4, 1)])
@@ -300,6 +331,26 @@ def test_decode_pruned_256_experts(bits, T):
     device_layer_matches_host(layer, host, experts[::5], w.E)
     _decode_parity(w, host, lg, x, layer=layer, dots=(bits == 4 and T == 4))
     out, _ = _layer_vs_two_calls(w, layer, lg, x)
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_decode_config3_timed_instances_all_tokens(T):
+    # the call the benchmark times: moe_layer_decode without debug buffers (the fast
+    # kernel instances), all 64*T tokens of the batch against the oracle
+    w = synth.config(3, T)
+    layer = workloads.device_layer(w, 1)
+    lg, x = synth.layer_inputs(w, 1)
+    res = to_dev(x)
+    r = qmoe.layer_decode(layer, to_dev(lg), to_dev(x), res)
+    torch.cuda.synchronize()
+    ids, wt = check_routing(lg, w.k, r)
+    host = synth.host_layer(w, 1, experts=np.unique(ids))
+    out_o, _ = O.ffn_decode(*(omat(h) for h in host), w.E, x, ids, wt, x)
+    out = res.cpu().numpy()
+    assert_output_tolerance(out, out_o)
+    assert_output_tolerance(out - x, out_o - x, what="moe delta")
+    # the work list covers every touched expert: most of the 512 at this batch size
+    assert len(np.unique(ids)) > (300 if T == 1 else 480)
 
 
 @pytest.mark.parametrize("T", [1, 4])
@@ -446,6 +497,40 @@ def test_decode_down_grid_past_one_round(E, d, f, k, n, bits):
     # quantizes h before requesting its weights (fewer registers: two workgroups a CU)
     w, host, lg, x = _small(E, d, f, k, n, bits, seed=13)
     _decode_parity(w, host, lg, x)
+
+
+@pytest.mark.parametrize("n,k", [(16, 4), (12, 5), (9, 7)])
+def test_layer_decode_stages_ids_path_up_to_16_tokens(n, k):
+    # windows of 9..16 tokens with n*k <= 64 pairs take their chunks from the expert ids
+    # (8-pair chunks): PREP writes the ids and weights, GATE_UP the grouping. Expert 5 is
+    # in every token, so it holds n > 8 pairs and is split over two chunks.
+    E, d, f, bits = 32, 256, 128, 4
+    w, host, lg, x = _small(E, d, f, k, n, bits, seed=23)
+    lg[:, 5] = 10.0
+    layer = workloads.layer_from_host(*host, w.k)
+    lg_d, x_d = to_dev(lg), to_dev(x)
+    ws = qmoe.workspace(layer, n)
+    res = x_d.clone()
+    r = qmoe.Routing.empty(n, E, k, "cuda")
+    r.expert_offsets.fill_(-1)
+    r.pair_index.fill_(-1)
+    ids_o, wt_o = O.route(lg, k)
+    off_o, pidx_o = O.group(ids_o, E)
+    assert (ids_o == 5).sum() == n
+    qmoe.layer_decode(layer, lg_d, x_d, res, routing=r, ws=ws, stages=qmoe.DECODE_PREP)
+    torch.cuda.synchronize()
+    assert np.array_equal(r.topk_ids.cpu().numpy(), ids_o)
+    np.testing.assert_array_max_ulp(r.topk_w.cpu().numpy(), wt_o, maxulp=1)
+    qmoe.layer_decode(layer, lg_d, x_d, res, routing=r, ws=ws, stages=qmoe.DECODE_GATE_UP)
+    torch.cuda.synchronize()
+    assert np.array_equal(r.expert_offsets.cpu().numpy(), off_o)
+    assert np.array_equal(r.pair_index.cpu().numpy()[: n * k], pidx_o)
+    qmoe.layer_decode(layer, lg_d, x_d, res, routing=r, ws=ws,
+                      stages=qmoe.DECODE_DOWN | qmoe.DECODE_COMBINE)
+    torch.cuda.synchronize()
+    out_o, _ = O.ffn_decode(*(omat(h) for h in host), E, x, ids_o, wt_o, x)
+    assert_output_tolerance(res.cpu().numpy(), out_o)
+    assert_output_tolerance(res.cpu().numpy() - x, out_o - x, what="moe delta")
 
 
 @pytest.mark.parametrize("E,d,f,k,n,bits", [

@@ -133,12 +133,32 @@ def test_prefill_config5_routing(cfg5):
     assert counts.max() > 8 * counts.mean()  # Zipf: ragged per-expert row counts
 
 
-def test_prefill_config5_sampled_tokens(cfg5):
-    # full chunk (8192 tokens, 81,920 pairs) on the GPU; oracle on a token sample that
-    # covers the first, last and interior tokens
+PREFILL_TILE_ROWS = 256  # grouped pairs of one expert per M-tile of the prefill GEMMs
+
+
+def mtile_edge_tokens(offsets: np.ndarray, pair_index: np.ndarray, k: int, rows: int):
+    """Tokens holding the first and the last grouped row of every M-tile (runs of `rows`
+    consecutive grouped pairs of one expert), and the number of tiles."""
+    toks, ntiles = set(), 0
+    for e in range(len(offsets) - 1):
+        for s in range(int(offsets[e]), int(offsets[e + 1]), rows):
+            t_end = min(s + rows, int(offsets[e + 1])) - 1
+            toks.add(int(pair_index[s]) // k)
+            toks.add(int(pair_index[t_end]) // k)
+            ntiles += 1
+    return np.array(sorted(toks), np.int32), ntiles
+
+
+def test_prefill_config5_every_mtile(cfg5):
+    # full chunk (8192 tokens, 81,920 pairs) on the GPU; the oracle on every token that
+    # holds the first or the last grouped row of an M-tile, so every tile of every expert
+    # (and every column tile of those rows) is compared
     w, lg, _, routing, out, xb, res = cfg5
     ids, wt = O.route(lg, w.k)
-    tokens = np.array([0, 1, 2, 1000, 4095, 4096, 7777, 8191], np.int32)
+    off, pidx = O.group(ids, w.E)
+    tokens, ntiles = mtile_edge_tokens(off, pidx, w.k, PREFILL_TILE_ROWS)
+    print(f"{ntiles} M-tiles, {len(tokens)} tokens compared")
+    assert ntiles > 300 and len(tokens) > 500
     host = synth.host_layer(w, 0, experts=np.unique(ids[tokens]))
     out_o, _ = O.ffn_prefill(*(omat(h) for h in host), w.E, xb, ids, wt, res, tokens=tokens)
     _check(out, out_o, res, tokens)
