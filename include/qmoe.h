@@ -230,6 +230,26 @@ moe_status moe_layer_decode_stages(const moe_layer* L, const float* logits, cons
                                    size_t ws_bytes, const moe_debug* dbg, unsigned stages,
                                    void* stream);
 
+/* Bytes of the library's own decode workspace, used by moe_layer_decode_noalloc: one
+ * array of this size per GPU the library runs on, held until the process ends. */
+#define MOE_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+/* moe_layer_decode without a workspace argument, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation). The workspace is the library's static per-GPU array of
+ * MOE_NOALLOC_SCRATCH_BYTES bytes (enough for windows of 64 tokens at d_model = 2048,
+ * d_ff = 768, top-10 with a shared expert and router weights); nothing is allocated or
+ * freed by the call. Arguments, results and errors as moe_layer_decode (dbg = NULL),
+ * plus MOE_ERR_WORKSPACE_TOO_SMALL when the sizes need more workspace than the array
+ * holds (nothing is enqueued), and MOE_ERR_HIP if the array's device address cannot be
+ * resolved. Every call on one GPU uses that GPU's one array, which keeps the last call's
+ * contents (the decode path needs no initialised workspace): calls that overlap on one
+ * GPU (on different streams, or from different host threads without ordering) race;
+ * calls on one stream are ordered and safe. */
+moe_status moe_layer_decode_noalloc(const moe_layer* L, const float* logits, const float* x,
+                                    int n_tokens, const moe_routing* r, float* residual,
+                                    void* stream);
+
 /* Prefill-chunk expert FFN with bf16 arithmetic on the matrix cores: weights are
  * dequantized to bf16 (bf16 of fp32 scale*q + min), x_bf16: device bf16 bits [n][d];
  * gate/up accumulate in fp32; h = bf16(silu(g) * u); down accumulates in fp32;

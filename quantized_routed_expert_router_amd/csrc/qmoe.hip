@@ -6,6 +6,12 @@
 
 #include "qmoe_internal.h"
 
+// Workspace of moe_layer_decode_noalloc: one array per GPU, held by the library's code
+// object until the process ends. In host code the name is only a stand-in for the
+// symbol: the device address comes from hipGetSymbolAddress, per device (scratch_address
+// below), and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
 namespace qmoe {
 
 int device_cu_count() {
@@ -26,6 +32,23 @@ int device_cu_count() {
 }
 
 namespace {
+
+// Device address of this GPU's scratch array, resolved once per device with that device
+// current. Returns nullptr if the runtime cannot resolve it.
+void* scratch_address() {
+  static std::mutex mu;
+  static std::vector<void*> cache;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return nullptr;
+  std::lock_guard<std::mutex> lock(mu);
+  if ((int)cache.size() <= dev) cache.resize(dev + 1, nullptr);
+  if (!cache[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    cache[dev] = ptr;
+  }
+  return cache[dev];
+}
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -216,6 +239,27 @@ moe_status moe_layer_decode_stages(const moe_layer* L, const float* logits, cons
   }
   return decode_entry(L, logits, project, x, n_tokens, r, residual, ws, ws_bytes, dbg, stages,
                       stream);
+}
+
+moe_status moe_layer_decode_noalloc(const moe_layer* L, const float* logits, const float* x,
+                                    int n_tokens, const moe_routing* r, float* residual,
+                                    void* stream) {
+  const bool project = !logits && L && L->router_w;
+  if (n_tokens > 0 && !logits && !project) return MOE_ERR_INVALID_ARGUMENT;
+  if (n_tokens == 0)
+    return moe_layer_decode_stages(L, logits, x, 0, r, residual, nullptr, 0, nullptr,
+                                   MOE_DECODE_ALL, stream);
+  moe_status s = check_layer(L);
+  if (s != MOE_OK) return s;
+  if (n_tokens < 0 || n_tokens > MOE_MAX_DECODE_TOKENS) return MOE_ERR_INVALID_ARGUMENT;
+  const size_t need = decode_ws_layout(n_tokens, L->top_k, L->d_model, L->d_ff, has_shared(*L),
+                                       L->router_w ? L->n_experts : 0)
+                          .total;
+  if (need > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE_TOO_SMALL;
+  void* ws = scratch_address();
+  if (!ws) return MOE_ERR_HIP;
+  return decode_entry(L, logits, project, x, n_tokens, r, residual, ws,
+                      (size_t)MOE_NOALLOC_SCRATCH_BYTES, nullptr, MOE_DECODE_ALL, stream);
 }
 
 moe_status moe_expert_ffn_prefill(const moe_layer* L, const uint16_t* x_bf16, int n_tokens,

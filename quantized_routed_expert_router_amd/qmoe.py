@@ -26,8 +26,10 @@ MAX_PREFILL_TOKENS = 8192
 
 EXPORTS = ("moe_status_string", "moe_route_workspace_bytes", "moe_route",
            "moe_ffn_workspace_bytes", "moe_expert_ffn_decode", "moe_expert_ffn_decode_stages",
-           "moe_layer_decode", "moe_layer_decode_stages", "moe_expert_ffn_prefill",
-           "moe_expert_ffn_prefill_stages")
+           "moe_layer_decode", "moe_layer_decode_stages", "moe_layer_decode_noalloc",
+           "moe_expert_ffn_prefill", "moe_expert_ffn_prefill_stages")
+
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 DECODE_PREP, DECODE_GATE_UP, DECODE_DOWN, DECODE_COMBINE, DECODE_ALL = 1, 2, 4, 8, 15
 PREFILL_PREP, PREFILL_GATE_UP, PREFILL_DOWN, PREFILL_COMBINE, PREFILL_ALL = 1, 2, 4, 8, 15
@@ -88,6 +90,8 @@ def _load():
     L.moe_layer_decode_stages.argtypes = [
         ctypes.POINTER(_Layer), vp, vp, i32, ctypes.POINTER(_Routing), vp, vp, sz,
         ctypes.POINTER(_Debug), ctypes.c_uint, vp]
+    L.moe_layer_decode_noalloc.argtypes = [ctypes.POINTER(_Layer), vp, vp, i32,
+                                           ctypes.POINTER(_Routing), vp, vp]
     L.moe_expert_ffn_prefill.argtypes = [ctypes.POINTER(_Layer), vp, i32, ctypes.POINTER(_Routing),
                                          vp, vp, sz, vp]
     L.moe_expert_ffn_prefill_stages.argtypes = [
@@ -384,6 +388,20 @@ def layer_decode(layer: Layer, logits: torch.Tensor | None, x: torch.Tensor,
         fn = "moe_layer_decode_stages"
     if rc != MOE_OK:
         raise MoeError(fn, rc)
+    return routing
+
+
+def layer_decode_noalloc(layer: Layer, logits: torch.Tensor | None, x: torch.Tensor,
+                         residual: torch.Tensor, routing: Routing, stream=None) -> Routing:
+    """moe_layer_decode_noalloc: layer_decode on the library's own per-GPU workspace (no
+    workspace argument; the call allocates nothing). `routing` is written in place."""
+    n = x.shape[0]
+    _check_decode_args(layer, x, residual, routing, logits, None, None)
+    st, rs = layer._struct(), routing._struct()
+    rc = lib.moe_layer_decode_noalloc(ctypes.byref(st), _ptr(logits), _ptr(x), n,
+                                      ctypes.byref(rs), _ptr(residual), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError("moe_layer_decode_noalloc", rc)
     return routing
 
 

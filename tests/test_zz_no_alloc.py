@@ -1,0 +1,74 @@
+"""moe_layer_decode_noalloc (the decode layer on the library's own per-GPU workspace)
+against moe_layer_decode with a caller workspace: two calls in a row, the second with a
+smaller window, each bit for bit equal to the existing entry point and within the decode
+tolerance of the oracle; a window needing more workspace than the array is rejected on
+the host."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from quantized_routed_expert_router_amd import qmoe, synth, workloads
+
+from gpu_common import assert_output_tolerance, check_routing, omat, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _pair(layer, w, lg, x):
+    res_a = to_dev(x)
+    r_a = qmoe.layer_decode(layer, to_dev(lg), to_dev(x), res_a)
+    res_b = to_dev(x)
+    r_b = qmoe.Routing.empty(x.shape[0], w.E, w.k)
+    qmoe.layer_decode_noalloc(layer, to_dev(lg), to_dev(x), res_b, r_b)
+    torch.cuda.synchronize()
+    return res_a, r_a, res_b, r_b
+
+
+def test_noalloc_matches_layer_decode_two_calls():
+    w = synth.config(2)
+    layer = workloads.device_layer(w, 0)
+    for n, inst in ((5, 7), (2, 8)):  # the second call is smaller
+        ww = synth.Workload(w.name, w.d, w.f, w.E, w.k, n, w.bits, w.logits)
+        lg, x = synth.layer_inputs(ww, inst)
+        res_a, r_a, res_b, r_b = _pair(layer, ww, lg, x)
+        assert torch.equal(res_a, res_b), f"n={n}: residual differs from moe_layer_decode"
+        for name in ("topk_ids", "topk_w", "expert_offsets"):
+            assert torch.equal(getattr(r_a, name), getattr(r_b, name)), name
+        assert torch.equal(r_a.pair_index[: n * w.k], r_b.pair_index[: n * w.k])
+        ids, wt = check_routing(lg, w.k, r_b)
+        host = synth.host_layer(w, 0, experts=np.unique(ids))
+        out_o, _ = O.ffn_decode(*(omat(h) for h in host), w.E, x, ids, wt, x)
+        out = res_b.cpu().numpy()
+        assert_output_tolerance(out, out_o)
+        assert_output_tolerance(out - x, out_o - x, what="moe delta")
+
+
+def test_noalloc_larger_batch_then_small_window():
+    # a 64-token batch (work-list path, grouping in the routing kernel), then one token
+    w = synth.Workload("b64", 2048, 768, 512, 10, 64, 2, "uniform")
+    layer = workloads.device_layer(w, 2)
+    for n in (64, 1):
+        ww = synth.Workload(w.name, w.d, w.f, w.E, w.k, n, w.bits, w.logits)
+        lg, x = synth.layer_inputs(ww, 3 + n)
+        res_a, r_a, res_b, r_b = _pair(layer, ww, lg, x)
+        assert torch.equal(res_a, res_b), f"n={n}"
+        assert torch.equal(r_a.expert_offsets, r_b.expert_offsets)
+
+
+def test_noalloc_rejects_windows_beyond_its_workspace():
+    w = synth.config(2)
+    layer = workloads.device_layer(w, 0)
+    n = 128  # 25.7 MB of workspace at this shape: more than the array holds
+    assert qmoe.ffn_workspace_bytes(layer, n) > qmoe.NOALLOC_SCRATCH_BYTES
+    lg = torch.zeros((n, w.E), device="cuda")
+    x = torch.zeros((n, w.d), device="cuda")
+    res = torch.full((n, w.d), 3.0, device="cuda")
+    r = qmoe.Routing.empty(n, w.E, w.k)
+    with pytest.raises(qmoe.MoeError) as ei:
+        qmoe.layer_decode_noalloc(layer, lg, x, res, r)
+    assert ei.value.status == 3  # MOE_ERR_WORKSPACE_TOO_SMALL, nothing enqueued
+    torch.cuda.synchronize()
+    assert bool((res == 3.0).all())
