@@ -19,10 +19,16 @@ Reported:
                 8 TB/s HBM peak, its average duration taken from HIP events around a run
                 of that kernel alone, launched back to back over the rotating instances
                 (each replaying its own step's gate/up stage);
-  cpu_baseline  the CPU oracle on the host cores, on a bounded sample of the same steps.
+  step_us_percentiles  p10 / p50 / p90 of event-bracketed steps;
+  cpu_baseline  the CPU oracle on the host, on a bounded sample of the same steps: on all
+                physical cores the process may use (capped by OMP_NUM_THREADS), with the
+                single-thread rate and the core counts beside it;
+  supplementary (default run) the other configurations, each with its own roofline:
+                1 = the tiny layer; 3 = 2-bit, 64 sequences x T (T=1 and 4), uniform
+                logits; 4 = 48 chained layers, one decode step, eager and as one HIP
+                graph, with bytes per token; 5 = the 8192-token prefill chunk (TFLOP/s).
 
-Supplementary workloads (--config): 3 = 2-bit, 64 sequences x T (T=1 or 4), uniform
-logits; 4 = 48 chained layers, one decode step; 5 = 8192-token prefill chunk.
+Single configurations: --config 1..5 (3 with --T).
 """
 from __future__ import annotations
 
@@ -46,7 +52,7 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=400)
     ap.add_argument("--warmup", type=int, default=40)
-    ap.add_argument("--config", type=int, default=2, choices=[2, 3, 4, 5])
+    ap.add_argument("--config", type=int, default=2, choices=[1, 2, 3, 4, 5])
     ap.add_argument("--T", type=int, default=4, help="window size for --config 3")
     ap.add_argument("--instances", type=int, default=0,
                     help="layer instances rotated over (default: 10 for config 2, 3 for 3)")
@@ -62,6 +68,8 @@ def parse():
                          "(bf16 router rows) instead of taking the workload's logits")
     ap.add_argument("--shared", action="store_true",
                     help="--config 2 or 4: layers with one always-active shared expert")
+    ap.add_argument("--no-supplementary", action="store_true",
+                    help="default run: only the headline configuration (no configs 1, 3, 4, 5)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="first run one plain device-to-device copy of MIB MiB (the reference "
                          "dispatch that scales hardware byte counters)")
@@ -130,7 +138,10 @@ def timed_region(torch, steps, order, instrument, enqueue_estimate, call="full")
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    plans = [steps[i].stages() for i in order] if instrument else None
+    if instrument == "step":  # one event pair per whole step
+        plans = [[("step", steps[i].full)] for i in order]
+    else:
+        plans = [steps[i].stages() for i in order] if instrument else None
     evs = None
     if instrument:
         evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(p) + 1)] for p in plans]
@@ -161,19 +172,47 @@ def timed_region(torch, steps, order, instrument, enqueue_estimate, call="full")
     return total_ms, stages, host_s, covered
 
 
+def percentiles(ms_list):
+    """p10 / p50 / p90 of per-step times given in ms, reported in us."""
+    import numpy as np
+
+    a = np.asarray(ms_list, np.float64) * 1e3
+    return {"p10": round(float(np.percentile(a, 10)), 2),
+            "p50": round(float(np.percentile(a, 50)), 2),
+            "p90": round(float(np.percentile(a, 90)), 2), "steps": int(a.size),
+            "how": "HIP events around every step on the launch stream (about 1 us each)"}
+
+
 def touched_experts(routing) -> int:
     off = routing.expert_offsets.cpu()
     return int(((off[1:] - off[:-1]) > 0).sum())
 
 
-def cpu_baseline(w, instances_inputs, seconds):
-    """The oracle (as it stands) on host cores, over config steps until ~`seconds`."""
+def host_cores():
+    """Logical CPUs, the CPUs this process may run on, and the physical cores among them
+    (distinct (package, core) pairs from sysfs)."""
+    logical = os.cpu_count() or 1
+    allowed = sorted(os.sched_getaffinity(0))
+    phys = set()
+    for c in allowed:
+        base = f"/sys/devices/system/cpu/cpu{c}/topology/"
+        try:
+            core = open(base + "core_id").read().strip()
+            pkg = open(base + "physical_package_id").read().strip()
+            phys.add((pkg, core))
+        except OSError:
+            phys.add(("?", str(c)))
+    return logical, len(allowed), len(phys)
+
+
+def _oracle_rate(w, instances_inputs, seconds, nthreads):
+    """The oracle (as it stands) on `nthreads` host threads over config steps until about
+    `seconds` of oracle time; returns (GB/s, tokens/s, steps, seconds, instances)."""
     import numpy as np
 
     from oracle import oracle as O
     from quantized_routed_expert_router_amd import synth
 
-    cores = O.threads(0)
     total_t, total_b, steps = 0.0, 0, 0
     host_layers = {}
     i = 0
@@ -188,16 +227,35 @@ def cpu_baseline(w, instances_inputs, seconds):
         t0 = time.perf_counter()
         ids, wt = O.route(lg, w.k)
         O.group(ids, w.E)
-        O.ffn_decode(om(g), om(u), om(dn), w.E, x, ids, wt, x)
+        O.ffn_decode(om(g), om(u), om(dn), w.E, x, ids, wt, x, nthreads=nthreads)
         total_t += time.perf_counter() - t0
         total_b += len(np.unique(ids)) * synth.expert_bytes(w.d, w.f, w.bits)
         steps += 1
         i += 1
-    return dict(value=round(total_b / total_t / 1e9, 4), unit="GB/s", cores=cores, kind="oracle",
-                sample=f"{steps} steps of the same workload (route + decode layer, {w.n} tokens "
-                       f"each) over {min(steps, len(instances_inputs))} layer instances, "
-                       f"{total_t:.1f} s of oracle time on {cores} threads",
-                tokens_per_s=round(steps * w.n / total_t, 3))
+    return (total_b / total_t / 1e9, steps * w.n / total_t, steps, total_t,
+            min(steps, len(instances_inputs)))
+
+
+def cpu_baseline(w, instances_inputs, seconds):
+    """The oracle on one host thread and on all physical cores this process may use
+    (capped by OMP_NUM_THREADS, the machine's CPU share), each for about seconds/2."""
+    from oracle import oracle as O
+
+    logical, allowed, physical = host_cores()
+    cap = int(os.environ.get("OMP_NUM_THREADS", "0") or 0)
+    all_threads = max(1, min(physical, cap) if cap > 0 else physical)
+    gb1, tok1, st1, t1, _ = _oracle_rate(w, instances_inputs, seconds / 2, 1)
+    gbn, tokn, stn, tn, inst = _oracle_rate(w, instances_inputs, seconds / 2, all_threads)
+    used = O.threads(all_threads)
+    return dict(value=round(gbn, 4), unit="GB/s", cores=used, kind="oracle",
+                sample=f"{stn} steps of the same workload (route + decode layer, {w.n} tokens "
+                       f"each) over {inst} layer instances, {tn:.1f} s of oracle time on "
+                       f"{used} threads; and {st1} steps, {t1:.1f} s on 1 thread",
+                tokens_per_s=round(tokn, 3),
+                single_thread={"value": round(gb1, 4), "unit": "GB/s",
+                               "tokens_per_s": round(tok1, 3), "steps": st1},
+                host={"logical_cpus": logical, "cpus_allowed": allowed,
+                      "physical_cores_allowed": physical, "omp_num_threads_cap": cap or None})
 
 
 TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "decode_t4_k_gateup_traffic.md")
@@ -229,7 +287,7 @@ def measured_traffic(profile_path):
 def bench_decode(args, torch, q, synth, workloads):
     import numpy as np
 
-    w = synth.config(args.config, args.T, args.experts)
+    w = synth.config(args.config, args.T, None if args.config == 1 else args.experts)
     shared = args.shared and args.config == 2
     router = args.router and args.config == 2
     if shared:
@@ -238,7 +296,7 @@ def bench_decode(args, torch, q, synth, workloads):
         w.name += "_router"
     # the headline line: configuration 2 as the workload defines it
     primary = args.config == 2 and not shared and not router and args.experts == 512
-    L = args.instances or (10 if args.config == 2 else 3)
+    L = args.instances or {1: 4, 2: 10}.get(args.config, 3)
     log(f"workload {w.name}: generating {L} layer instances on the GPU")
     t0 = time.perf_counter()
     steps, inputs = [], []
@@ -274,6 +332,8 @@ def bench_decode(args, torch, q, synth, workloads):
     est = host_s / max(1, len(warm)) * len(order)
     total_ms, _, host_s, covered = timed_region(torch, steps, order, False, est)
     inst_ms, stage_ms, _, covered_i = timed_region(torch, steps, order, True, est * 2)
+    # per-step times, one event pair around each step (the events add about 1 us a step)
+    _, step_ms, _, _ = timed_region(torch, steps, order, "step", est * 2)
     # the dominant kernel alone: gate/up launches back to back, rotating over the instances
     # (each replays its own step's gate/up stage on that step's workspace)
     gu_ms, _, _, covered_g = timed_region(torch, steps, order, False, est, call="gate_up")
@@ -306,6 +366,7 @@ def bench_decode(args, torch, q, synth, workloads):
         "expert_bytes_per_step": round(float(np.mean([step_bytes[i] for i in order])), 1),
         "touched_experts_per_step": round(mean_touched, 2),
         "stage_us": stage_us,
+        "step_us_percentiles": percentiles(step_ms["step"]),
         "roofline": {"bound": "hbm", "kernel": "k_gateup (gate/up + SwiGLU)",
                      "achieved": round(gu_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_ach / HBM_PEAK_GBS, 4),
@@ -386,6 +447,9 @@ def bench_chain(args, torch, q, synth, workloads):
         "touched_experts_per_layer": round(float(np.mean(touched)), 2),
         "enqueue_covered": covered,
         "graph": graph,
+        "roofline": {"bound": "hbm", "kernel": "whole 48-layer step",
+                     "achieved": round(value, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(value / HBM_PEAK_GBS, 4)},
     }
 
 
@@ -546,13 +610,63 @@ def main():
         torch.cuda.synchronize()
         log(f"calibration copy: {nbytes} bytes read, {nbytes} bytes written")
         del src, dst
-    if args.config in (2, 3):
+    if args.config in (1, 2, 3):
         rec = bench_decode(args, torch, q, synth, workloads)
     elif args.config == 4:
         rec = bench_chain(args, torch, q, synth, workloads)
     else:
         rec = bench_prefill(args, torch, q, synth, workloads)
+    headline = (args.config == 2 and not args.shared and not args.router
+                and args.experts == 512 and not args.instances)
+    if headline and not args.no_supplementary:
+        rec["supplementary"] = supplementary(args, torch, q, synth, workloads)
     print(json.dumps(rec), flush=True)
+
+
+def _summary(r):
+    """The figures of one supplementary record that the headline line carries."""
+    keep = ("value", "unit", "ms_per_step", "tokens_per_s", "pct_of_hbm_peak",
+            "expert_bytes_per_step", "expert_bytes_per_token", "touched_experts_per_step",
+            "layer_tflops", "stage_us", "step_us_percentiles", "graph", "steps")
+    out = {k: r[k] for k in keep if k in r}
+    out["workload"] = r["config"]["workload"]
+    if r.get("roofline"):
+        rf = r["roofline"]
+        out["roofline"] = {k: rf[k] for k in ("bound", "kernel", "achieved", "peak", "unit",
+                                              "frac")}
+    return out
+
+
+def supplementary(args, torch, q, synth, workloads):
+    """Configurations 1, 3 (T = 1 and 4), 4 (eager and one HIP graph) and 5 in the same
+    run, each on its own freshly generated layers, with fewer steps than the headline."""
+    import gc
+
+    plans = [("cfg1_tiny", dict(config=1, steps=200, warmup=20)),
+             ("cfg3_2bit_b64xt1", dict(config=3, T=1, steps=60, warmup=6)),
+             ("cfg3_2bit_b64xt4", dict(config=3, T=4, steps=60, warmup=6)),
+             ("cfg4_chain48", dict(config=4, steps=480, warmup=1)),
+             ("cfg5_prefill8192", dict(config=5, steps=10, warmup=2))]
+    out = {}
+    for name, over in plans:
+        a = argparse.Namespace(**vars(args))
+        a.instances = 0
+        a.no_cpu_baseline = True
+        for k_, v in over.items():
+            setattr(a, k_, v)
+        log(f"supplementary {name}")
+        if a.config in (1, 3):
+            r = bench_decode(a, torch, q, synth, workloads)
+        elif a.config == 4:
+            r = bench_chain(a, torch, q, synth, workloads)
+        else:
+            r = bench_prefill(a, torch, q, synth, workloads)
+        out[name] = _summary(r)
+        del r
+        gc.collect()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return out
 
 
 if __name__ == "__main__":

@@ -43,3 +43,19 @@ def test_step_keeps_its_weights_alive(cls):
         assert callable(getattr(step, name))
     if cls is bench.Step:
         assert callable(step.layer) and callable(step.gate_up)
+
+
+def test_percentiles_and_host_cores():
+    p = bench.percentiles([0.010, 0.020, 0.030, 0.040, 0.050])
+    assert (p["p10"], p["p50"], p["p90"]) == (14.0, 30.0, 46.0) and p["steps"] == 5
+    logical, allowed, physical = bench.host_cores()
+    assert 1 <= physical <= allowed <= logical
+
+
+def test_bench_refuses_more_than_one_gpu():
+    import subprocess
+    import sys
+
+    res = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
+                         text=True, timeout=120)
+    assert res.returncode == 2 and "exactly one" in res.stderr
