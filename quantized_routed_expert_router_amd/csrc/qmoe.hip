@@ -146,7 +146,11 @@ using namespace qmoe;
 extern "C" {
 
 const char* moe_status_string(moe_status s) {
-  switch (s) {
+  // C callers may pass any int; an enum load of a value outside the enumerators' range is
+  // undefined in C++, so the code is read as the int it was passed as
+  int code;
+  memcpy(&code, &s, sizeof code);
+  switch (code) {
     case MOE_OK:
       return "MOE_OK";
     case MOE_ERR_INVALID_ARGUMENT:

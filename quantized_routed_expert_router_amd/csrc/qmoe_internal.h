@@ -233,9 +233,22 @@ struct DecodeArgs {
   unsigned stages;  // MOE_DECODE_* bits
 };
 
+// ------------------------------------------------------------------ routing workspace
+
+// Grouping of more than kSingleGroupPairs pairs runs over many workgroups, in chunks of
+// kChunkPairs pairs, each with its own expert histogram in the routing workspace.
+constexpr int kSingleGroupPairs = 4096;
+constexpr int kChunkPairs = 2048;
+
+inline size_t route_workspace_bytes(int n, int E, int k) {
+  const long long P = (long long)n * k;
+  if (n <= 64 || P <= kSingleGroupPairs) return 0;
+  const long long nchunks = (P + kChunkPairs - 1) / kChunkPairs;
+  return (size_t)(nchunks * E * (long long)sizeof(int));
+}
+
 // ------------------------------------------------------------------ launchers
 
-size_t route_workspace_bytes(int n, int E, int k);
 hipError_t launch_route(const float* logits, int n, int E, int k, const moe_routing* out,
                         void* ws, hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a);

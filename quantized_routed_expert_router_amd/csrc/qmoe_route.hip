@@ -23,7 +23,6 @@ namespace {
 constexpr int kGroupWaves = 8;
 constexpr int kGroupThreads = kGroupWaves * kWave;
 // up to this many pairs one workgroup groups them (k_route_group) without a workspace
-constexpr int kSingleGroupPairs = 4096;
 
 template <int KPL>
 __global__ __launch_bounds__(kGroupThreads) void k_route_fused(
@@ -81,7 +80,6 @@ __global__ __launch_bounds__(kGroupThreads) void k_route_group(const int32_t* __
 // k_group_scatter lets every workgroup derive what it needs from those histograms: the
 // expert totals (hence the offsets, by a scan) and the number of pairs of each expert in
 // earlier chunks; inside its chunk the scatter is the stable per-wave one of group_block.
-constexpr int kChunkPairs = 2048;
 constexpr int kScatterThreads = 1024;
 constexpr int kScatterWaves = kScatterThreads / kWave;
 
@@ -195,13 +193,6 @@ hipError_t launch_route_kpl(const float* logits, int n, int E, int k, const moe_
 }
 
 }  // namespace
-
-size_t route_workspace_bytes(int n, int E, int k) {
-  const long long P = (long long)n * k;
-  if (n <= 64 || P <= kSingleGroupPairs) return 0;
-  const long long nchunks = (P + kChunkPairs - 1) / kChunkPairs;
-  return (size_t)(nchunks * E * (long long)sizeof(int));
-}
 
 hipError_t launch_route(const float* logits, int n, int E, int k, const moe_routing* out,
                         void* ws, hipStream_t stream) {
