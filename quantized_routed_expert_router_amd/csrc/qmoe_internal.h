@@ -97,6 +97,22 @@ __device__ __forceinline__ int block_dot(const uint32_t (&w)[BITS], const int* a
   return acc;
 }
 
+// Workgroup barrier that publishes LDS written by global_load_lds: the caller has already
+// waited (wait_vmcnt) for its own staging loads, so no release fence (which would also wait
+// for the weight loads still in flight) is placed before the barrier.
+__device__ __forceinline__ void barrier_after_lds_dma() {
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// s_waitcnt with only the vector-memory count limited to `vm` (gfx9 encoding: vmcnt in
+// bits 3:0 and 15:14, expcnt 6:4 and lgkmcnt 11:8 left at their maxima).
+template <int VM>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(VM >= 0 && VM < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((VM & 15) | ((VM >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // ------------------------------------------------------------------ workspace layouts
 
 __host__ __device__ inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }

@@ -9,16 +9,14 @@
 //   k_pf_prep     M-tile work list (expert, first grouped position, rows) and the token
 //                 and grouped-position maps of every pair.
 //   k_pf_gateup   one workgroup per (M-tile of 256 pairs, 128 rows of f): the gathered bf16
-//                 activations and the gate and up weight tiles, dequantized from the packed
-//                 codes to bf16 (bf16 of fp32 scale*q + min) straight into LDS, go through
+//                 activations and the packed gate and up codes of each K-step arrive in
+//                 LDS by direct loads; each wave dequantizes its own matrix-core B operands
+//                 (bf16 of fp32 scale*q + min) in registers and runs
 //                 v_mfma_f32_32x32x16_bf16 with fp32 accumulators; the epilogue applies
 //                 SwiGLU and writes h = bf16(silu(g) * u) in grouped pair order.
-//   k_pf_down     the same GEMM over (M-tile, 128 output columns) with h as the A operand
-//                 and the dequantized down tile as B, fp32 outputs y in grouped order.
+//   k_pf_down     the same GEMM over (M-tile, 256 output columns) with h as the A operand
+//                 and the down codes as B, fp32 outputs y in grouped order.
 //   k_pf_combine  residual[t] += sum_j w[t][j] * y[pair (t, j)], slot order, binary64 sum.
-//
-// The K loop steps over one 32-column quantization block at a time with two LDS buffers
-// (see GemmCore below).
 #include <algorithm>
 
 #include "qmoe_internal.h"
@@ -31,9 +29,7 @@ typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 
 constexpr int kBM = kPrefillBM;  // pairs per M-tile
-constexpr int kBN = 128;         // weight rows (output columns) per N-tile
 constexpr int kBK = 32;          // one quantization block of the reduction axis
-constexpr int kLdsRow = kBK + 8; // bf16 per LDS row (padding against bank conflicts)
 
 // ---------------------------------------------------------------- prep
 
@@ -118,256 +114,340 @@ __device__ __forceinline__ int xcd_item(int nitems) {
   return (slot < per && item < nitems) ? item : -1;
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u in fp32 with the hardware exponential and reciprocal (each within about an
+// ulp; h is rounded to bf16 next)
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 // ---------------------------------------------------------------- grouped GEMM core
 //
-// One workgroup computes a kBM (256 pairs) x kBN (128 weight rows) tile for NMAT weight
-// matrices that share the A operand. 8 waves: wave w covers pairs 64*(w/2) .. +64 and
-// weight rows 64*(w%2) .. +64 of every matrix with 2 x 2 x NMAT accumulators of 32x32, so
-// each A fragment read from LDS feeds 2*NMAT matrix-core ops and each B fragment 2, and
-// each dequantized weight serves 256 pairs. Waves whose pair range lies past the tile's
-// rows skip their matrix-core work. Each K-step is one 32-wide quantization block.
-// Thread (lr = tid/4, seg = tid%4) brings in 8 consecutive A values of rows lr and lr+128
-// and one code word plus the scale/min word of weight row lr of each matrix, and writes
-// them (dequantized) into the LDS buffer of its K-step. Raw operands run two K-steps
-// ahead in a register ring; step kb dequantizes step kb+1 into the other LDS buffer right
-// after issuing its matrix-core work.
+// One workgroup of 4 waves (one per SIMD) computes kBM (256) pairs x 32 weight rows per B
+// operand set of each wave; a wave has two sets (gate/up: the gate and the up rows of the
+// same 32 rows, 128 rows a workgroup; down: two groups of 32 output columns, 256 a
+// workgroup). Each wave dequantizes its own matrix-core B operands straight into
+// registers: lane l needs 8 consecutive reduction-axis codes of weight row l%32 (one 4-bit
+// code word, or half a 2-bit word), so no weight passes through LDS as bf16 and none is
+// dequantized twice within the tile. Each K-step's operands (the A tile of 256 pairs x 32
+// bf16 and each wave's packed code and scale/min words) arrive by direct loads into LDS
+// (global_load_lds, no register trip) in a ring of kRbStages stages, each stage its own
+// LDS variable so that the compiler can tell the stage being filled from the one being
+// read, and registers carry nothing from one loop iteration to the next (which would make
+// its wait counts drain the ring). In the A tile, row m's 16-byte segment s sits at
+// position s ^ (m/4 % 4), so that the 16 lanes of each quarter-wave read 16 different bank
+// groups. The 8 x 2 accumulators of 32x32 of a wave live in the accumulation registers
+// (256 a lane). While a K-step's matrix-core ops run, the wave reads and dequantizes the
+// next step's operands.
 //
-// (Measured on MI355X: the dequantization and the matrix-core work of a SIMD do not
-// overlap, whether they are issued by the same waves or by separate producer and consumer
-// waves; the time per tile is their sum, so the 256-pair tile, which halves the
-// dequantization per flop against a 128-pair tile, is the one that pays.)
-constexpr int kGemmThreads = 512;
-static_assert(kBM == 256 && kBN == 128, "tile shape of the grouped GEMM core");
+// (Measured on MI355X at the 8192-token chunk: the waves spend about half their time
+// waiting for the direct loads of the operands; a ring of six stages is 5% faster than
+// four. Weights dequantized once per chunk into bf16 for the experts with several M-tiles
+// made the gate/up GEMM no faster, and the dequantization pass itself cost 158 us.)
+constexpr int kRbThreads = 256;
+constexpr int kRbStages = 6;                       // K-steps in flight
+constexpr int kRbSlots = kBM * kBK * 2 / 16;       // 16-byte slots of one A tile (1024)
+constexpr int kRbDma = kRbSlots / kRbThreads;      // A direct loads a thread a K-step (4)
 
-template <int BITS, int NMAT>
-struct GemmCore {
-  typedef __bf16 ATile[kBM][kLdsRow];
-  typedef __bf16 BTile[kBN][kLdsRow];
-  static constexpr size_t kLdsBytes = 2 * sizeof(ATile) + (size_t)2 * NMAT * sizeof(BTile);
+struct RbStage {
+  uint4 a[kRbSlots];          // A tile
+  uint4 codes[4][kWave];      // per wave: [set][row] 16 bytes (2-bit: 16 row pairs a set)
+  uint32_t sm[4][kWave];      // per wave: [set][row] scale/min word
+};
 
-  struct Raw {
-    uint4 a[2];
-    uint32_t w[NMAT], sm[NMAT];
+__device__ __forceinline__ int swz(int row, int seg) { return seg ^ ((row >> 2) & 3); }
+
+template <int BITS>
+struct RbCore {
+  typedef __attribute__((address_space(3))) void* lptr_t;
+  typedef const __attribute__((address_space(1))) void* gptr_t;
+  static constexpr int kNSet = 2;
+  static constexpr int kOps = kRbDma + 2;  // direct loads a thread a K-step
+
+  RbStage* st[kRbStages];
+  const char* arow[kRbDma];  // this thread's A segments at K-step 0
+  const char* bcode;         // this lane's code bytes at K-step 0
+  const char* bsm;           // this lane's scale/min word at K-step 0
+  size_t bstep, smstep;      // bytes per K-step of the codes and of the scale/min words
+  int lane, wave, nk;
+  f32x16 acc[kNSet][8];
+
+  // A tile and this wave's weight words of K-step kb (past the end: the last step again,
+  // into a stage no matrix-core step reads).
+  template <int S>
+  __device__ __forceinline__ void dma(int kb) const {
+    const size_t k = (size_t)min(kb, nk - 1);
+    const size_t aoff = k * (kBK * 2);
+#pragma unroll
+    for (int i = 0; i < kRbDma; ++i)
+      __builtin_amdgcn_global_load_lds((gptr_t)(arow[i] + aoff),
+                                       (lptr_t)(st[S]->a + kRbThreads * i + kWave * wave), 16, 0,
+                                       0);
+    __builtin_amdgcn_global_load_lds((gptr_t)(bcode + k * bstep), (lptr_t)(st[S]->codes[wave]),
+                                     16, 0, 0);
+    __builtin_amdgcn_global_load_lds((gptr_t)(bsm + k * smstep), (lptr_t)(st[S]->sm[wave]), 4, 0,
+                                     0);
+  }
+
+  // Operands of one K-step in registers: the A fragments of both 16-wide halves and the
+  // dequantized B operands of both sets.
+  struct Ops {
+    bf16x8 a[2][8];
+    bf16x8 b[2][kNSet];
   };
 
-  ATile* sA;                    // [2]
-  BTile* sB;                    // [NMAT][2]
-  const uint16_t* arow[2];      // A rows lr and lr+128 of this thread, at column 8*seg
-  const uint32_t* wcol[NMAT];   // code word of weight row lr at K-step 0
-  const uint32_t* smcol[NMAT];  // scale/min word at K-step 0
-  size_t wstep, smstep;         // stride of one K-step in words
-  int lr, seg, lane, wm, wn, nk;
-  bool active;                  // this wave's pair range holds rows of the tile
-  f32x16 acc[NMAT][2][2];
-
-  __device__ __forceinline__ Raw load(int kb) const {
-    Raw R;
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      R.a[i] = *reinterpret_cast<const uint4*>(arow[i] + (size_t)kb * kBK);
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m) {
-      R.w[m] = wcol[m][(size_t)kb * wstep];
-      R.sm[m] = smcol[m][(size_t)kb * smstep];
-    }
-    return R;
-  }
-
-  __device__ __forceinline__ void stage(const Raw& R, int buf) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<uint4*>(&sA[buf][lr + 128 * i][8 * seg]) = R.a[i];
-#pragma unroll
-    for (int m = 0; m < NMAT; ++m)
-      *reinterpret_cast<bf16x8*>(&sB[2 * m + buf][lr][8 * seg]) =
-          dequant_word<BITS>(R.w[m], seg, R.sm[m]);
-  }
-
-  __device__ __forceinline__ void mma(int buf) {
+  // Read K-step operands from stage S; keep = 0 (steps past the last) zeroes the scale and
+  // min, hence the B operands.
+  template <int S>
+  __device__ __forceinline__ Ops read_ops(uint32_t keep) const {
+    Ops o;
+    const RbStage& sg = *st[S];
+    const int r = lane & 31, hi = lane >> 5;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int kk = ks * 16 + (lane / 32) * 8;
-      bf16x8 a[2], b[NMAT][2];
+      const int seg = 2 * ks + hi;
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        a[i] = *reinterpret_cast<const bf16x8*>(&sA[buf][wm + 32 * i + lane % 32][kk]);
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          b[m][j] =
-              *reinterpret_cast<const bf16x8*>(&sB[2 * m + buf][wn + 32 * j + lane % 32][kk]);
-#pragma unroll
-      for (int m = 0; m < NMAT; ++m)
-#pragma unroll
-        for (int i = 0; i < 2; ++i)
-#pragma unroll
-          for (int j = 0; j < 2; ++j)
-            acc[m][i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[i], b[m][j], acc[m][i][j],
-                                                                   0, 0, 0);
+      for (int i = 0; i < 8; ++i) {
+        const int mrow = 32 * i + r;
+        const uint4 av = sg.a[4 * mrow + swz(mrow, seg)];
+        __builtin_memcpy(&o.a[ks][i], &av, 16);
+      }
     }
+#pragma unroll
+    for (int q = 0; q < kNSet; ++q) {
+      const uint32_t smw = sg.sm[wave][32 * q + r] & keep;
+      uint32_t w0, w1;  // the code words of the two halves (ks = 0, 1)
+      if (BITS == 4) {
+        const uint4 c = sg.codes[wave][32 * q + r];
+        w0 = hi ? c.y : c.x;
+        w1 = hi ? c.w : c.z;
+      } else {
+        // set q's rows 2i, 2i+1 in slot 16q + i: words (row 2i: 0, 1; row 2i+1: 2, 3)
+        const uint4 c = sg.codes[wave][16 * q + r / 2];
+        w0 = (r & 1) ? c.z : c.x;
+        w1 = (r & 1) ? c.w : c.y;
+      }
+      o.b[0][q] = dequant_word<BITS>(w0, hi, smw);
+      o.b[1][q] = dequant_word<BITS>(w1, 2 + hi, smw);
+    }
+    return o;
   }
 
-  // One K-step: the matrix-core work of step kb (skipped past the last step and by waves
-  // with no rows), then step kb+1 dequantized into the other buffer and step kb+3
-  // requested into the freed ring slot. Staging and loads run unconditionally (past the
-  // end they repeat the last block into a buffer no matrix-core step reads), so the loop
-  // has no data-dependent branches around its memory operations and the wait counts stay
-  // exact across iterations.
-  __device__ __forceinline__ Raw step(int kb, const Raw next) {
-    if (active && kb < nk) mma(kb & 1);
-    stage(next, (kb + 1) & 1);
-    const Raw refill = load(min(kb + 3, nk - 1));
-    __syncthreads();
-    return refill;
+  __device__ __forceinline__ void mma(const Ops& o) {
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int q = 0; q < kNSet; ++q)
+          acc[q][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[ks][i], o.b[ks][q], acc[q][i],
+                                                              0, 0, 0);
+  }
+
+  // One K-step kb (its operands `cur` already in registers, read from stage S): wait for
+  // step kb + 1's operands and publish them (this wave's reads of step kb have completed,
+  // so after the barrier no wave reads stage S any more), request step kb + kRbStages into
+  // stage S, then step kb's matrix-core work with the reads of step kb + 1 placed ahead of
+  // it and their dequantization interleaved with the matrix-core ops, which run while it
+  // executes. Steps past the last one multiply zero B operands (an AND with a uniform
+  // mask, not a branch), so that each step is one basic block in which that order holds.
+  template <int S>
+  __device__ __forceinline__ Ops step(int kb, const Ops& cur) {
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
+    wait_vmcnt<(kRbStages - 2) * kOps>();
+    barrier_after_lds_dma();
+    dma<S>(kb + kRbStages);
+    __builtin_amdgcn_sched_barrier(0);
+    Ops next = read_ops<(S + 1) % kRbStages>(kb + 1 < nk ? 0xffffffffu : 0u);
+    mma(cur);
+    // the next step's operands are complete within this step
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+      for (int q = 0; q < kNSet; ++q) {
+        uint4 v;
+        __builtin_memcpy(&v, &next.b[ks][q], 16);
+        asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
+        __builtin_memcpy(&next.b[ks][q], &v, 16);
+      }
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * 8 + 2 * kNSet, 0);  // LDS reads
+#pragma unroll
+    for (int i = 0; i < 16 * kNSet; ++i) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix-core op
+      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU instructions
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    return next;
   }
 
   __device__ __forceinline__ void run() {
 #pragma unroll
-    for (int m = 0; m < NMAT; ++m)
+    for (int q = 0; q < kNSet; ++q)
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+      for (int i = 0; i < 8; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-          for (int q = 0; q < 16; ++q) acc[m][i][j][q] = 0.0f;
-    Raw r0 = load(0);
-    Raw r1 = load(min(1, nk - 1));
-    stage(r0, 0);
-    r0 = load(min(2, nk - 1));
-    __syncthreads();
-    for (int kb = 0; kb < nk; kb += 2) {
-      r1 = step(kb, r1);
-      r0 = step(kb + 1, r0);
+        for (int e = 0; e < 16; ++e) acc[q][i][e] = 0.0f;
+    dma<0>(0);
+    dma<1>(1);
+    dma<2>(2);
+    dma<3>(3);
+    dma<4>(4);
+    dma<5>(5);
+    wait_vmcnt<(kRbStages - 1) * kOps>();
+    barrier_after_lds_dma();
+    Ops o0 = read_ops<0>(0xffffffffu);
+    static_assert(kRbStages == 6, "the loop below is unrolled over the ring");
+    for (int kb = 0; kb < nk; kb += kRbStages) {
+      const Ops o1 = step<0>(kb, o0);
+      const Ops o2 = step<1>(kb + 1, o1);
+      const Ops o3 = step<2>(kb + 2, o2);
+      const Ops o4 = step<3>(kb + 3, o3);
+      const Ops o5 = step<4>(kb + 4, o4);
+      o0 = step<5>(kb + 5, o5);
     }
+    wait_vmcnt<0>();  // the direct loads past the last step have landed
   }
 
-  // Set up the LDS views and the wave's tile position.
-  __device__ __forceinline__ void init(char* smem, int rows, int nk_) {
-    const int tid = threadIdx.x, wave = tid / kWave;
-    sA = reinterpret_cast<ATile*>(smem);
-    sB = reinterpret_cast<BTile*>(smem + 2 * sizeof(ATile));
-    lr = tid / 4;
-    seg = tid % 4;
-    lane = tid & (kWave - 1);
-    wm = (wave / 2) * 64;
-    wn = (wave % 2) * 64;
+  __device__ __forceinline__ void init(RbStage* stages, int nk_) {
+#pragma unroll
+    for (int i = 0; i < kRbStages; ++i) st[i] = stages + i;
+    lane = threadIdx.x & (kWave - 1);
+    wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x / kWave);
     nk = nk_;
-    active = wm < rows;
+  }
+
+  // A row m (0..255) of this thread's slot set i, and the byte offset of its segment
+  __device__ __forceinline__ int arow_index(int i) const { return ((int)threadIdx.x >> 2) + 64 * i; }
+  __device__ __forceinline__ int aseg_bytes() const {
+    const int t = threadIdx.x;
+    return 16 * swz(t >> 2, t & 3);
+  }
+
+  // The weight row and set whose codes lane l brings in: 4-bit, set l/32 row l%32; 2-bit,
+  // set (l%32)/16, rows 2(l%16) and 2(l%16)+1 (16 bytes; lanes 32..63 repeat 0..31). The
+  // scale/min word: set l/32, row l%32. row_of(q, r) is the matrix row of set q's row r;
+  // past the matrix, a valid row (never stored) is loaded.
+  template <class RowOf>
+  __device__ __forceinline__ void set_weights(const uint32_t* codes0, const uint32_t* codes1,
+                                              const uint32_t* sm0, const uint32_t* sm1,
+                                              size_t eoff, int NR, RowOf row_of) {
+    const int cq = BITS == 4 ? lane >> 5 : (lane & 31) >> 4;
+    const int cr = BITS == 4 ? (lane & 31) : 2 * (lane & 15);
+    const int crow = min(row_of(cq, cr), BITS == 4 ? NR - 1 : NR - 2);
+    bcode = reinterpret_cast<const char*>((cq ? codes1 : codes0) + (eoff + crow) * BITS);
+    bsm = reinterpret_cast<const char*>((lane >> 5 ? sm1 : sm0) + eoff +
+                                        min(row_of(lane >> 5, lane & 31), NR - 1));
+    bstep = (size_t)NR * BITS * 4;
+    smstep = (size_t)NR * 4;
   }
 };
 
 // ---------------------------------------------------------------- gate/up GEMM
 
+// h = bf16(silu(g) * u). Lane l holds column 32*wave + l%32 of rows 32i + 8(q/4) +
+// 4(l/32) + q%4; the wave's 256 x 32 block goes through LDS (the ring is free by then) so
+// that rows leave as 16-byte stores.
 template <int BITS>
-__global__ __launch_bounds__(kGemmThreads) void k_pf_gateup(
+__global__ __launch_bounds__(kRbThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_pf_gateup(
     const uint32_t* __restrict__ gcodes, const uint32_t* __restrict__ gsm,
     const uint32_t* __restrict__ ucodes, const uint32_t* __restrict__ usm, int d, int f,
     const int4* __restrict__ tiles, const int* __restrict__ ntiles,
-    const uint16_t* __restrict__ x, const int* __restrict__ tok_of_g, uint16_t* __restrict__ h,
-    int) {
-  typedef GemmCore<BITS, 2> Core;
-  __shared__ __attribute__((aligned(16))) char smem[Core::kLdsBytes];
-  const int ntn = (f + kBN - 1) / kBN;
+    const uint16_t* __restrict__ x, const int* __restrict__ tok_of_g, uint16_t* __restrict__ h) {
+  __shared__ RbStage stages[kRbStages];
+  constexpr int kN = 4 * 32;  // weight rows a workgroup
+  const int ntn = (f + kN - 1) / kN;
   const int item = xcd_item(load_uniform(ntiles) * ntn);
   if (item < 0) return;
   const int mt = item / ntn, nt = item % ntn;
   const int4 tile = load_uniform(tiles + mt);
   const int e = tile.x, g0 = tile.y, rows = tile.z;
   const int nbd = d / kBK;
-  const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
-
-  Core c;
-  c.init(smem, rows, nbd);
+  RbCore<BITS> c;
+  c.init(stages, nbd);
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int tok = tok_of_g[g0 + min(c.lr + 128 * i, rows - 1)];  // padded rows repeat
-    c.arow[i] = x + (size_t)tok * d + 8 * c.seg;                   // a valid token
+  for (int i = 0; i < kRbDma; ++i) {
+    const int tok = tok_of_g[g0 + min(c.arow_index(i), rows - 1)];  // padded rows: a valid row
+    c.arow[i] = reinterpret_cast<const char*>(x + (size_t)tok * d) + c.aseg_bytes();
   }
-  const int wrow = min(nt * kBN + c.lr, f - 1);  // rows past f load row f-1, never stored
-  const size_t blk0 = (size_t)e * nbd * f + wrow;
-  c.wcol[0] = gcodes + blk0 * BITS + code_word_index<BITS>(c.seg);
-  c.wcol[1] = ucodes + blk0 * BITS + code_word_index<BITS>(c.seg);
-  c.smcol[0] = gsm + blk0;
-  c.smcol[1] = usm + blk0;
-  c.wstep = (size_t)f * BITS;
-  c.smstep = (size_t)f;
+  const int n0 = nt * kN + 32 * c.wave;  // this wave's rows n0 + 0..31: gate (set 0), up (set 1)
+  c.set_weights(gcodes, ucodes, gsm, usm, (size_t)e * nbd * f, f,
+                [&](int, int r) { return n0 + r; });
   c.run();
 
-  // epilogue: h = bf16(silu(g) * u), staged per wave in LDS (64 x 64 bf16 = 8 KB per wave)
-  // for 16-byte global stores
-  if (!c.active) return;
-  __bf16* st = reinterpret_cast<__bf16*>(smem) + wave * (64 * 64);
+  __syncthreads();  // every wave is done with the ring before it is reused
+  uint16_t* stg = reinterpret_cast<uint16_t*>(stages) + c.wave * (kBM * 32);
+  const int lane = c.lane;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int rr = 32 * i + (q / 4) * 8 + (lane / 32) * 4 + (q % 4);
-        const int cc = 32 * j + lane % 32;
-        st[rr * 64 + cc] = (__bf16)silu_mul(c.acc[0][i][j][q], c.acc[1][i][j][q]);
-      }
+    for (int q = 0; q < 16; ++q) {
+      const int rr = 32 * i + (q / 4) * 8 + (lane / 32) * 4 + (q % 4);
+      const __bf16 v = (__bf16)silu_mul(c.acc[0][i][q], c.acc[1][i][q]);
+      __builtin_memcpy(&stg[rr * 32 + (lane & 31)], &v, 2);
+    }
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // 256 rows x 4 chunks of 8 bf16: lane l takes chunk l%4 of rows l/4 + 16p
+  const int col0 = n0 + 8 * (lane & 3);
+  if (col0 < f) {
 #pragma unroll
-  for (int q = 0; q < 8; ++q) {
-    const int ch = lane + kWave * q;  // 512 chunks of 8 bf16
-    const int rr = ch / 8, cc = (ch % 8) * 8;
-    const int col = nt * kBN + c.wn + cc;
-    if (c.wm + rr < rows && col < f) {
-      const uint4 v = *reinterpret_cast<const uint4*>(&st[rr * 64 + cc]);
-      *reinterpret_cast<uint4*>(h + (size_t)(g0 + c.wm + rr) * f + col) = v;
+    for (int p = 0; p < 16; ++p) {
+      const int rr = (lane >> 2) + 16 * p;
+      if (rr < rows)
+        *reinterpret_cast<uint4*>(h + (size_t)(g0 + rr) * f + col0) =
+            *reinterpret_cast<const uint4*>(&stg[rr * 32 + 8 * (lane & 3)]);
     }
   }
 }
 
 // ---------------------------------------------------------------- down GEMM
 
+// Lanes l and l+32 hold column 32q + l%32 of rows 32i + 8(e/4) + 4(l/32) + e%4; 32-row
+// groups wholly inside the tile store without a per-row test.
 template <int BITS>
-__global__ __launch_bounds__(kGemmThreads) void k_pf_down(
+__global__ __launch_bounds__(kRbThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_pf_down(
     const uint32_t* __restrict__ dcodes, const uint32_t* __restrict__ dsm, int d, int f,
     const int4* __restrict__ tiles, const int* __restrict__ ntiles,
-    const uint16_t* __restrict__ h, float* __restrict__ y, int) {
-  typedef GemmCore<BITS, 1> Core;
-  __shared__ __attribute__((aligned(16))) char smem[Core::kLdsBytes];
-  const int ntn = (d + kBN - 1) / kBN;
+    const uint16_t* __restrict__ h, float* __restrict__ y) {
+  __shared__ RbStage stages[kRbStages];
+  constexpr int kN = 4 * 64;  // output columns a workgroup
+  const int ntn = (d + kN - 1) / kN;
   const int item = xcd_item(load_uniform(ntiles) * ntn);
   if (item < 0) return;
   const int mt = item / ntn, nt = item % ntn;
   const int4 tile = load_uniform(tiles + mt);
   const int e = tile.x, g0 = tile.y, rows = tile.z;
   const int nbf = f / kBK;
-  const int lane = threadIdx.x & (kWave - 1);
-
-  Core c;
-  c.init(smem, rows, nbf);
+  RbCore<BITS> c;
+  c.init(stages, nbf);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
-    c.arow[i] = h + (size_t)(g0 + min(c.lr + 128 * i, rows - 1)) * f + 8 * c.seg;
-  const int wrow = min(nt * kBN + c.lr, d - 1);  // rows past d load row d-1, never stored
-  const size_t blk0 = (size_t)e * nbf * d + wrow;
-  c.wcol[0] = dcodes + blk0 * BITS + code_word_index<BITS>(c.seg);
-  c.smcol[0] = dsm + blk0;
-  c.wstep = (size_t)d * BITS;
-  c.smstep = (size_t)d;
+  for (int i = 0; i < kRbDma; ++i)
+    c.arow[i] = reinterpret_cast<const char*>(h + (size_t)(g0 + min(c.arow_index(i), rows - 1)) * f) +
+                c.aseg_bytes();
+  const int c0 = nt * kN + 64 * c.wave;  // set q: output columns c0 + 32q + 0..31
+  c.set_weights(dcodes, dcodes, dsm, dsm, (size_t)e * nbf * d, d,
+                [&](int q, int r) { return c0 + 32 * q + r; });
   c.run();
-  if (!c.active) return;
-
-  // y in grouped order: lanes 0..31 of a row write 32 consecutive floats
+  const int lane = c.lane;
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int q = 0; q < 2; ++q) {
+    const int col = c0 + 32 * q + (lane & 31);
+    if (col >= d) continue;
 #pragma unroll
-    for (int j = 0; j < 2; ++j)
+    for (int i = 0; i < 8; ++i) {
+      float* yb = y + (size_t)(g0 + 32 * i + (lane / 32) * 4) * d + col;
+      if (32 * i + 32 <= rows) {
 #pragma unroll
-      for (int q = 0; q < 16; ++q) {
-        const int rr = c.wm + 32 * i + (q / 4) * 8 + (lane / 32) * 4 + (q % 4);
-        const int col = nt * kBN + c.wn + 32 * j + lane % 32;
-        if (rr < rows && col < d) y[(size_t)(g0 + rr) * d + col] = c.acc[0][i][j][q];
+        for (int e2 = 0; e2 < 16; ++e2) yb[(size_t)((e2 / 4) * 8 + (e2 % 4)) * d] = c.acc[q][i][e2];
+      } else if (32 * i < rows) {
+#pragma unroll
+        for (int e2 = 0; e2 < 16; ++e2) {
+          const int rr = 32 * i + (e2 / 4) * 8 + (lane / 32) * 4 + (e2 % 4);
+          if (rr < rows) yb[(size_t)((e2 / 4) * 8 + (e2 % 4)) * d] = c.acc[q][i][e2];
+        }
       }
+    }
+  }
 }
 
 // ---------------------------------------------------------------- combine
@@ -441,19 +521,19 @@ hipError_t launch_prefill_bits(const PrefillArgs& a) {
 
   const int max_mt = prefill_max_mtiles(P, E);
   if (a.stages & MOE_PREFILL_GATE_UP) {
-    const int gu_items = ((max_mt * ((f + kBN - 1) / kBN) + 7) / 8) * 8;
-    hipLaunchKernelGGL(k_pf_gateup<BITS>, dim3(gu_items), dim3(kGemmThreads), 0, a.stream,
+    const int gu_items = ((max_mt * ((f + 127) / 128) + 7) / 8) * 8;
+    hipLaunchKernelGGL(k_pf_gateup<BITS>, dim3(gu_items), dim3(kRbThreads), 0, a.stream,
                        L.gate.codes, reinterpret_cast<const uint32_t*>(L.gate.scale_min),
                        L.up.codes, reinterpret_cast<const uint32_t*>(L.up.scale_min), d, f, tiles,
-                       ntiles, a.x, tok_of_g, h, gu_items);
+                       ntiles, a.x, tok_of_g, h);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
   if (a.stages & MOE_PREFILL_DOWN) {
-    const int dn_items = ((max_mt * ((d + kBN - 1) / kBN) + 7) / 8) * 8;
-    hipLaunchKernelGGL(k_pf_down<BITS>, dim3(dn_items), dim3(kGemmThreads), 0, a.stream,
+    const int dn_items = ((max_mt * ((d + 255) / 256) + 7) / 8) * 8;
+    hipLaunchKernelGGL(k_pf_down<BITS>, dim3(dn_items), dim3(kRbThreads), 0, a.stream,
                        L.down.codes, reinterpret_cast<const uint32_t*>(L.down.scale_min), d, f,
-                       tiles, ntiles, h, y, dn_items);
+                       tiles, ntiles, h, y);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
