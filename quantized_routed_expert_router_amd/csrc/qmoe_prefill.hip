@@ -122,31 +122,37 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 
 // ---------------------------------------------------------------- grouped GEMM core
 //
-// One workgroup of 4 waves (one per SIMD) computes kBM (256) pairs x 32 weight rows per B
-// operand set of each wave; a wave has two sets (gate/up: the gate and the up rows of the
-// same 32 rows, 128 rows a workgroup; down: two groups of 32 output columns, 256 a
-// workgroup). Each wave dequantizes its own matrix-core B operands straight into
-// registers: lane l needs 8 consecutive reduction-axis codes of weight row l%32 (one 4-bit
-// code word, or half a 2-bit word), so no weight passes through LDS as bf16 and none is
-// dequantized twice within the tile. Each K-step's operands (the A tile of 256 pairs x 32
-// bf16 and each wave's packed code and scale/min words) arrive by direct loads into LDS
-// (global_load_lds, no register trip) in a ring of kRbStages stages, each stage its own
-// LDS variable so that the compiler can tell the stage being filled from the one being
-// read, and registers carry nothing from one loop iteration to the next (which would make
-// its wait counts drain the ring). In the A tile, row m's 16-byte segment s sits at
-// position s ^ (m/4 % 4), so that the 16 lanes of each quarter-wave read 16 different bank
-// groups. The 8 x 2 accumulators of 32x32 of a wave live in the accumulation registers
-// (256 a lane). While a K-step's matrix-core ops run, the wave reads and dequantizes the
-// next step's operands.
+// One workgroup of 4 waves (one per SIMD) computes up to kBM (256) pairs x 32 weight rows
+// per B operand set of each wave; a wave has two sets (gate/up: the gate and the up rows of
+// the same 32 rows, 128 rows a workgroup; down: two groups of 32 output columns, 256 a
+// workgroup). The pairs are taken in NI groups of 32 (NI = 1, 2, 4 or 8, the smallest that
+// holds the M-tile's rows), so that the last, partly filled M-tile of an expert issues
+// matrix-core ops and A loads only for the row groups it has. Each wave dequantizes its own
+// matrix-core B operands straight into registers: lane l needs 8 consecutive
+// reduction-axis codes of weight row l%32 (one 4-bit code word, or half a 2-bit word), so
+// no weight passes through LDS as bf16 and none is dequantized twice within the tile.
+// Each K-step's operands (the A tile of 32*NI pairs x 32 bf16 and each wave's packed code
+// and scale/min words) arrive by direct loads into LDS (global_load_lds, no register trip)
+// in a ring of kRbStages slots, each slot its own LDS variable so that the compiler can
+// tell the slot being filled from the one being read, and no register written by a global
+// load is carried from one loop iteration to the next (which would make its wait counts
+// drain the ring). The weight words are read from LDS two steps ahead, so that a step's
+// dequantization needs no memory access; the A fragments one step ahead. In the A tile,
+// row m's 16-byte segment s sits at position s ^ (m/4 % 4), so that the 16 lanes of each
+// quarter-wave read 16 different bank groups. The NI x 2 accumulators of 32x32 of a wave
+// live in the accumulation registers (32*NI a lane). A step's LDS reads and dequantization
+// are interleaved with its matrix-core ops, one read after each op, so that the reads of
+// the four waves do not hold up the issue of their matrix-core ops.
 //
-// (Measured on MI355X at the 8192-token chunk: the waves spend about half their time
-// waiting for the direct loads of the operands; a ring of six stages is 5% faster than
-// four. Weights dequantized once per chunk into bf16 for the experts with several M-tiles
-// made the gate/up GEMM no faster, and the dequantization pass itself cost 158 us.)
+// (Measured on MI355X at the 8192-token chunk, gate/up: with every row group computed the
+// ragged M-tiles made 31% of the matrix-core ops; the kernel runs near 1.9 GHz, limited by
+// power; leaving out the direct loads, the dequantization or the LDS reads each saves
+// 100-190 us, and waiting for older data does not, so the loads cost issue slots and power,
+// not latency. Weights dequantized once per chunk into bf16 for the experts with several
+// M-tiles made the gate/up GEMM no faster, and the dequantization pass itself cost 158 us.)
 constexpr int kRbThreads = 256;
 constexpr int kRbStages = 6;                       // K-steps in flight
-constexpr int kRbSlots = kBM * kBK * 2 / 16;       // 16-byte slots of one A tile (1024)
-constexpr int kRbDma = kRbSlots / kRbThreads;      // A direct loads a thread a K-step (4)
+constexpr int kRbSlots = kBM * kBK * 2 / 16;       // 16-byte slots of a full A tile (1024)
 
 struct RbStage {
   uint4 a[kRbSlots];          // A tile
@@ -156,32 +162,44 @@ struct RbStage {
 
 __device__ __forceinline__ int swz(int row, int seg) { return seg ^ ((row >> 2) & 3); }
 
-template <int BITS>
+// Row groups of 32 computed for an M-tile of `rows` pairs
+__device__ __forceinline__ int row_groups(int rows) {
+  return rows <= 32 ? 1 : rows <= 64 ? 2 : rows <= 128 ? 4 : 8;
+}
+
+template <int BITS, int NI>
 struct RbCore {
   typedef __attribute__((address_space(3))) void* lptr_t;
   typedef const __attribute__((address_space(1))) void* gptr_t;
   static constexpr int kNSet = 2;
-  static constexpr int kOps = kRbDma + 2;  // direct loads a thread a K-step
+  // A direct loads a thread a K-step: each covers 64 rows (4 threads a row)
+  static constexpr int kDmaA = NI >= 2 ? NI / 2 : 1;
+  static constexpr int kOps = kDmaA + 2;  // direct loads a thread a K-step
 
   RbStage* st[kRbStages];
-  const char* arow[kRbDma];  // this thread's A segments at K-step 0
+  const char* arow[kDmaA];   // this thread's A segments at K-step 0
   const char* bcode;         // this lane's code bytes at K-step 0
   const char* bsm;           // this lane's scale/min word at K-step 0
   size_t bstep, smstep;      // bytes per K-step of the codes and of the scale/min words
   int lane, wave, nk;
-  f32x16 acc[kNSet][8];
+  f32x16 acc[kNSet][NI];
 
-  // A tile and this wave's weight words of K-step kb (past the end: the last step again,
-  // into a stage no matrix-core step reads).
+  // Direct loads of K-step j (past the end: the last step again, into a slot that no
+  // matrix-core step reads): the A tile into slot S, and this wave's code and scale/min
+  // words into slot S of their own ring (the fields of a slot are filled at different
+  // steps: A(j) and the words of j + 1 are requested together).
   template <int S>
-  __device__ __forceinline__ void dma(int kb) const {
-    const size_t k = (size_t)min(kb, nk - 1);
-    const size_t aoff = k * (kBK * 2);
+  __device__ __forceinline__ void dma_a(int kb) const {
+    const size_t aoff = (size_t)min(kb, nk - 1) * (kBK * 2);
 #pragma unroll
-    for (int i = 0; i < kRbDma; ++i)
+    for (int i = 0; i < kDmaA; ++i)
       __builtin_amdgcn_global_load_lds((gptr_t)(arow[i] + aoff),
                                        (lptr_t)(st[S]->a + kRbThreads * i + kWave * wave), 16, 0,
                                        0);
+  }
+  template <int S>
+  __device__ __forceinline__ void dma_w(int kb) const {
+    const size_t k = (size_t)min(kb, nk - 1);
     __builtin_amdgcn_global_load_lds((gptr_t)(bcode + k * bstep), (lptr_t)(st[S]->codes[wave]),
                                      16, 0, 0);
     __builtin_amdgcn_global_load_lds((gptr_t)(bsm + k * smstep), (lptr_t)(st[S]->sm[wave]), 4, 0,
@@ -191,73 +209,99 @@ struct RbCore {
   // Operands of one K-step in registers: the A fragments of both 16-wide halves and the
   // dequantized B operands of both sets.
   struct Ops {
-    bf16x8 a[2][8];
+    bf16x8 a[2][NI];
     bf16x8 b[2][kNSet];
   };
+  // This lane's packed weight words of one K-step: per set, the code words of the two
+  // halves and the scale/min word.
+  struct Raw {
+    uint32_t w[kNSet][2];
+    uint32_t sm[kNSet];
+  };
 
-  // Read K-step operands from stage S; keep = 0 (steps past the last) zeroes the scale and
-  // min, hence the B operands.
   template <int S>
-  __device__ __forceinline__ Ops read_ops(uint32_t keep) const {
-    Ops o;
+  __device__ __forceinline__ void read_a(Ops& o) const {
     const RbStage& sg = *st[S];
     const int r = lane & 31, hi = lane >> 5;
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const int seg = 2 * ks + hi;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
+      for (int i = 0; i < NI; ++i) {
         const int mrow = 32 * i + r;
         const uint4 av = sg.a[4 * mrow + swz(mrow, seg)];
         __builtin_memcpy(&o.a[ks][i], &av, 16);
       }
     }
+  }
+
+  template <int S>
+  __device__ __forceinline__ Raw read_w() const {
+    Raw o;
+    const RbStage& sg = *st[S];
+    const int r = lane & 31, hi = lane >> 5;
 #pragma unroll
     for (int q = 0; q < kNSet; ++q) {
-      const uint32_t smw = sg.sm[wave][32 * q + r] & keep;
-      uint32_t w0, w1;  // the code words of the two halves (ks = 0, 1)
+      o.sm[q] = sg.sm[wave][32 * q + r];
+      const uint32_t* cw = reinterpret_cast<const uint32_t*>(sg.codes[wave]);
       if (BITS == 4) {
-        const uint4 c = sg.codes[wave][32 * q + r];
-        w0 = hi ? c.y : c.x;
-        w1 = hi ? c.w : c.z;
+        // row r of set q in slot 32q + r: halves (ks = 0, 1) in words hi and 2 + hi
+        const uint32_t* p = cw + 4 * (32 * q + r) + hi;
+        o.w[q][0] = p[0];
+        o.w[q][1] = p[2];
       } else {
-        // set q's rows 2i, 2i+1 in slot 16q + i: words (row 2i: 0, 1; row 2i+1: 2, 3)
-        const uint4 c = sg.codes[wave][16 * q + r / 2];
-        w0 = (r & 1) ? c.z : c.x;
-        w1 = (r & 1) ? c.w : c.y;
+        // rows 2i, 2i+1 of set q in slot 16q + i: words (row 2i: 0, 1; row 2i+1: 2, 3)
+        const uint32_t* p = cw + 4 * (16 * q + r / 2) + 2 * (r & 1);
+        o.w[q][0] = p[0];
+        o.w[q][1] = p[1];
       }
-      o.b[0][q] = dequant_word<BITS>(w0, hi, smw);
-      o.b[1][q] = dequant_word<BITS>(w1, 2 + hi, smw);
     }
     return o;
+  }
+
+  // keep = 0 (steps past the last) zeroes the scale and min, hence the B operands
+  __device__ __forceinline__ void dequant(Ops& o, const Raw& w, uint32_t keep) const {
+    const int hi = lane >> 5;
+#pragma unroll
+    for (int q = 0; q < kNSet; ++q) {
+      const uint32_t smw = w.sm[q] & keep;
+      o.b[0][q] = dequant_word<BITS>(w.w[q][0], hi, smw);
+      o.b[1][q] = dequant_word<BITS>(w.w[q][1], 2 + hi, smw);
+    }
   }
 
   __device__ __forceinline__ void mma(const Ops& o) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int q = 0; q < kNSet; ++q)
           acc[q][i] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(o.a[ks][i], o.b[ks][q], acc[q][i],
                                                               0, 0, 0);
   }
 
-  // One K-step kb (its operands `cur` already in registers, read from stage S): wait for
-  // step kb + 1's operands and publish them (this wave's reads of step kb have completed,
-  // so after the barrier no wave reads stage S any more), request step kb + kRbStages into
-  // stage S, then step kb's matrix-core work with the reads of step kb + 1 placed ahead of
-  // it and their dequantization interleaved with the matrix-core ops, which run while it
-  // executes. Steps past the last one multiply zero B operands (an AND with a uniform
-  // mask, not a branch), so that each step is one basic block in which that order holds.
+  // One K-step kb, S = kb % kRbStages. On entry: step kb's operands `cur` and step kb + 1's
+  // weight words `w1` are in registers. Wait for the A tile of kb + 1 and the words of
+  // kb + 2 and publish them (this wave's reads of step kb - 1 have completed, so after the
+  // barrier no wave reads A slot S or word slot S + 1 any more), request the A tile of
+  // kb + 6 into A slot S and the words of kb + 7 into word slot S + 1, then run step kb's
+  // matrix-core ops with the reads of the A tile of kb + 1 and of the words of kb + 2, and
+  // the dequantization of w1 (no memory access), placed between them. Steps past the last
+  // multiply zero B operands (an AND with a uniform mask, not a branch), so that each step
+  // is one basic block in which that order holds.
   template <int S>
-  __device__ __forceinline__ Ops step(int kb, const Ops& cur) {
+  __device__ __forceinline__ Ops step(int kb, const Ops& cur, Raw& w1) {
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS reads are done
     wait_vmcnt<(kRbStages - 2) * kOps>();
     barrier_after_lds_dma();
-    dma<S>(kb + kRbStages);
+    dma_a<S>(kb + kRbStages);
+    dma_w<(S + 1) % kRbStages>(kb + kRbStages + 1);
     __builtin_amdgcn_sched_barrier(0);
-    Ops next = read_ops<(S + 1) % kRbStages>(kb + 1 < nk ? 0xffffffffu : 0u);
+    Ops next;
+    read_a<(S + 1) % kRbStages>(next);
+    const Raw w2 = read_w<(S + 2) % kRbStages>();
+    dequant(next, w1, kb + 1 < nk ? 0xffffffffu : 0u);
     mma(cur);
     // the next step's operands are complete within this step
 #pragma unroll
@@ -269,40 +313,64 @@ struct RbCore {
         asm volatile("" : "+v"(v.x), "+v"(v.y), "+v"(v.z), "+v"(v.w));
         __builtin_memcpy(&next.b[ks][q], &v, 16);
       }
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * 8 + 2 * kNSet, 0);  // LDS reads
+    // M matrix-core ops, R LDS reads (A fragments, 2 code words, the scale/min pair)
+    constexpr int M = 2 * NI * kNSet, R = 2 * NI + 3;
+    constexpr int kRd = (R + M - 1) / M, kValu = NI == 8 ? 3 : 24 / NI;
 #pragma unroll
-    for (int i = 0; i < 16 * kNSet; ++i) {
+    for (int i = 0; i < M; ++i) {
       __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // one matrix-core op
-      __builtin_amdgcn_sched_group_barrier(0x002, 3, 0);  // three VALU instructions
+      if (i * kRd + kRd <= R)
+        __builtin_amdgcn_sched_group_barrier(0x100, kRd, 0);  // LDS reads
+      else if (i * kRd < R)
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU instructions
     }
     __builtin_amdgcn_sched_barrier(0);
+    w1 = w2;
     return next;
   }
 
+  // Request order: words(0), then A(j) and words(j + 1) for j < kRbStages; words(6) once
+  // words(0) and words(1) have been read (word slot 0 is then free). Every step then
+  // requests A(kb + 6) and words(kb + 7) together, so at the top of step kb the batch that
+  // holds A(kb + 1) and words(kb + 2) has kRbStages - 2 batches after it.
   __device__ __forceinline__ void run() {
 #pragma unroll
     for (int q = 0; q < kNSet; ++q)
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
+      for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[q][i][e] = 0.0f;
-    dma<0>(0);
-    dma<1>(1);
-    dma<2>(2);
-    dma<3>(3);
-    dma<4>(4);
-    dma<5>(5);
-    wait_vmcnt<(kRbStages - 1) * kOps>();
+    static_assert(kRbStages == 6, "the request order and the loop below are written for six");
+    dma_w<0>(0);
+    dma_a<0>(0);
+    dma_w<1>(1);
+    dma_a<1>(1);
+    dma_w<2>(2);
+    dma_a<2>(2);
+    dma_w<3>(3);
+    dma_a<3>(3);
+    dma_w<4>(4);
+    dma_a<4>(4);
+    dma_w<5>(5);
+    dma_a<5>(5);
+    // words(0), A(0), words(1) have landed: after them come A(1..5) and words(2..5)
+    wait_vmcnt<5 * kDmaA + 4 * 2>();
     barrier_after_lds_dma();
-    Ops o0 = read_ops<0>(0xffffffffu);
-    static_assert(kRbStages == 6, "the loop below is unrolled over the ring");
+    Ops o0;
+    read_a<0>(o0);
+    const Raw w0 = read_w<0>();
+    Raw w1 = read_w<1>();
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0) before word slot 0 is refilled
+    dma_w<0>(kRbStages);
+    dequant(o0, w0, 0xffffffffu);
     for (int kb = 0; kb < nk; kb += kRbStages) {
-      const Ops o1 = step<0>(kb, o0);
-      const Ops o2 = step<1>(kb + 1, o1);
-      const Ops o3 = step<2>(kb + 2, o2);
-      const Ops o4 = step<3>(kb + 3, o3);
-      const Ops o5 = step<4>(kb + 4, o4);
-      o0 = step<5>(kb + 5, o5);
+      const Ops o1 = step<0>(kb, o0, w1);
+      const Ops o2 = step<1>(kb + 1, o1, w1);
+      const Ops o3 = step<2>(kb + 2, o2, w1);
+      const Ops o4 = step<3>(kb + 3, o3, w1);
+      const Ops o5 = step<4>(kb + 4, o4, w1);
+      o0 = step<5>(kb + 5, o5, w1);
     }
     wait_vmcnt<0>();  // the direct loads past the last step have landed
   }
@@ -315,7 +383,8 @@ struct RbCore {
     nk = nk_;
   }
 
-  // A row m (0..255) of this thread's slot set i, and the byte offset of its segment
+  // A row m of this thread's slot set i (rows 64i .. 64i + 63), and the byte offset of its
+  // segment
   __device__ __forceinline__ int arow_index(int i) const { return ((int)threadIdx.x >> 2) + 64 * i; }
   __device__ __forceinline__ int aseg_bytes() const {
     const int t = threadIdx.x;
@@ -344,8 +413,54 @@ struct RbCore {
 // ---------------------------------------------------------------- gate/up GEMM
 
 // h = bf16(silu(g) * u). Lane l holds column 32*wave + l%32 of rows 32i + 8(q/4) +
-// 4(l/32) + q%4; the wave's 256 x 32 block goes through LDS (the ring is free by then) so
+// 4(l/32) + q%4; the wave's 32*NI x 32 block goes through LDS (the ring is free by then) so
 // that rows leave as 16-byte stores.
+template <int BITS, int NI>
+__device__ __forceinline__ void pf_gateup_tile(
+    RbStage* stages, const uint32_t* __restrict__ gcodes, const uint32_t* __restrict__ gsm,
+    const uint32_t* __restrict__ ucodes, const uint32_t* __restrict__ usm, int d, int f, int e,
+    int g0, int rows, int n0w, const uint16_t* __restrict__ x, const int* __restrict__ tok_of_g,
+    uint16_t* __restrict__ h) {
+  const int nbd = d / kBK;
+  RbCore<BITS, NI> c;
+  c.init(stages, nbd);
+#pragma unroll
+  for (int i = 0; i < RbCore<BITS, NI>::kDmaA; ++i) {
+    const int tok = tok_of_g[g0 + min(c.arow_index(i), rows - 1)];  // padded rows: a valid row
+    c.arow[i] = reinterpret_cast<const char*>(x + (size_t)tok * d) + c.aseg_bytes();
+  }
+  const int n0 = n0w + 32 * c.wave;  // this wave's rows n0 + 0..31: gate (set 0), up (set 1)
+  c.set_weights(gcodes, ucodes, gsm, usm, (size_t)e * nbd * f, f,
+                [&](int, int r) { return n0 + r; });
+  c.run();
+
+  __syncthreads();  // every wave is done with the ring before it is reused
+  uint16_t* stg = reinterpret_cast<uint16_t*>(stages) + c.wave * (kBM * 32);
+  const int lane = c.lane;
+#pragma unroll
+  for (int i = 0; i < NI; ++i)
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int rr = 32 * i + (q / 4) * 8 + (lane / 32) * 4 + (q % 4);
+      const __bf16 v = (__bf16)silu_mul(c.acc[0][i][q], c.acc[1][i][q]);
+      __builtin_memcpy(&stg[rr * 32 + (lane & 31)], &v, 2);
+    }
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // 32*NI rows x 4 chunks of 8 bf16: lane l takes chunk l%4 of rows l/4 + 16p
+  const int col0 = n0 + 8 * (lane & 3);
+  if (col0 < f) {
+#pragma unroll
+    for (int p = 0; p < 2 * NI; ++p) {
+      const int rr = (lane >> 2) + 16 * p;
+      if (rr < rows)
+        *reinterpret_cast<uint4*>(h + (size_t)(g0 + rr) * f + col0) =
+            *reinterpret_cast<const uint4*>(&stg[rr * 32 + 8 * (lane & 3)]);
+    }
+  }
+}
+
 template <int BITS>
 __global__ __launch_bounds__(kRbThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_pf_gateup(
     const uint32_t* __restrict__ gcodes, const uint32_t* __restrict__ gsm,
@@ -360,43 +475,22 @@ __global__ __launch_bounds__(kRbThreads) __attribute__((amdgpu_waves_per_eu(1, 1
   const int mt = item / ntn, nt = item % ntn;
   const int4 tile = load_uniform(tiles + mt);
   const int e = tile.x, g0 = tile.y, rows = tile.z;
-  const int nbd = d / kBK;
-  RbCore<BITS> c;
-  c.init(stages, nbd);
-#pragma unroll
-  for (int i = 0; i < kRbDma; ++i) {
-    const int tok = tok_of_g[g0 + min(c.arow_index(i), rows - 1)];  // padded rows: a valid row
-    c.arow[i] = reinterpret_cast<const char*>(x + (size_t)tok * d) + c.aseg_bytes();
-  }
-  const int n0 = nt * kN + 32 * c.wave;  // this wave's rows n0 + 0..31: gate (set 0), up (set 1)
-  c.set_weights(gcodes, ucodes, gsm, usm, (size_t)e * nbd * f, f,
-                [&](int, int r) { return n0 + r; });
-  c.run();
-
-  __syncthreads();  // every wave is done with the ring before it is reused
-  uint16_t* stg = reinterpret_cast<uint16_t*>(stages) + c.wave * (kBM * 32);
-  const int lane = c.lane;
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-#pragma unroll
-    for (int q = 0; q < 16; ++q) {
-      const int rr = 32 * i + (q / 4) * 8 + (lane / 32) * 4 + (q % 4);
-      const __bf16 v = (__bf16)silu_mul(c.acc[0][i][q], c.acc[1][i][q]);
-      __builtin_memcpy(&stg[rr * 32 + (lane & 31)], &v, 2);
-    }
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // 256 rows x 4 chunks of 8 bf16: lane l takes chunk l%4 of rows l/4 + 16p
-  const int col0 = n0 + 8 * (lane & 3);
-  if (col0 < f) {
-#pragma unroll
-    for (int p = 0; p < 16; ++p) {
-      const int rr = (lane >> 2) + 16 * p;
-      if (rr < rows)
-        *reinterpret_cast<uint4*>(h + (size_t)(g0 + rr) * f + col0) =
-            *reinterpret_cast<const uint4*>(&stg[rr * 32 + 8 * (lane & 3)]);
-    }
+  switch (row_groups(rows)) {
+    case 1:
+      pf_gateup_tile<BITS, 1>(stages, gcodes, gsm, ucodes, usm, d, f, e, g0, rows, nt * kN, x,
+                              tok_of_g, h);
+      break;
+    case 2:
+      pf_gateup_tile<BITS, 2>(stages, gcodes, gsm, ucodes, usm, d, f, e, g0, rows, nt * kN, x,
+                              tok_of_g, h);
+      break;
+    case 4:
+      pf_gateup_tile<BITS, 4>(stages, gcodes, gsm, ucodes, usm, d, f, e, g0, rows, nt * kN, x,
+                              tok_of_g, h);
+      break;
+    default:
+      pf_gateup_tile<BITS, 8>(stages, gcodes, gsm, ucodes, usm, d, f, e, g0, rows, nt * kN, x,
+                              tok_of_g, h);
   }
 }
 
@@ -404,6 +498,45 @@ __global__ __launch_bounds__(kRbThreads) __attribute__((amdgpu_waves_per_eu(1, 1
 
 // Lanes l and l+32 hold column 32q + l%32 of rows 32i + 8(e/4) + 4(l/32) + e%4; 32-row
 // groups wholly inside the tile store without a per-row test.
+template <int BITS, int NI>
+__device__ __forceinline__ void pf_down_tile(RbStage* stages, const uint32_t* __restrict__ dcodes,
+                                             const uint32_t* __restrict__ dsm, int d, int f,
+                                             int e, int g0, int rows, int c0w,
+                                             const uint16_t* __restrict__ h,
+                                             float* __restrict__ y) {
+  const int nbf = f / kBK;
+  RbCore<BITS, NI> c;
+  c.init(stages, nbf);
+#pragma unroll
+  for (int i = 0; i < RbCore<BITS, NI>::kDmaA; ++i)
+    c.arow[i] = reinterpret_cast<const char*>(h + (size_t)(g0 + min(c.arow_index(i), rows - 1)) * f) +
+                c.aseg_bytes();
+  const int c0 = c0w + 64 * c.wave;  // set q: output columns c0 + 32q + 0..31
+  c.set_weights(dcodes, dcodes, dsm, dsm, (size_t)e * nbf * d, d,
+                [&](int q, int r) { return c0 + 32 * q + r; });
+  c.run();
+  const int lane = c.lane;
+#pragma unroll
+  for (int q = 0; q < 2; ++q) {
+    const int col = c0 + 32 * q + (lane & 31);
+    if (col >= d) continue;
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      float* yb = y + (size_t)(g0 + 32 * i + (lane / 32) * 4) * d + col;
+      if (32 * i + 32 <= rows) {
+#pragma unroll
+        for (int e2 = 0; e2 < 16; ++e2) yb[(size_t)((e2 / 4) * 8 + (e2 % 4)) * d] = c.acc[q][i][e2];
+      } else if (32 * i < rows) {
+#pragma unroll
+        for (int e2 = 0; e2 < 16; ++e2) {
+          const int rr = 32 * i + (e2 / 4) * 8 + (lane / 32) * 4 + (e2 % 4);
+          if (rr < rows) yb[(size_t)((e2 / 4) * 8 + (e2 % 4)) * d] = c.acc[q][i][e2];
+        }
+      }
+    }
+  }
+}
+
 template <int BITS>
 __global__ __launch_bounds__(kRbThreads) __attribute__((amdgpu_waves_per_eu(1, 1))) void k_pf_down(
     const uint32_t* __restrict__ dcodes, const uint32_t* __restrict__ dsm, int d, int f,
@@ -417,36 +550,18 @@ __global__ __launch_bounds__(kRbThreads) __attribute__((amdgpu_waves_per_eu(1, 1
   const int mt = item / ntn, nt = item % ntn;
   const int4 tile = load_uniform(tiles + mt);
   const int e = tile.x, g0 = tile.y, rows = tile.z;
-  const int nbf = f / kBK;
-  RbCore<BITS> c;
-  c.init(stages, nbf);
-#pragma unroll
-  for (int i = 0; i < kRbDma; ++i)
-    c.arow[i] = reinterpret_cast<const char*>(h + (size_t)(g0 + min(c.arow_index(i), rows - 1)) * f) +
-                c.aseg_bytes();
-  const int c0 = nt * kN + 64 * c.wave;  // set q: output columns c0 + 32q + 0..31
-  c.set_weights(dcodes, dcodes, dsm, dsm, (size_t)e * nbf * d, d,
-                [&](int q, int r) { return c0 + 32 * q + r; });
-  c.run();
-  const int lane = c.lane;
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int col = c0 + 32 * q + (lane & 31);
-    if (col >= d) continue;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      float* yb = y + (size_t)(g0 + 32 * i + (lane / 32) * 4) * d + col;
-      if (32 * i + 32 <= rows) {
-#pragma unroll
-        for (int e2 = 0; e2 < 16; ++e2) yb[(size_t)((e2 / 4) * 8 + (e2 % 4)) * d] = c.acc[q][i][e2];
-      } else if (32 * i < rows) {
-#pragma unroll
-        for (int e2 = 0; e2 < 16; ++e2) {
-          const int rr = 32 * i + (e2 / 4) * 8 + (lane / 32) * 4 + (e2 % 4);
-          if (rr < rows) yb[(size_t)((e2 / 4) * 8 + (e2 % 4)) * d] = c.acc[q][i][e2];
-        }
-      }
-    }
+  switch (row_groups(rows)) {
+    case 1:
+      pf_down_tile<BITS, 1>(stages, dcodes, dsm, d, f, e, g0, rows, nt * kN, h, y);
+      break;
+    case 2:
+      pf_down_tile<BITS, 2>(stages, dcodes, dsm, d, f, e, g0, rows, nt * kN, h, y);
+      break;
+    case 4:
+      pf_down_tile<BITS, 4>(stages, dcodes, dsm, d, f, e, g0, rows, nt * kN, h, y);
+      break;
+    default:
+      pf_down_tile<BITS, 8>(stages, dcodes, dsm, d, f, e, g0, rows, nt * kN, h, y);
   }
 }
 
