@@ -27,6 +27,8 @@ namespace {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int kBM = kPrefillBM;  // pairs per M-tile
 constexpr int kBK = 32;          // one quantization block of the reduction axis
@@ -79,27 +81,44 @@ __device__ __forceinline__ int code_word_index(int seg) {
 }
 
 // 8 codes of one word -> 8 bf16 of fp32(scale*q + min) rounded to nearest even (scale*q
-// is exact in fp32, so the fma rounds once, like the separate multiply and add).
+// is exact in fp32, so the fma rounds once, like the separate multiply and add). The codes
+// are spread one a byte and converted by the byte-to-float conversions (the empty asm keeps
+// the compiler from folding the byte masks into a shift and mask per code), and the bf16
+// pairs are rounded two at a time.
 template <int BITS>
 __device__ __forceinline__ bf16x8 dequant_word(uint32_t w, int seg, uint32_t sm) {
   const float s = half_bits_to_float(sm & 0xffffu), mn = half_bits_to_float(sm >> 16);
   float q[8];
   if (BITS == 4) {
-    // byte j of lo holds code 2j, byte j of hi code 2j+1 (byte-to-float conversions)
-    const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    // byte j of lo holds code 2j, byte j of hi code 2j+1
+    uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu;
+    asm("" : "+v"(lo), "+v"(hi));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       q[2 * j] = (float)((lo >> (8 * j)) & 0xffu);
       q[2 * j + 1] = (float)((hi >> (8 * j)) & 0xffu);
     }
   } else {
+    // codes 0..7 of the half word at bits 2i; byte 0 of t[j] holds code j, byte 1 code j+4
     const uint32_t v = w >> (16 * (seg & 1));
+    uint32_t t[4];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) q[i] = (float)((v >> (2 * i)) & 3u);
+    for (int j = 0; j < 4; ++j) t[j] = (v >> (2 * j)) & 0x0303u;
+    asm("" : "+v"(t[0]), "+v"(t[1]), "+v"(t[2]), "+v"(t[3]));
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      q[j] = (float)(t[j] & 0xffu);
+      q[j + 4] = (float)((t[j] >> 8) & 0xffu);
+    }
   }
   bf16x8 out;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) out[i] = (__bf16)__builtin_fmaf(s, q[i], mn);
+  for (int j = 0; j < 4; ++j) {
+    const f32x2 v = {__builtin_fmaf(s, q[2 * j], mn), __builtin_fmaf(s, q[2 * j + 1], mn)};
+    const bf16x2 r = __builtin_convertvector(v, bf16x2);
+    out[2 * j] = r[0];
+    out[2 * j + 1] = r[1];
+  }
   return out;
 }
 
