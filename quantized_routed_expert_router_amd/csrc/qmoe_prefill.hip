@@ -43,25 +43,45 @@ __global__ __launch_bounds__(1024) void k_pf_prep(const int32_t* __restrict__ of
                                                   int* __restrict__ g_of_p) {
   const int tid = threadIdx.x;
   if (blockIdx.x == 0) {
+    // One thread per expert. The M-tiles are listed longest first: every full tile (in
+    // expert order), then the last, partly filled tiles grouped by the row groups they
+    // compute (8, 4, 2, 1), each group in expert order.
     __shared__ int s_wsum[16];
+    __shared__ int s_total;
     const int lane = tid & (kWave - 1), wave = tid / kWave;
     const int e = tid;
     const int beg = e < E ? offsets[e] : 0;
     const int m = e < E ? offsets[e + 1] - beg : 0;
-    const int cnt = (m + kBM - 1) / kBM;
-    int incl = cnt;
+    const int nfull = m / kBM, rem = m - nfull * kBM;
+    const int cls = rem == 0 ? -1 : rem > 128 ? 0 : rem > 64 ? 1 : rem > 32 ? 2 : 3;
+    int start = 0;  // tiles of the groups listed so far
+    // position of this expert's first tile of a group of v tiles an expert
+    auto place = [&](int v) {
+      int incl = v;
 #pragma unroll
-    for (int off = 1; off < kWave; off <<= 1) {
-      const int o = __shfl_up(incl, off);
-      if (lane >= off) incl += o;
+      for (int off = 1; off < kWave; off <<= 1) {
+        const int o = __shfl_up(incl, off);
+        if (lane >= off) incl += o;
+      }
+      if (lane == kWave - 1) s_wsum[wave] = incl;
+      __syncthreads();
+      int base = incl - v;
+      for (int w = 0; w < wave; ++w) base += s_wsum[w];
+      if (tid == 1023) s_total = base + v;
+      __syncthreads();
+      const int pos = start + base;
+      start += s_total;
+      __syncthreads();  // s_wsum and s_total are rewritten by the next group
+      return pos;
+    };
+    const int fb = place(nfull);
+    for (int i = 0; i < nfull; ++i) tiles[fb + i] = make_int4(e, beg + i * kBM, kBM, 0);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const int pb = place(cls == c ? 1 : 0);
+      if (cls == c) tiles[pb] = make_int4(e, beg + nfull * kBM, rem, 0);
     }
-    if (lane == kWave - 1) s_wsum[wave] = incl;
-    __syncthreads();
-    int base = incl - cnt;
-    for (int w = 0; w < wave; ++w) base += s_wsum[w];
-    for (int i = 0; i < cnt; ++i)
-      tiles[base + i] = make_int4(e, beg + i * kBM, min(kBM, m - i * kBM), 0);
-    if (tid == 1023) *ntiles = base + cnt;
+    if (tid == 0) *ntiles = start;
     return;
   }
   const int g = (blockIdx.x - 1) * 1024 + tid;
@@ -122,16 +142,21 @@ __device__ __forceinline__ bf16x8 dequant_word(uint32_t w, int seg, uint32_t sm)
   return out;
 }
 
-// XCD-aware placement. Workgroups are dealt to the 8 XCDs round robin by workgroup id;
-// XCD x takes the contiguous item range [x*per, (x+1)*per) of the live items, so that the
-// consecutive M-tiles of one expert share that XCD's L2 for the expert's weight tiles.
-// The grid is sized for the largest possible item count; returns -1 for idle workgroups.
-__device__ __forceinline__ int xcd_item(int nitems) {
-  const int per = (nitems + 7) / 8;
+// XCD-aware placement. Workgroups are dealt to the 8 XCDs round robin by workgroup id. M-tile
+// mt goes to XCD mt % 8, whose workgroups take its ntn column tiles one after another (they
+// share the A rows in that XCD's L2) and the XCD's M-tiles in list order, longest first, so
+// that the XCDs get equal shares of the long and the short tiles and each ends on short
+// ones. The grid is sized for the largest possible tile count; returns false for idle
+// workgroups.
+__device__ __forceinline__ bool xcd_tile(int ntiles, int ntn, int& mt, int& nt) {
   const int slot = (int)(blockIdx.x / 8);
-  const int item = (int)(blockIdx.x % 8) * per + slot;
-  return (slot < per && item < nitems) ? item : -1;
+  mt = (int)(blockIdx.x % 8) + 8 * (slot / ntn);
+  nt = slot % ntn;
+  return mt < ntiles;
 }
+
+// Workgroups of a launch over at most max_mt M-tiles of ntn column tiles each
+inline int xcd_grid(int max_mt, int ntn) { return ((max_mt + 7) / 8) * 8 * ntn; }
 
 // silu(g) * u in fp32 with the hardware exponential and reciprocal (each within about an
 // ulp; h is rounded to bf16 next)
@@ -489,9 +514,8 @@ __global__ __launch_bounds__(kRbThreads) __attribute__((amdgpu_waves_per_eu(1, 1
   __shared__ RbStage stages[kRbStages];
   constexpr int kN = 4 * 32;  // weight rows a workgroup
   const int ntn = (f + kN - 1) / kN;
-  const int item = xcd_item(load_uniform(ntiles) * ntn);
-  if (item < 0) return;
-  const int mt = item / ntn, nt = item % ntn;
+  int mt, nt;
+  if (!xcd_tile(load_uniform(ntiles), ntn, mt, nt)) return;
   const int4 tile = load_uniform(tiles + mt);
   const int e = tile.x, g0 = tile.y, rows = tile.z;
   switch (row_groups(rows)) {
@@ -564,9 +588,8 @@ __global__ __launch_bounds__(kRbThreads) __attribute__((amdgpu_waves_per_eu(1, 1
   __shared__ RbStage stages[kRbStages];
   constexpr int kN = 4 * 64;  // output columns a workgroup
   const int ntn = (d + kN - 1) / kN;
-  const int item = xcd_item(load_uniform(ntiles) * ntn);
-  if (item < 0) return;
-  const int mt = item / ntn, nt = item % ntn;
+  int mt, nt;
+  if (!xcd_tile(load_uniform(ntiles), ntn, mt, nt)) return;
   const int4 tile = load_uniform(tiles + mt);
   const int e = tile.x, g0 = tile.y, rows = tile.z;
   switch (row_groups(rows)) {
@@ -655,7 +678,7 @@ hipError_t launch_prefill_bits(const PrefillArgs& a) {
 
   const int max_mt = prefill_max_mtiles(P, E);
   if (a.stages & MOE_PREFILL_GATE_UP) {
-    const int gu_items = ((max_mt * ((f + 127) / 128) + 7) / 8) * 8;
+    const int gu_items = xcd_grid(max_mt, (f + 127) / 128);
     hipLaunchKernelGGL(k_pf_gateup<BITS>, dim3(gu_items), dim3(kRbThreads), 0, a.stream,
                        L.gate.codes, reinterpret_cast<const uint32_t*>(L.gate.scale_min),
                        L.up.codes, reinterpret_cast<const uint32_t*>(L.up.scale_min), d, f, tiles,
@@ -664,7 +687,7 @@ hipError_t launch_prefill_bits(const PrefillArgs& a) {
     if (err != hipSuccess) return err;
   }
   if (a.stages & MOE_PREFILL_DOWN) {
-    const int dn_items = ((max_mt * ((d + 255) / 256) + 7) / 8) * 8;
+    const int dn_items = xcd_grid(max_mt, (d + 255) / 256);
     hipLaunchKernelGGL(k_pf_down<BITS>, dim3(dn_items), dim3(kRbThreads), 0, a.stream,
                        L.down.codes, reinterpret_cast<const uint32_t*>(L.down.scale_min), d, f,
                        tiles, ntiles, h, y);
