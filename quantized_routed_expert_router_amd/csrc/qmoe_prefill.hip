@@ -256,10 +256,11 @@ struct RbCore {
     bf16x8 a[2][NI];
     bf16x8 b[2][kNSet];
   };
-  // This lane's packed weight words of one K-step: per set, the code words of the two
-  // halves and the scale/min word.
+  // This lane's packed weight words of one K-step: per set, the scale/min word and the
+  // code words (4-bit: the row's whole 16-byte slot, read without bank conflicts, of which
+  // the lane's half uses words hi and 2 + hi; 2-bit: the two words of its row).
   struct Raw {
-    uint32_t w[kNSet][2];
+    uint32_t w[kNSet][BITS == 4 ? 4 : 2];
     uint32_t sm[kNSet];
   };
 
@@ -283,19 +284,21 @@ struct RbCore {
   __device__ __forceinline__ Raw read_w() const {
     Raw o;
     const RbStage& sg = *st[S];
-    const int r = lane & 31, hi = lane >> 5;
+    const int r = lane & 31;
 #pragma unroll
     for (int q = 0; q < kNSet; ++q) {
       o.sm[q] = sg.sm[wave][32 * q + r];
-      const uint32_t* cw = reinterpret_cast<const uint32_t*>(sg.codes[wave]);
-      if (BITS == 4) {
-        // row r of set q in slot 32q + r: halves (ks = 0, 1) in words hi and 2 + hi
-        const uint32_t* p = cw + 4 * (32 * q + r) + hi;
-        o.w[q][0] = p[0];
-        o.w[q][1] = p[2];
+      if constexpr (BITS == 4) {
+        // row r of set q in slot 32q + r
+        const uint4 c = sg.codes[wave][32 * q + r];
+        o.w[q][0] = c.x;
+        o.w[q][1] = c.y;
+        o.w[q][2] = c.z;
+        o.w[q][3] = c.w;
       } else {
         // rows 2i, 2i+1 of set q in slot 16q + i: words (row 2i: 0, 1; row 2i+1: 2, 3)
-        const uint32_t* p = cw + 4 * (16 * q + r / 2) + 2 * (r & 1);
+        const uint32_t* p =
+            reinterpret_cast<const uint32_t*>(sg.codes[wave]) + 4 * (16 * q + r / 2) + 2 * (r & 1);
         o.w[q][0] = p[0];
         o.w[q][1] = p[1];
       }
@@ -309,8 +312,16 @@ struct RbCore {
 #pragma unroll
     for (int q = 0; q < kNSet; ++q) {
       const uint32_t smw = w.sm[q] & keep;
-      o.b[0][q] = dequant_word<BITS>(w.w[q][0], hi, smw);
-      o.b[1][q] = dequant_word<BITS>(w.w[q][1], 2 + hi, smw);
+      uint32_t w0, w1;  // the code words of the two halves (ks = 0, 1)
+      if constexpr (BITS == 4) {
+        w0 = hi ? w.w[q][1] : w.w[q][0];
+        w1 = hi ? w.w[q][3] : w.w[q][2];
+      } else {
+        w0 = w.w[q][0];
+        w1 = w.w[q][1];
+      }
+      o.b[0][q] = dequant_word<BITS>(w0, hi, smw);
+      o.b[1][q] = dequant_word<BITS>(w1, 2 + hi, smw);
     }
   }
 
