@@ -20,6 +20,10 @@ Reported:
                 of that kernel alone, launched back to back over the rotating instances
                 (each replaying its own step's gate/up stage);
   step_us_percentiles  p10 / p50 / p90 of event-bracketed steps;
+  cache_variants (configs 2 and 3) p10 / p50 / p90 of event-bracketed steps with the
+                layer instances in turn, with a 1 GiB scratch write ahead of every step
+                (outside its events), and warm (one instance repeated);
+  seed, source  the generator seed (0), a hash of the library sources and the git commit;
   cpu_baseline  the CPU oracle on the host, on a bounded sample of the same steps: on all
                 physical cores the process may use (capped by OMP_NUM_THREADS), with the
                 single-thread rate and the core counts beside it;
@@ -183,6 +187,53 @@ def percentiles(ms_list):
             "how": "HIP events around every step on the launch stream (about 1 us each)"}
 
 
+def event_steps(torch, steps, order, enqueue_estimate, before=None):
+    """Per-step GPU times (ms) of steps[i].full for i in order, one event pair around each
+    step only. `before(stream)`, if given, is enqueued ahead of each step's first event, so
+    its work is not in the measured span. A spin kernel holds the queue while the host
+    enqueues everything."""
+    sh = torch.cuda.current_stream().cuda_stream
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in order]
+    cycles = sleep_cycles_for(torch, max(0.02, 2.0 * enqueue_estimate))
+    torch.cuda.synchronize()
+    torch.cuda._sleep(cycles)
+    for (e0, e1), i in zip(evs, order):
+        if before is not None:
+            before(sh)
+        e0.record()
+        steps[i].full(sh)
+        e1.record()
+    torch.cuda.synchronize()
+    return [e0.elapsed_time(e1) for e0, e1 in evs]
+
+
+def source_ids():
+    """What the timed kernels were built from: a hash of the library sources (the C ABI
+    header and every HIP source and header of the package), and the git commit when the
+    tree is a checkout (null otherwise)."""
+    import glob
+    import hashlib
+    import subprocess
+
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "quantized_routed_expert_router_amd", "csrc")
+    files = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")) +
+                   glob.glob(os.path.join(csrc, "*.hip")) + glob.glob(os.path.join(csrc, "*.h")))
+    for f in files:
+        h.update(os.path.relpath(f, ROOT).encode())
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    sha = None
+    try:
+        res = subprocess.run(["git", "-C", ROOT, "rev-parse", "HEAD"], capture_output=True,
+                             text=True, timeout=10)
+        sha = res.stdout.strip() if res.returncode == 0 and res.stdout.strip() else None
+    except (OSError, subprocess.SubprocessError):
+        sha = None
+    return {"library_sources_sha256_16": h.hexdigest()[:16], "git_sha": sha}
+
+
 def touched_experts(routing) -> int:
     off = routing.expert_offsets.cpu()
     return int(((off[1:] - off[:-1]) > 0).sum())
@@ -339,6 +390,35 @@ def bench_decode(args, torch, q, synth, workloads):
     gu_ms, _, _, covered_g = timed_region(torch, steps, order, False, est, call="gate_up")
     if not (covered and covered_i and covered_g):
         log("warning: the host enqueue outlasted the spin kernel; gaps may be included")
+    variants = None
+    if args.config in (2, 3):
+        # cache variants: a 1 GiB scratch write ahead of every step (outside its events),
+        # and one instance repeated (its touched experts stay in the 256 MB memory-side
+        # cache: the warm number)
+        K = min(len(order), 100)
+        per = est / max(1, len(order))
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        fl_ms = event_steps(torch, steps, order[:K], 3.0 * per * K,
+                            before=lambda sh_: scratch.fill_(1))
+        del scratch
+        wm_ms = event_steps(torch, steps, [0] * K, 2.0 * per * K)
+
+        def _variant(ms, idx, how):
+            p = percentiles(ms)
+            p["how"] = how
+            p["value_GBs_at_p50"] = round(
+                float(np.mean([step_bytes[i] for i in idx])) / (p["p50"] * 1e-6) / 1e9, 1)
+            return p
+
+        variants = {
+            "rotate_instances": _variant(step_ms["step"], order,
+                                         f"{L} layer instances in turn (the timed value's "
+                                         "workload), an event pair around each step"),
+            "flush_1GiB": _variant(fl_ms, order[:K], "instances in turn, a 1 GiB scratch "
+                                   "write before each step, outside its event pair"),
+            "warm_one_instance": _variant(wm_ms, [0] * K, "one instance repeated: its "
+                                          "touched experts stay in the memory-side cache"),
+        }
 
     sec = total_ms * 1e-3
     tot_bytes = sum(step_bytes[i] for i in order)
@@ -367,6 +447,7 @@ def bench_decode(args, torch, q, synth, workloads):
         "touched_experts_per_step": round(mean_touched, 2),
         "stage_us": stage_us,
         "step_us_percentiles": percentiles(step_ms["step"]),
+        "cache_variants": variants,
         "roofline": {"bound": "hbm", "kernel": "k_gateup (gate/up + SwiGLU)",
                      "achieved": round(gu_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(gu_ach / HBM_PEAK_GBS, 4),
@@ -595,6 +676,7 @@ def main():
         print("bench.py measures the routed-expert layer on exactly one MI355X; rerun with "
               "--gpus 1.", file=sys.stderr)
         sys.exit(2)
+    source = source_ids()  # before the GPU is touched (it may start git)
     import torch
 
     from quantized_routed_expert_router_amd import qmoe as q
@@ -616,6 +698,8 @@ def main():
         rec = bench_chain(args, torch, q, synth, workloads)
     else:
         rec = bench_prefill(args, torch, q, synth, workloads)
+    rec["seed"] = 0
+    rec["source"] = source
     headline = (args.config == 2 and not args.shared and not args.router
                 and args.experts == 512 and not args.instances)
     if headline and not args.no_supplementary:
@@ -627,7 +711,8 @@ def _summary(r):
     """The figures of one supplementary record that the headline line carries."""
     keep = ("value", "unit", "ms_per_step", "tokens_per_s", "pct_of_hbm_peak",
             "expert_bytes_per_step", "expert_bytes_per_token", "touched_experts_per_step",
-            "layer_tflops", "stage_us", "step_us_percentiles", "graph", "steps")
+            "layer_tflops", "stage_us", "step_us_percentiles", "cache_variants", "graph",
+            "steps")
     out = {k: r[k] for k in keep if k in r}
     out["workload"] = r["config"]["workload"]
     if r.get("roofline"):

@@ -59,3 +59,23 @@ def test_bench_refuses_more_than_one_gpu():
     res = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True,
                          text=True, timeout=120)
     assert res.returncode == 2 and "exactly one" in res.stderr
+
+
+def test_source_ids_track_the_library_sources(tmp_path, monkeypatch):
+    ids = bench.source_ids()
+    h = ids["library_sources_sha256_16"]
+    assert len(h) == 16 and int(h, 16) >= 0
+    assert ids["git_sha"] is None or len(ids["git_sha"]) == 40
+    # the hash covers the header and the HIP sources: a copy of the tree with one source
+    # byte changed hashes differently, and an unchanged copy (no git) the same
+    import shutil
+
+    root = tmp_path / "tree"
+    for sub in ("include", "quantized_routed_expert_router_amd/csrc"):
+        shutil.copytree(bench.os.path.join(bench.ROOT, sub), root / sub)
+    monkeypatch.setattr(bench, "ROOT", str(root))
+    same = bench.source_ids()
+    assert same["library_sources_sha256_16"] == h and same["git_sha"] is None
+    src = root / "quantized_routed_expert_router_amd/csrc/qmoe_prefill.hip"
+    src.write_bytes(src.read_bytes() + b"\n")
+    assert bench.source_ids()["library_sources_sha256_16"] != h
