@@ -28,6 +28,7 @@ namespace {
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
 typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
 
 constexpr int kBM = kPrefillBM;  // pairs per M-tile
@@ -551,7 +552,10 @@ __global__ __launch_bounds__(kRbThreads) __attribute__((amdgpu_waves_per_eu(1, 1
 // ---------------------------------------------------------------- down GEMM
 
 // Lanes l and l+32 hold column 32q + l%32 of rows 32i + 8(e/4) + 4(l/32) + e%4; 32-row
-// groups wholly inside the tile store without a per-row test.
+// groups wholly inside the tile store without a per-row test. The fp32 pair outputs
+// (671 MB at the 8192-token chunk, more than the 256 MB memory-side cache) are stored
+// non-temporally: left dirty in that cache, their write-back competed with the combine's
+// reads of them (172 against 146 us for the combine).
 template <int BITS, int NI>
 __device__ __forceinline__ void pf_down_tile(RbStage* stages, const uint32_t* __restrict__ dcodes,
                                              const uint32_t* __restrict__ dsm, int d, int f,
@@ -579,12 +583,12 @@ __device__ __forceinline__ void pf_down_tile(RbStage* stages, const uint32_t* __
       float* yb = y + (size_t)(g0 + 32 * i + (lane / 32) * 4) * d + col;
       if (32 * i + 32 <= rows) {
 #pragma unroll
-        for (int e2 = 0; e2 < 16; ++e2) yb[(size_t)((e2 / 4) * 8 + (e2 % 4)) * d] = c.acc[q][i][e2];
+        for (int e2 = 0; e2 < 16; ++e2) __builtin_nontemporal_store(c.acc[q][i][e2], &yb[(size_t)((e2 / 4) * 8 + (e2 % 4)) * d]);
       } else if (32 * i < rows) {
 #pragma unroll
         for (int e2 = 0; e2 < 16; ++e2) {
           const int rr = 32 * i + (e2 / 4) * 8 + (lane / 32) * 4 + (e2 % 4);
-          if (rr < rows) yb[(size_t)((e2 / 4) * 8 + (e2 % 4)) * d] = c.acc[q][i][e2];
+          if (rr < rows) __builtin_nontemporal_store(c.acc[q][i][e2], &yb[(size_t)((e2 / 4) * 8 + (e2 % 4)) * d]);
         }
       }
     }
@@ -621,8 +625,8 @@ __global__ __launch_bounds__(kRbThreads) __attribute__((amdgpu_waves_per_eu(1, 1
 // ---------------------------------------------------------------- combine
 
 // One workgroup per token, 4 columns per thread: the token's k pair-output rows are all
-// requested before the first is summed, then residual[t] += sum_j w[t][j] * y[g(t,j)] in
-// slot order (binary64, one rounding).
+// requested (non-temporal loads: each is read once) before the first is summed, then
+// residual[t] += sum_j w[t][j] * y[g(t,j)] in slot order (binary64, one rounding).
 constexpr int kCombineBatch = 16;
 
 __global__ __launch_bounds__(1024) void k_pf_combine(const float* __restrict__ y,
@@ -640,7 +644,8 @@ __global__ __launch_bounds__(1024) void k_pf_combine(const float* __restrict__ y
         if (j0 + i < k) {
           const int g = load_uniform(g_of_p + (size_t)t * k + j0 + i);
           wj[i] = w[(size_t)t * k + j0 + i];
-          v[i] = *reinterpret_cast<const float4*>(y + (size_t)g * d + c);
+          const f32x4 t = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(y + (size_t)g * d + c));
+          v[i] = make_float4(t[0], t[1], t[2], t[3]);
         }
       }
 #pragma unroll
