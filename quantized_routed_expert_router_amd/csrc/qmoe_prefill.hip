@@ -194,7 +194,9 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // power; leaving out the direct loads, the dequantization or the LDS reads each saves
 // 100-190 us, and waiting for older data does not, so the loads cost issue slots and power,
 // not latency. Weights dequantized once per chunk into bf16 for the experts with several
-// M-tiles made the gate/up GEMM no faster, and the dequantization pass itself cost 158 us.)
+// M-tiles made the gate/up GEMM no faster, and the dequantization pass itself cost 158 us.
+// Tiles of 128 pairs, two workgroups a CU and so two waves a SIMD, measured the same:
+// twice the dequantization per flop pays for the latency the second wave hides.)
 constexpr int kRbThreads = 256;
 constexpr int kRbStages = 6;                       // K-steps in flight
 constexpr int kRbSlots = kBM * kBK * 2 / 16;       // 16-byte slots of a full A tile (1024)
