@@ -170,3 +170,31 @@ def test_prefill_config5_untouched_tokens_finite_and_changed(cfg5):
     assert np.isfinite(out).all()
     changed = (out != res).any(axis=1)
     assert changed.all(), f"{(~changed).sum()} tokens without an update"
+
+
+# Pairs per expert spanning every row-group boundary of the M-tiles (1, 2, 4 or 8 groups of
+# 32 rows computed in a 256-row tile) and tiles of one expert past the first.
+PLANTED_COUNTS = [1, 31, 32, 33, 63, 64, 65, 127, 128, 129, 255, 256, 257, 511, 513]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_prefill_row_group_boundaries(bits):
+    E, d, f, k = len(PLANTED_COUNTS), 128, 96, 1
+    n = sum(PLANTED_COUNTS)
+    w = synth.Workload("small", d, f, E, k, n, bits, "normal", seed=5)
+    host = synth.host_layer(w, 0)
+    _, x = synth.layer_inputs(w, 0)
+    # top-1 routing planted through the logits: token t goes to expert owner[t], tokens in
+    # a shuffled order so that every tile gathers scattered rows
+    owner = np.repeat(np.arange(E), PLANTED_COUNTS)
+    np.random.default_rng(5).shuffle(owner)
+    lg = (0.1 * np.random.default_rng(6).standard_normal((n, E))).astype(np.float32)
+    lg[np.arange(n), owner] = 10.0
+    dev = workloads.layer_from_host(*host, k)
+    routing, out, xb, res = _run_prefill(dev, lg, x, k)
+    ids, wt = check_routing(lg, k, routing)
+    assert np.array_equal(ids[:, 0], owner)
+    counts = np.diff(routing.expert_offsets.cpu().numpy())
+    assert counts.tolist() == PLANTED_COUNTS
+    out_o, _ = O.ffn_prefill(*(omat(h) for h in host), E, xb, ids, wt, res)
+    _check(out, out_o, res)
