@@ -1,5 +1,5 @@
 // Stand-ins for the library's kernel launchers, linked with the ABI file alone for the
-// host sanitizer build: the driver makes only calls that are rejected, or accepted with
+// host sanitizer build: the test program makes only calls that are rejected, or accepted with
 // nothing to enqueue, before a launcher would run, so reaching one is an error.
 #include <stdio.h>
 #include <stdlib.h>
