@@ -198,7 +198,7 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
 // Tiles of 128 pairs, two workgroups a CU and so two waves a SIMD, measured the same:
 // twice the dequantization per flop pays for the latency the second wave hides.)
 constexpr int kRbThreads = 256;
-constexpr int kRbStages = 6;                       // K-steps in flight
+constexpr int kRbStages = 4;                       // K-steps in flight
 constexpr int kRbSlots = kBM * kBK * 2 / 16;       // 16-byte slots of a full A tile (1024)
 
 struct RbStage {
@@ -343,7 +343,7 @@ struct RbCore {
   // weight words `w1` are in registers. Wait for the A tile of kb + 1 and the words of
   // kb + 2 and publish them (this wave's reads of step kb - 1 have completed, so after the
   // barrier no wave reads A slot S or word slot S + 1 any more), request the A tile of
-  // kb + 6 into A slot S and the words of kb + 7 into word slot S + 1, then run step kb's
+  // kb + 4 into A slot S and the words of kb + 5 into word slot S + 1, then run step kb's
   // matrix-core ops with the reads of the A tile of kb + 1 and of the words of kb + 2, and
   // the dequantization of w1 (no memory access), placed between them. Steps past the last
   // multiply zero B operands (an AND with a uniform mask, not a branch), so that each step
@@ -388,10 +388,12 @@ struct RbCore {
     return next;
   }
 
-  // Request order: words(0), then A(j) and words(j + 1) for j < kRbStages; words(6) once
+  // Request order: words(0), then A(j) and words(j + 1) for j < kRbStages; words(4) once
   // words(0) and words(1) have been read (word slot 0 is then free). Every step then
-  // requests A(kb + 6) and words(kb + 7) together, so at the top of step kb the batch that
-  // holds A(kb + 1) and words(kb + 2) has kRbStages - 2 batches after it.
+  // requests A(kb + 4) and words(kb + 5) together, so at the top of step kb the batch that
+  // holds A(kb + 1) and words(kb + 2) has kRbStages - 2 batches after it. A ring of four
+  // steps divides the usual reduction lengths (64 and 24 steps at d = 2048, f = 768), so no
+  // step runs past the last one there.
   __device__ __forceinline__ void run() {
 #pragma unroll
     for (int q = 0; q < kNSet; ++q)
@@ -399,7 +401,7 @@ struct RbCore {
       for (int i = 0; i < NI; ++i)
 #pragma unroll
         for (int e = 0; e < 16; ++e) acc[q][i][e] = 0.0f;
-    static_assert(kRbStages == 6, "the request order and the loop below are written for six");
+    static_assert(kRbStages == 4, "the request order and the loop below are written for four");
     dma_w<0>(0);
     dma_a<0>(0);
     dma_w<1>(1);
@@ -408,12 +410,8 @@ struct RbCore {
     dma_a<2>(2);
     dma_w<3>(3);
     dma_a<3>(3);
-    dma_w<4>(4);
-    dma_a<4>(4);
-    dma_w<5>(5);
-    dma_a<5>(5);
-    // words(0), A(0), words(1) have landed: after them come A(1..5) and words(2..5)
-    wait_vmcnt<5 * kDmaA + 4 * 2>();
+    // words(0), A(0), words(1) have landed: after them come A(1..3) and words(2..3)
+    wait_vmcnt<3 * kDmaA + 2 * 2>();
     barrier_after_lds_dma();
     Ops o0;
     read_a<0>(o0);
@@ -426,9 +424,7 @@ struct RbCore {
       const Ops o1 = step<0>(kb, o0, w1);
       const Ops o2 = step<1>(kb + 1, o1, w1);
       const Ops o3 = step<2>(kb + 2, o2, w1);
-      const Ops o4 = step<3>(kb + 3, o3, w1);
-      const Ops o5 = step<4>(kb + 4, o4, w1);
-      o0 = step<5>(kb + 5, o5, w1);
+      o0 = step<3>(kb + 3, o3, w1);
     }
     wait_vmcnt<0>();  // the direct loads past the last step have landed
   }
