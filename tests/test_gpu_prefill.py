@@ -164,6 +164,32 @@ def test_prefill_config5_every_mtile(cfg5):
     _check(out, out_o, res, tokens)
 
 
+@pytest.fixture(scope="module")
+def cfg5_2bit():
+    # the 8192-token chunk with 2-bit weights (the same shape, logits and activations)
+    import dataclasses
+
+    w = dataclasses.replace(synth.config(5), name="prefill8192_2bit", bits=2)
+    layer = workloads.device_layer(w, 0)
+    lg, x = synth.layer_inputs(w, 0)
+    routing, out, xb, res = _run_prefill(layer, lg, x, w.k)
+    return w, lg, x, routing, out, xb, res
+
+
+def test_prefill_config5_2bit_every_mtile(cfg5_2bit):
+    # the 2-bit GEMM instances (half-word codes, row pairs in a code slot) over the full
+    # chunk, compared on the tokens at the edges of every M-tile like the 4-bit chunk
+    w, lg, _, routing, out, xb, res = cfg5_2bit
+    ids, wt = check_routing(lg, w.k, routing)
+    off, pidx = O.group(ids, w.E)
+    tokens, ntiles = mtile_edge_tokens(off, pidx, w.k, PREFILL_TILE_ROWS)
+    assert ntiles > 300 and len(tokens) > 500
+    host = synth.host_layer(w, 0, experts=np.unique(ids[tokens]))
+    out_o, _ = O.ffn_prefill(*(omat(h) for h in host), w.E, xb, ids, wt, res, tokens=tokens)
+    _check(out, out_o, res, tokens)
+    assert np.isfinite(out).all() and (out != res).any(axis=1).all()
+
+
 def test_prefill_config5_untouched_tokens_finite_and_changed(cfg5):
     # every token of the chunk got an MoE update (no tile or row was skipped)
     _, _, _, _, out, _, res = cfg5
