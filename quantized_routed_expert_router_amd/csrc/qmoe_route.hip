@@ -105,9 +105,11 @@ __global__ __launch_bounds__(kScatterThreads) void k_group_scatter(
   __shared__ int s_wsum[kScatterWaves];
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
   const int b = blockIdx.x;
-  // expert totals and the pairs of each expert in earlier chunks
+  // expert totals and the pairs of each expert in earlier chunks (unrolled, so that several
+  // histogram loads are in flight instead of one round trip per chunk)
   for (int e = tid; e < E; e += kScatterThreads) {
     int tot = 0, before = 0;
+#pragma unroll 8
     for (int c = 0; c < nchunks; ++c) {
       const int v = hist[(size_t)c * E + e];
       tot += v;
