@@ -205,8 +205,9 @@ moe_status moe_expert_ffn_decode_stages(const moe_layer* L, const float* x, int 
                                         void* stream);
 
 /* The whole routed-expert layer for a decode window: moe_route followed by
- * moe_expert_ffn_decode on the same arguments, with the routing done inside the first
- * kernel of the layer. The router hands expert ids and weights to the expert pass
+ * moe_expert_ffn_decode on the same arguments. Windows of up to 16 tokens are routed inside
+ * the first kernel of the layer, larger ones by the routing kernels of moe_route launched
+ * first. The router hands expert ids and weights to the expert pass
  * (Strata engine explainer, m.lqnn.cn/news/264700, "Doorbell handshake": routing ends
  * the first half of a layer, combine and residual write-back end the second). logits:
  * device fp32 [n][E], or NULL when the layer has router weights (L->router_w): the

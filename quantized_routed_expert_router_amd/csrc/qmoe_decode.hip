@@ -193,7 +193,7 @@ __global__ __launch_bounds__(kPrepThreads) void k_prep(
 // builds the work list without leaving LDS, writing the routing outputs on the way; the
 // other blocks quantize x meanwhile. Without GROUP, block 0 stops after the top-k: the
 // gate/up kernel then takes its chunks from the expert ids and writes the grouping.
-constexpr int kFusedMaxTokens = 64;
+constexpr int kFusedMaxTokens = 16;
 constexpr int kFusedMaxPairs = kFusedMaxTokens * MOE_MAX_TOP_K;
 constexpr int kFusedGroupWaves = 8;
 

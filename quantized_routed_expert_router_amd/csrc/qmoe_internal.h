@@ -255,6 +255,10 @@ struct DecodeArgs {
 // kChunkPairs pairs, each with its own expert histogram in the routing workspace.
 constexpr int kSingleGroupPairs = 4096;
 constexpr int kChunkPairs = 2048;
+// Up to this many tokens moe_route selects and groups in one workgroup (k_route_fused).
+// Above it the selection is spread over many workgroups: at 17-32 tokens the two forms
+// take the same time, and from 24 tokens on the spread one is faster.
+constexpr int kFusedRouteTokens = 16;
 
 inline size_t route_workspace_bytes(int n, int E, int k) {
   const long long P = (long long)n * k;

@@ -168,7 +168,7 @@ __global__ __launch_bounds__(kScatterThreads) void k_group_scatter(
 template <int KPL>
 hipError_t launch_route_kpl(const float* logits, int n, int E, int k, const moe_routing* out,
                             void* ws, hipStream_t stream) {
-  if (n <= 64) {
+  if (n <= kFusedRouteTokens) {
     hipLaunchKernelGGL(k_route_fused<KPL>, dim3(1), dim3(kGroupThreads), 0, stream, logits, n, E,
                        k, out->topk_ids, out->topk_w, out->expert_offsets, out->pair_index);
     return hipGetLastError();

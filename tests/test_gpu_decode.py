@@ -74,7 +74,8 @@ def test_route_golden_ties():
 
 @pytest.mark.parametrize("n,E,k,kind", [
     (1, 8, 2, "normal"), (4, 512, 10, "zipf"), (5, 33, 7, "normal"), (3, 8, 8, "normal"),
-    (6, 100, 1, "normal"), (64, 512, 10, "uniform"), (65, 512, 10, "uniform"),
+    (6, 100, 1, "normal"), (16, 512, 10, "zipf"), (17, 512, 10, "zipf"),
+    (64, 512, 10, "uniform"), (65, 512, 10, "uniform"),
     (256, 512, 10, "uniform"), (8192, 512, 10, "zipf"), (2, 1024, 64, "normal"),
     (300, 1000, 3, "normal"),
     # grouping spread over many workgroups (more than 4096 pairs): ragged last chunk,
@@ -391,9 +392,12 @@ def _layer_vs_two_calls(w, host_or_layer, lg, x, logits_kind=None):
     (8, 256, 128, 2, 1, 4),      # config 1 shape, one expert slot per lane
     (64, 128, 96, 8, 5, 2),      # T = 5 window
     (6, 128, 64, 5, 8, 4),       # 8 tokens, 6 experts: chunks split in two, grouping in gate/up
-    (1024, 64, 64, 64, 64, 4),   # largest fused batch: 4096 pairs, grouped by histograms
+    (1024, 64, 64, 64, 16, 4),   # largest fused window: 1024 pairs, grouped by histograms
+    (16, 64, 64, 4, 16, 2),      # the fused limit
+    (16, 64, 64, 4, 17, 2),      # one token past it: separate routing kernels
+    (1024, 64, 64, 64, 64, 4),   # 4096 pairs through the separate kernels, one grouping workgroup
     (100, 96, 64, 3, 64, 4),     # E not a multiple of 64
-    (16, 64, 64, 4, 65, 2),      # one token past the fused limit: separate routing kernels
+    (16, 64, 64, 4, 65, 2),      # past the single-workgroup moe_route limit
 ])
 def test_layer_decode_matches_two_calls(E, d, f, k, n, bits):
     w, host, lg, x = _small(E, d, f, k, n, bits)

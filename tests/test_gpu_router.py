@@ -74,8 +74,9 @@ def _small_layer(E, d, f, k, n, bits, seed):
     (37, 96, 64, 3, 5, 2),      # E not a multiple of the workgroup's 4 experts; d < 512
     (16, 4096, 64, 2, 3, 4),    # two staged column chunks
     (64, 128, 96, 8, 9, 4),     # three token groups, the last ragged
-    (32, 64, 64, 4, 64, 2),     # the largest window routed inside the first layer kernel
-    (32, 64, 64, 4, 65, 4),     # one token more: separate routing kernels
+    (32, 64, 64, 4, 16, 2),     # the largest window routed inside the first layer kernel
+    (32, 64, 64, 4, 17, 4),     # one token more: separate routing kernels
+    (32, 64, 64, 4, 64, 2),     # 64 tokens, 256 pairs grouped by one workgroup
     (100, 160, 64, 3, 300, 4),  # a batch
 ])
 def test_router_small_shapes(E, d, f, k, n, bits):
