@@ -239,6 +239,40 @@ __global__ __launch_bounds__(kPrepThreads) void k_route_prep(
   quant_x_block<BITS>(x, d, gid / nbd, gid % nbd, xq, xsc, dbg_xq, dbg_xs);
 }
 
+// Prep after the spread top-k, for windows past kFusedMaxTokens with at most
+// kSingleGroupPairs pairs: block 0 copies the expert ids into LDS, groups the pairs by
+// expert and builds the work list there, writing the grouping outputs on the way (one
+// launch and one memory round trip fewer than a separate grouping kernel followed by
+// k_prep); the other blocks quantize x.
+template <int BITS>
+__global__ __launch_bounds__(kPrepThreads) void k_group_prep(
+    const float* __restrict__ x, int n, int d, const int32_t* __restrict__ topk_ids, int E,
+    int k, int npc, int32_t* __restrict__ offsets, int32_t* __restrict__ pair_index,
+    int* __restrict__ chunks, int* __restrict__ nchunks, int8_t* __restrict__ xq,
+    double2* __restrict__ xsc, int8_t* __restrict__ dbg_xq, float* __restrict__ dbg_xs) {
+  if (blockIdx.x == 0) {
+    __shared__ int s_ids[kSingleGroupPairs];
+    __shared__ int s_pidx[kSingleGroupPairs];
+    __shared__ int s_off[MOE_MAX_EXPERTS + 1];
+    __shared__ int s_hist[kFusedGroupWaves * MOE_MAX_EXPERTS];
+    __shared__ int s_wsum[kPrepWaves];
+    const int tid = threadIdx.x;
+    const int P = n * k;
+    ids_to_lds<kSingleGroupPairs, kPrepThreads>(topk_ids, P, s_ids);
+    __syncthreads();
+    group_block<kFusedGroupWaves>(s_ids, P, E, s_hist, s_off, s_wsum, s_off, s_pidx);
+    __syncthreads();
+    for (int e = tid; e <= E; e += kPrepThreads) offsets[e] = s_off[e];
+    for (int i = tid; i < P; i += kPrepThreads) pair_index[i] = s_pidx[i];
+    build_work_list(s_off, s_pidx, E, k, npc, chunks, nchunks, s_wsum);
+    return;
+  }
+  const int nbd = d / 32;
+  const int gid = (blockIdx.x - 1) * kPrepThreads + threadIdx.x;
+  if (gid >= n * nbd) return;
+  quant_x_block<BITS>(x, d, gid / nbd, gid % nbd, xq, xsc, dbg_xq, dbg_xs);
+}
+
 // ---------------------------------------------------------------- router projection
 
 // logits[t][e] = sum_c x[t][c] * W[e][c], W bf16 [E][d], x fp32 [n][d] (the layer's router;
@@ -1314,6 +1348,13 @@ hipError_t launch_ffn(const DecodeArgs& a) {
 #undef QMOE_RP
       hipLaunchKernelGGL(kern, dim3(prep_blocks), dim3(kPrepThreads), 0, a.stream, logits, a.x,
                          n, d, E, k, NPC, a.r->topk_ids, a.r->topk_w, a.r->expert_offsets,
+                         a.r->pair_index, chunks, nchunks, xq, xsc, DBG ? dbg.xq : nullptr,
+                         DBG ? dbg.xs : nullptr);
+    } else if (logits && (long long)n * k <= kSingleGroupPairs) {
+      err = launch_route_topk(logits, n, E, k, a.r->topk_ids, a.r->topk_w, a.stream);
+      if (err != hipSuccess) return err;
+      hipLaunchKernelGGL(k_group_prep<BITS>, dim3(prep_blocks), dim3(kPrepThreads), 0, a.stream,
+                         a.x, n, d, a.r->topk_ids, E, k, NPC, a.r->expert_offsets,
                          a.r->pair_index, chunks, nchunks, xq, xsc, DBG ? dbg.xq : nullptr,
                          DBG ? dbg.xs : nullptr);
     } else {

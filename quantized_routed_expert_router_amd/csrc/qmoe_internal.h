@@ -271,6 +271,9 @@ inline size_t route_workspace_bytes(int n, int E, int k) {
 
 hipError_t launch_route(const float* logits, int n, int E, int k, const moe_routing* out,
                         void* ws, hipStream_t stream);
+// The spread top-k alone (one wave a token): expert ids and routing weights, no grouping.
+hipError_t launch_route_topk(const float* logits, int n, int E, int k, int32_t* ids, float* w,
+                             hipStream_t stream);
 hipError_t launch_decode(const DecodeArgs& a);
 hipError_t launch_prefill(const PrefillArgs& a);
 

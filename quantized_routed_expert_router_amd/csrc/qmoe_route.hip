@@ -67,10 +67,13 @@ __global__ __launch_bounds__(kGroupThreads) void k_route_group(const int32_t* __
                                                                int P, int E,
                                                                int32_t* __restrict__ offsets,
                                                                int32_t* __restrict__ pair_index) {
+  __shared__ int s_ids[kSingleGroupPairs];
   __shared__ int s_hist[kGroupWaves * MOE_MAX_EXPERTS];
   __shared__ int s_off[MOE_MAX_EXPERTS + 1];
   __shared__ int s_wsum[kGroupWaves];
-  group_block<kGroupWaves>(ids, P, E, s_hist, s_off, s_wsum, offsets, pair_index);
+  ids_to_lds<kSingleGroupPairs, kGroupThreads>(ids, P, s_ids);
+  __syncthreads();
+  group_block<kGroupWaves>(s_ids, P, E, s_hist, s_off, s_wsum, offsets, pair_index);
 }
 
 // ---- grouping of large batches over many workgroups -------------------------------
@@ -173,9 +176,7 @@ hipError_t launch_route_kpl(const float* logits, int n, int E, int k, const moe_
                        k, out->topk_ids, out->topk_w, out->expert_offsets, out->pair_index);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL(k_route_topk<KPL>, dim3((n + 3) / 4), dim3(256), 0, stream, logits, n, E, k,
-                     out->topk_ids, out->topk_w);
-  hipError_t err = hipGetLastError();
+  hipError_t err = launch_route_topk(logits, n, E, k, out->topk_ids, out->topk_w, stream);
   if (err != hipSuccess) return err;
   const int P = n * k;
   if (P <= kSingleGroupPairs) {
@@ -195,6 +196,18 @@ hipError_t launch_route_kpl(const float* logits, int n, int E, int k, const moe_
 }
 
 }  // namespace
+
+hipError_t launch_route_topk(const float* logits, int n, int E, int k, int32_t* ids, float* w,
+                             hipStream_t stream) {
+  const int kpl = (E + kWave - 1) / kWave;
+  auto kern = kpl <= 1   ? k_route_topk<1>
+              : kpl <= 2 ? k_route_topk<2>
+              : kpl <= 4 ? k_route_topk<4>
+              : kpl <= 8 ? k_route_topk<8>
+                         : k_route_topk<16>;
+  hipLaunchKernelGGL(kern, dim3((n + 3) / 4), dim3(256), 0, stream, logits, n, E, k, ids, w);
+  return hipGetLastError();
+}
 
 hipError_t launch_route(const float* logits, int n, int E, int k, const moe_routing* out,
                         void* ws, hipStream_t stream) {

@@ -226,6 +226,22 @@ __device__ __forceinline__ void block_exclusive_scan(int* v, int n, int* wsum) {
   __syncthreads();
 }
 
+// Copies the P expert ids of a grouping (1 <= P <= MAXP) from global memory into LDS. Every
+// thread issues all its loads (clamped indexes, no branch around them) before its first
+// store, so the copy costs one memory round trip; the counting and the scatter of
+// group_block then read LDS instead of waiting on a load per 64 pairs.
+template <int MAXP, int NT>
+__device__ __forceinline__ void ids_to_lds(const int32_t* __restrict__ ids, int P, int* s_ids) {
+  constexpr int kPer = (MAXP + NT - 1) / NT;
+  const int tid = threadIdx.x;
+  int v[kPer];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j) v[j] = ids[min(tid + j * NT, P - 1)];
+#pragma unroll
+  for (int j = 0; j < kPer; ++j)
+    if (tid + j * NT < P) s_ids[tid + j * NT] = v[j];
+}
+
 // Stable counting sort of pair ids 0..P-1 by ids[p] (ids may live in LDS or global
 // memory), by the first NW waves of the workgroup; the rest of the workgroup only joins
 // the barriers. hist: LDS of NW*E ints; s_off: LDS of E+1 ints, which ends up holding the

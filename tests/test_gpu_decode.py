@@ -395,7 +395,8 @@ def _layer_vs_two_calls(w, host_or_layer, lg, x, logits_kind=None):
     (1024, 64, 64, 64, 16, 4),   # largest fused window: 1024 pairs, grouped by histograms
     (16, 64, 64, 4, 16, 2),      # the fused limit
     (16, 64, 64, 4, 17, 2),      # one token past it: separate routing kernels
-    (1024, 64, 64, 64, 64, 4),   # 4096 pairs through the separate kernels, one grouping workgroup
+    (1024, 64, 64, 64, 64, 4),   # 4096 pairs: the largest grouping inside the prep kernel
+    (1024, 64, 64, 64, 65, 4),   # 4160 pairs: separate routing, grouping over many workgroups
     (100, 96, 64, 3, 64, 4),     # E not a multiple of 64
     (16, 64, 64, 4, 65, 2),      # past the single-workgroup moe_route limit
 ])
