@@ -538,6 +538,38 @@ def test_layer_decode_stages_ids_path_up_to_16_tokens(n, k):
     assert_output_tolerance(res.cpu().numpy() - x, out_o - x, what="moe delta")
 
 
+@pytest.mark.parametrize("n,k,bits", [(17, 4, 4), (40, 3, 2), (100, 10, 4)])
+def test_layer_decode_stages_grouped_in_prep(n, k, bits):
+    # windows past 16 tokens with at most 4096 pairs: the spread top-k, then the prep
+    # launch groups the pairs and builds the work list, so all of the routing is written
+    # by PREP. Expert 5 is in every token: its n pairs span several 8-pair chunks.
+    E, d, f = 32, 256, 128
+    w, host, lg, x = _small(E, d, f, k, n, bits, seed=29)
+    lg[:, 5] = 10.0
+    layer = workloads.layer_from_host(*host, w.k)
+    lg_d, x_d = to_dev(lg), to_dev(x)
+    ws = qmoe.workspace(layer, n)
+    res = x_d.clone()
+    r = qmoe.Routing.empty(n, E, k, "cuda")
+    r.expert_offsets.fill_(-1)
+    r.pair_index.fill_(-1)
+    ids_o, wt_o = O.route(lg, k)
+    off_o, pidx_o = O.group(ids_o, E)
+    assert (ids_o == 5).sum() == n
+    qmoe.layer_decode(layer, lg_d, x_d, res, routing=r, ws=ws, stages=qmoe.DECODE_PREP)
+    torch.cuda.synchronize()
+    assert np.array_equal(r.topk_ids.cpu().numpy(), ids_o)
+    np.testing.assert_array_max_ulp(r.topk_w.cpu().numpy(), wt_o, maxulp=1)
+    assert np.array_equal(r.expert_offsets.cpu().numpy(), off_o)
+    assert np.array_equal(r.pair_index.cpu().numpy()[: n * k], pidx_o)
+    for st in (qmoe.DECODE_GATE_UP, qmoe.DECODE_DOWN | qmoe.DECODE_COMBINE):
+        qmoe.layer_decode(layer, lg_d, x_d, res, routing=r, ws=ws, stages=st)
+    torch.cuda.synchronize()
+    out_o, _ = O.ffn_decode(*(omat(h) for h in host), E, x, ids_o, wt_o, x)
+    assert_output_tolerance(res.cpu().numpy(), out_o)
+    assert_output_tolerance(res.cpu().numpy() - x, out_o - x, what="moe delta")
+
+
 @pytest.mark.parametrize("E,d,f,k,n,bits", [
     (32, 256, 128, 6, 4, 4),   # chunks from the ids: the down stage builds the work list
     (64, 128, 96, 8, 5, 2),    # eight-pair chunks from the ids
