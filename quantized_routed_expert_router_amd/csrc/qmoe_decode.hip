@@ -7,11 +7,14 @@
 // weight rows with 4-wide int8 dot products (section "CPU expert pool"). Kernels here:
 //
 //   k_router_logits  (optional) logits = x . W_r^T from bf16 router rows, binary64 sums.
-//   k_route_prep     top-k routing of up to 64 tokens by one workgroup (one wave per
+//   k_route_prep     top-k routing of up to 16 tokens by one workgroup (one wave per
 //                    token), fused with the int8 block quantization of x by the other
-//                    workgroups; for larger windows it also groups the pairs and builds
-//                    the work list. k_prep does the quantization and the work list after
-//                    a separate routing call.
+//                    workgroups; past the ids path it also groups the pairs and builds
+//                    the work list.
+//   k_group_prep     wider windows (up to 4096 pairs), after the spread top-k: grouping
+//                    and work list in workgroup 0, the quantization of x in the others.
+//                    k_prep does the quantization and the work list after a separate
+//                    routing call.
 //   k_gateup         one workgroup per (chunk of pairs of one expert, 16 or 32 rows of
 //                    f): the gate and up rows of the item stream through raw buffer loads
 //                    (all blocks of a lane at once), exact int32 block dots with v_dot4
