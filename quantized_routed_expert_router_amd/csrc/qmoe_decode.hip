@@ -485,6 +485,10 @@ __device__ __forceinline__ int quant_half_wave(float h, float& scale, int& sum) 
 //   workgroups a CU, 16 blocks a lane) serve the batched work list, whose thousands of
 //   items run in many rounds: 4-8% faster there than eight waves, which serve the ids
 //   path of windows too wide for the token-major down.
+template <int V>
+struct Int {
+  static constexpr int value = V;
+};
 constexpr int kGuRows = 32;   // rows of an h block
 constexpr int kGuGroup = 64;  // blocks per group
 template <int WAVES, int ROWS>
@@ -776,16 +780,19 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<2 * S::kUnroll>();  // this wave's staging loads have landed
       barrier_after_lds_dma();
+      // the block terms of the chunk's first NP pairs (all of them when NP == np)
+      auto blocks = [&](auto np_c) {
+        constexpr int NP = decltype(np_c)::value;
 #pragma unroll
-      for (int u = 0; u < S::kUnroll; ++u) {
-        const int bb = ke + S::kSplit * u;
-        const int b = g0 + bb;
-        if (b < nbd) {
-          const double sc_w = half_bits_to_double(smw[u] & 0xffffu);
-          const double mn_w = half_bits_to_double(smw[u] >> 16);
+        for (int u = 0; u < S::kUnroll; ++u) {
+          const int bb = ke + S::kSplit * u;
+          const int b = g0 + bb;
+          if (b < nbd) {
+            const double sc_w = half_bits_to_double(smw[u] & 0xffffu);
+            const double mn_w = half_bits_to_double(smw[u] >> 16);
 #pragma unroll
-          for (int j = 0; j < NPC; ++j) {
-            if (j < np) {
+            for (int j = 0; j < NP; ++j) {
+              if (NP == NPC && j >= np) continue;
               const int4 a0 = s_act[j][bb][0], a1 = s_act[j][bb][1], scv = s_act[j][bb][2];
               const int a[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
               double2 sc;
@@ -801,6 +808,23 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
             }
           }
         }
+      };
+      // 2-bit 32-row items of a work list (the batched windows, thousands of small
+      // chunks) take one variant per chunk size, without a branch per pair slot. The 4-bit
+      // and the ids-path instances keep the branches: the variants would spill there.
+      if constexpr (ROWS == 32 && NPC == 8 && BITS == 2 && !IDS) {
+        switch (np) {
+          case 1: blocks(Int<1>{}); break;
+          case 2: blocks(Int<2>{}); break;
+          case 3: blocks(Int<3>{}); break;
+          case 4: blocks(Int<4>{}); break;
+          case 5: blocks(Int<5>{}); break;
+          case 6: blocks(Int<6>{}); break;
+          case 7: blocks(Int<7>{}); break;
+          default: blocks(Int<8>{}); break;
+        }
+      } else {
+        blocks(Int<NPC>{});
       }
       // Blocks past the reduction axis leave their loads unused; the empty asm takes every
       // loaded register, so no load is outstanding at the loop's back edge (the compiler
