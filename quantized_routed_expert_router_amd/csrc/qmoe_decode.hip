@@ -489,6 +489,15 @@ template <int V>
 struct Int {
   static constexpr int value = V;
 };
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+typedef int i32x16_t __attribute__((ext_vector_type(16)));
+// 2-bit 32-row work-list items of at least this many pairs take the int8 matrix-core
+// block dots (k_gateup); smaller chunks the per-chunk-size dot4 variants
+constexpr int kMmaMinPairs = 4;
+template <int BITS, int NPC, int WAVES, int ROWS, bool IDS>
+constexpr bool gu_has_mma() {
+  return BITS == 2 && NPC == 8 && WAVES == 4 && ROWS == 32 && !IDS;
+}
 constexpr int kGuRows = 32;   // rows of an h block
 constexpr int kGuGroup = 64;  // blocks per group
 template <int WAVES, int ROWS>
@@ -809,19 +818,91 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
           }
         }
       };
-      // 2-bit 32-row items of a work list (the batched windows, thousands of small
-      // chunks) take one variant per chunk size, without a branch per pair slot. The 4-bit
-      // and the ids-path instances keep the branches: the variants would spill there.
-      if constexpr (ROWS == 32 && NPC == 8 && BITS == 2 && !IDS) {
-        switch (np) {
-          case 1: blocks(Int<1>{}); break;
-          case 2: blocks(Int<2>{}); break;
-          case 3: blocks(Int<3>{}); break;
-          case 4: blocks(Int<4>{}); break;
-          case 5: blocks(Int<5>{}); break;
-          case 6: blocks(Int<6>{}); break;
-          case 7: blocks(Int<7>{}); break;
-          default: blocks(Int<8>{}); break;
+      // The int8 matrix-core form of the block dots (2-bit work-list items of at least
+      // kMmaMinPairs pairs). One v_mfma_i32_32x32x32_i8 computes the exact int32 dots of
+      // one block for the 32 rows of the wave's matrix (N) and up to 32 pair slots (M;
+      // slots past the chunk read a valid slot and are discarded), K = the block's 32
+      // codes. Operand lanes: row (B) or pair (A) lane % 32, codes 16 * (lane / 32) + 0..15;
+      // result register i (< 4) of lane l holds pair 4 * (l / 32) + i of row l % 32. The
+      // lanes' loads hold the two 16-code words of their own block, lanes 0..31 block b0
+      // and lanes 32..63 block b0 + 1; one cross-half swap turns them into the B operands
+      // of both blocks (word h of each for the lanes of half h), and another gives every
+      // lane the scale/min words of both. The code bytes of a word follow the activation
+      // permutation (byte m of (word >> 2s) & 0x03030303 is code 4m + s), so A is the
+      // staged activation half as it stands. The binary64 block terms follow as in the
+      // dot4 form, for the lane's four pair slots.
+      // (a whole group of blocks without a test per block, so that the compiler can issue
+      // the next block's matrix-core op ahead of this block's terms; a partial last group
+      // tests each block)
+      auto mma_blocks = [&](auto partial_c) {
+        constexpr bool kPartial = decltype(partial_c)::value != 0;
+        const int h = lane >> 5;
+        const int am = min(lane & 31, NPC - 1);
+        const i32x16_t zero = {};
+#pragma unroll
+        for (int u = 0; u < S::kUnroll; ++u) {
+          const int b0 = g0 + S::kPW * (wave % S::kKWaves) + S::kSplit * u;  // wave-uniform
+          const auto cw = __builtin_amdgcn_permlane32_swap(w[u][0], w[u][1], false, false);
+          const auto sw = __builtin_amdgcn_permlane32_swap(smw[u], smw[u], false, false);
+          // both blocks' matrix-core ops first, then their terms
+          i32x16_t dots[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int bb = b0 + q - g0;
+            const uint32_t word = q ? cw[1] : cw[0];
+            const i32x4_t bop = {(int)(word & 0x03030303u), (int)((word >> 2) & 0x03030303u),
+                                 (int)((word >> 4) & 0x03030303u),
+                                 (int)((word >> 6) & 0x03030303u)};
+            const int4 av = s_act[am][min(bb, kGuGroup - 1)][h];
+            const i32x4_t aop = {av.x, av.y, av.z, av.w};
+            dots[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, bop, zero, 0, 0, 0);
+          }
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int b = b0 + q;
+            if (!kPartial || b < nbd) {
+              const int bb = b - g0;
+              const uint32_t smq = q ? sw[1] : sw[0];
+              const double sc_w = half_bits_to_double(smq & 0xffffu);
+              const double mn_w = half_bits_to_double(smq >> 16);
+              double2 sc[4];
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                const int4 scv = s_act[4 * h + i][bb][2];
+                __builtin_memcpy(&sc[i], &scv, 16);
+              }
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                acc[i] = __builtin_fma(sc_w * sc[i].x, (double)dots[q][i], acc[i]);
+                acc[i] = __builtin_fma(mn_w, sc[i].y, acc[i]);
+                if (DBG) {
+                  int32_t* dd = mat ? dbg.up_dots : dbg.gate_dots;
+                  const int j = 4 * h + i;
+                  int pj = pid[0];
+#pragma unroll
+                  for (int j2 = 1; j2 < NPC; ++j2) pj = j == j2 ? pid[j2] : pj;
+                  if (dd && j < np) dd[((size_t)pj * f + r) * nbd + b] = dots[q][i];
+                }
+              }
+            }
+          }
+        }
+      };
+      // Other 2-bit 32-row work-list items take one dot4 variant per chunk size, without a
+      // branch per pair slot. The 4-bit and the ids-path instances keep the branches: the
+      // variants would spill there.
+      if constexpr (gu_has_mma<BITS, NPC, WAVES, ROWS, IDS>()) {
+        if (np >= kMmaMinPairs) {
+          if (g0 + kGuGroup <= nbd)
+            mma_blocks(Int<0>{});
+          else
+            mma_blocks(Int<1>{});
+        } else {
+          switch (np) {
+            case 1: blocks(Int<1>{}); break;
+            case 2: blocks(Int<2>{}); break;
+            default: blocks(Int<3>{}); break;
+          }
         }
       } else {
         blocks(Int<NPC>{});
@@ -836,20 +917,29 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
         asm volatile("" ::"v"(smw[u]));
       }
     }
-    // the reduction parts of a row sit in lanes l, l+ROWS, ... (every lane of the row ends
-    // with the same sum: fp addition commutes)
+    if (gu_has_mma<BITS, NPC, WAVES, ROWS, IDS>() && np >= kMmaMinPairs) {
+      // matrix-core form: lane l holds the sums of pair slots 4 * (l / 32) + i of row l % 32
 #pragma unroll
-    for (int j = 0; j < NPC; ++j) {
-#pragma unroll
-      for (int m = ROWS; m < kWave; m *= 2) {
-        const double o = __shfl_xor(acc[j], m);
-        acc[j] = (lane & m) ? o + acc[j] : acc[j] + o;
+      for (int i = 0; i < 4; ++i) {
+        const int j = 4 * (lane >> 5) + i;
+        if (j < np) red[wave][j][rl] = acc[i];
       }
-    }
-    if (lane < ROWS) {
+    } else {
+      // the reduction parts of a row sit in lanes l, l+ROWS, ... (every lane of the row
+      // ends with the same sum: fp addition commutes)
 #pragma unroll
-      for (int j = 0; j < NPC; ++j)
-        if (j < np) red[wave][j][rl] = acc[j];
+      for (int j = 0; j < NPC; ++j) {
+#pragma unroll
+        for (int m = ROWS; m < kWave; m *= 2) {
+          const double o = __shfl_xor(acc[j], m);
+          acc[j] = (lane & m) ? o + acc[j] : acc[j] + o;
+        }
+      }
+      if (lane < ROWS) {
+#pragma unroll
+        for (int j = 0; j < NPC; ++j)
+          if (j < np) red[wave][j][rl] = acc[j];
+      }
     }
     __syncthreads();
     if (ROWS == 16 && wave == 0) {
