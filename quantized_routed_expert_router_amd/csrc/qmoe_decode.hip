@@ -1014,8 +1014,16 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
 
 constexpr int kDnWaves = 4;
 constexpr int kDnThreads = kDnWaves * kWave;
+// MMA: the instance with the matrix-core form for chunks of kMmaMinPairs or more pairs.
+// It needs 144 registers a lane (three waves a SIMD against five without), which costs
+// the dot4 form of small chunks more than the matrix cores save; the host takes it when
+// the window averages kMmaMinPairs or more pairs per busy expert.
+template <int BITS, int NPC, bool MMA>
+constexpr bool dn_has_mma() {
+  return MMA && BITS == 2 && NPC == 8;
+}
 
-template <int BITS, int NPC, bool DBG>
+template <int BITS, int NPC, bool DBG, bool MMA>
 __global__ __launch_bounds__(kDnThreads) void k_down(
     const uint32_t* __restrict__ dcodes, const uint32_t* __restrict__ dsm, int d, int f,
     const int* __restrict__ chunks, const int* __restrict__ nchunks, const int8_t* __restrict__ hq,
@@ -1065,7 +1073,69 @@ __global__ __launch_bounds__(kDnThreads) void k_down(
         smw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, rr * 4, b * d * 4, 0);
       }
     };
+    // Matrix-core form of the block dots (2-bit chunks of at least kMmaMinPairs pairs, as
+    // in k_gateup): per block, two v_mfma_i32_32x32x32_i8 give the exact dots of the
+    // wave's 64 rows (N: rows 0..31, then 32..63) for the pair slots (M). Every lane holds
+    // both code words of its own row; one cross-half swap makes the B operands of the two
+    // row halves (word h for the lanes of half h) and another the scale/min words of rows
+    // lane % 32 and 32 + lane % 32. Lane l then carries pair slots 4 * (l / 32) + i of
+    // those two rows.
+    auto compute_mma = [&](int g0, int s0) {
+      const int h = lane >> 5;
+      const int am = min(lane & 31, NPC - 1);
+      const i32x16_t zero = {};
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int b = g0 + wave + kDnWaves * u;  // wave-uniform
+        const int bb = b - s0;
+        if (b < nbf) {
+          const auto cw = __builtin_amdgcn_permlane32_swap(dw[u][0], dw[u][1], false, false);
+          const auto sw = __builtin_amdgcn_permlane32_swap(smw[u], smw[u], false, false);
+          const int4 av = s_act[am][bb][h];
+          const i32x4_t aop = {av.x, av.y, av.z, av.w};
+          i32x16_t dots[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t word = q ? cw[1] : cw[0];
+            const i32x4_t bop = {(int)(word & 0x03030303u), (int)((word >> 2) & 0x03030303u),
+                                 (int)((word >> 4) & 0x03030303u),
+                                 (int)((word >> 6) & 0x03030303u)};
+            dots[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, bop, zero, 0, 0, 0);
+          }
+          double2 sc[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int4 scv = s_act[4 * h + i][bb][2];
+            __builtin_memcpy(&sc[i], &scv, 16);
+          }
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t smq = q ? sw[1] : sw[0];
+            const double s = half_bits_to_double(smq & 0xffffu);
+            const double m = half_bits_to_double(smq >> 16);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              ay[4 * q + i] = __builtin_fma(s * sc[i].x, (double)dots[q][i], ay[4 * q + i]);
+              ay[4 * q + i] = __builtin_fma(m, sc[i].y, ay[4 * q + i]);
+              if (DBG && dbg.down_dots) {
+                const int j = 4 * h + i, rq = tile * kWave + 32 * q + (lane & 31);
+                int pj = pid[0];
+#pragma unroll
+                for (int j2 = 1; j2 < NPC; ++j2) pj = j == j2 ? pid[j2] : pj;
+                if (j < np && rq < d) dbg.down_dots[((size_t)pj * d + rq) * nbf + b] = dots[q][i];
+              }
+            }
+          }
+        }
+      }
+    };
     auto compute = [&](int g0, int s0) {
+      if constexpr (dn_has_mma<BITS, NPC, MMA>()) {
+        if (np >= kMmaMinPairs) {
+          compute_mma(g0, s0);
+          return;
+        }
+      }
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) {
         const int b = g0 + wave + kDnWaves * u;
@@ -1105,9 +1175,20 @@ __global__ __launch_bounds__(kDnThreads) void k_down(
       }
     }
     __syncthreads();
+    if (dn_has_mma<BITS, NPC, MMA>() && np >= kMmaMinPairs) {
+      // matrix-core form: slot 4 * (lane / 32) + i of rows lane % 32 and 32 + lane % 32
 #pragma unroll
-    for (int j = 0; j < NPC; ++j)
-      if (j < np) red[wave][j][lane] = ay[j];
+      for (int q = 0; q < 2; ++q)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int j = 4 * (lane >> 5) + i;
+          if (j < np) red[wave][j][32 * q + (lane & 31)] = ay[4 * q + i];
+        }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NPC; ++j)
+        if (j < np) red[wave][j][lane] = ay[j];
+    }
     __syncthreads();
     if (wave == 0) {
 #pragma unroll
@@ -1574,9 +1655,15 @@ hipError_t launch_ffn(const DecodeArgs& a) {
     }
     const long long dn_items = max_chunks * ((d + kWave - 1) / kWave);
     const int dn_grid = (int)std::max<long long>(1, std::min<long long>(dn_items, cap));
-    hipLaunchKernelGGL((k_down<BITS, NPC, DBG>), dim3(dn_grid), dim3(kDnThreads), 0, a.stream,
-                       L.down.codes, reinterpret_cast<const uint32_t*>(L.down.scale_min), d, f,
-                       chunks, nchunks, hq, hsc, y, dbg);
+    // the matrix-core instance when the pairs per busy expert average kMmaMinPairs or more
+    auto dn_kernel = k_down<BITS, NPC, DBG, false>;
+    if constexpr (dn_has_mma<BITS, NPC, true>()) {
+      if (P >= (long long)kMmaMinPairs * std::min<long long>(E, P))
+        dn_kernel = k_down<BITS, NPC, DBG, true>;
+    }
+    hipLaunchKernelGGL(dn_kernel, dim3(dn_grid), dim3(kDnThreads), 0, a.stream, L.down.codes,
+                       reinterpret_cast<const uint32_t*>(L.down.scale_min), d, f, chunks, nchunks,
+                       hq, hsc, y, dbg);
     err = hipGetLastError();
     if (err != hipSuccess) return err;
   }
