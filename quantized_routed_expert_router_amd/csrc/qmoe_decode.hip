@@ -491,9 +491,15 @@ struct Int {
 };
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
-// 2-bit 32-row work-list items of at least this many pairs take the int8 matrix-core
-// block dots (k_gateup); smaller chunks the per-chunk-size dot4 variants
+// Expert-major down items of at least this many pairs take the int8 matrix-core block
+// dots (k_down), and the host selects that instance when the window averages this many
+// pairs per busy expert.
 constexpr int kMmaMinPairs = 4;
+// 2-bit 32-row gate/up work-list items: chunks of at least kGuMmaFull pairs take the
+// matrix-core block dots on all eight pair slots, chunks of kGuMmaHalf to 4 pairs the
+// half-slot form (k_gateup), smaller chunks the per-chunk-size dot4 variants
+constexpr int kGuMmaFull = 5;
+constexpr int kGuMmaHalf = 3;
 template <int BITS, int NPC, int WAVES, int ROWS, bool IDS>
 constexpr bool gu_has_mma() {
   return BITS == 2 && NPC == 8 && WAVES == 4 && ROWS == 32 && !IDS;
@@ -819,8 +825,8 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
         }
       };
       // The int8 matrix-core form of the block dots (2-bit work-list items of at least
-      // kMmaMinPairs pairs). One v_mfma_i32_32x32x32_i8 computes the exact int32 dots of
-      // one block for the 32 rows of the wave's matrix (N) and up to 32 pair slots (M;
+      // kGuMmaFull pairs; chunks of kGuMmaHalf to 4 pairs take the half-slot form below).
+      // One v_mfma_i32_32x32x32_i8 computes the exact int32 dots of one block for the 32 rows of the wave's matrix (N) and up to 32 pair slots (M;
       // slots past the chunk read a valid slot and are discarded), K = the block's 32
       // codes. Operand lanes: row (B) or pair (A) lane % 32, codes 16 * (lane / 32) + 0..15;
       // result register i (< 4) of lane l holds pair 4 * (l / 32) + i of row l % 32. The
@@ -888,15 +894,78 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
           }
         }
       };
+      // The half-slot form for chunks of at most 4 pairs: only result registers 0..3 of
+      // lanes 0..31 (pair slots 0..3) hold pairs, so one cross-half swap per register moves
+      // the second block's slots 0..3 into lanes 32..63. Lane l then holds the dots of pair
+      // slots 0..3 of its own loaded block b0 + l / 32 (whose scale/min word it read) and
+      // row l % 32, and the block terms run once per lane for both blocks; the two halves'
+      // sums of a row meet in the final reduction like the dot4 form's parts.
+      auto mma_half_blocks = [&](auto partial_c) {
+        constexpr bool kPartial = decltype(partial_c)::value != 0;
+        const int h = lane >> 5;
+        const int am = min(lane & 31, NPC - 1);
+        const i32x16_t zero = {};
+#pragma unroll
+        for (int u = 0; u < S::kUnroll; ++u) {
+          const int b0 = g0 + S::kPW * (wave % S::kKWaves) + S::kSplit * u;  // wave-uniform
+          const auto cw = __builtin_amdgcn_permlane32_swap(w[u][0], w[u][1], false, false);
+          i32x16_t dots[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const int bb = b0 + q - g0;
+            const uint32_t word = q ? cw[1] : cw[0];
+            const i32x4_t bop = {(int)(word & 0x03030303u), (int)((word >> 2) & 0x03030303u),
+                                 (int)((word >> 4) & 0x03030303u),
+                                 (int)((word >> 6) & 0x03030303u)};
+            const int4 av = s_act[am][min(bb, kGuGroup - 1)][h];
+            const i32x4_t aop = {av.x, av.y, av.z, av.w};
+            dots[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, bop, zero, 0, 0, 0);
+          }
+          int dt[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+            dt[i] = (int)__builtin_amdgcn_permlane32_swap((uint32_t)dots[0][i],
+                                                          (uint32_t)dots[1][i], false, false)[0];
+          const int b = b0 + h;  // the lane's own block
+          if (!kPartial || b < nbd) {
+            const int bb = b - g0;
+            const double sc_w = half_bits_to_double(smw[u] & 0xffffu);
+            const double mn_w = half_bits_to_double(smw[u] >> 16);
+            double2 sc[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int4 scv = s_act[i][bb][2];
+              __builtin_memcpy(&sc[i], &scv, 16);
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              acc[i] = __builtin_fma(sc_w * sc[i].x, (double)dt[i], acc[i]);
+              acc[i] = __builtin_fma(mn_w, sc[i].y, acc[i]);
+              if (DBG) {
+                int32_t* dd = mat ? dbg.up_dots : dbg.gate_dots;
+                int pj = pid[0];
+#pragma unroll
+                for (int j2 = 1; j2 < 4; ++j2) pj = i == j2 ? pid[j2] : pj;
+                if (dd && i < np) dd[((size_t)pj * f + r) * nbd + b] = dt[i];
+              }
+            }
+          }
+        }
+      };
       // Other 2-bit 32-row work-list items take one dot4 variant per chunk size, without a
       // branch per pair slot. The 4-bit and the ids-path instances keep the branches: the
       // variants would spill there.
       if constexpr (gu_has_mma<BITS, NPC, WAVES, ROWS, IDS>()) {
-        if (np >= kMmaMinPairs) {
+        if (np >= kGuMmaFull) {
           if (g0 + kGuGroup <= nbd)
             mma_blocks(Int<0>{});
           else
             mma_blocks(Int<1>{});
+        } else if (np >= kGuMmaHalf) {
+          if (g0 + kGuGroup <= nbd)
+            mma_half_blocks(Int<0>{});
+          else
+            mma_half_blocks(Int<1>{});
         } else {
           switch (np) {
             case 1: blocks(Int<1>{}); break;
@@ -917,7 +986,7 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
         asm volatile("" ::"v"(smw[u]));
       }
     }
-    if (gu_has_mma<BITS, NPC, WAVES, ROWS, IDS>() && np >= kMmaMinPairs) {
+    if (gu_has_mma<BITS, NPC, WAVES, ROWS, IDS>() && np >= kGuMmaFull) {
       // matrix-core form: lane l holds the sums of pair slots 4 * (l / 32) + i of row l % 32
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -1073,8 +1142,8 @@ __global__ __launch_bounds__(kDnThreads) void k_down(
         smw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, rr * 4, b * d * 4, 0);
       }
     };
-    // Matrix-core form of the block dots (2-bit chunks of at least kMmaMinPairs pairs, as
-    // in k_gateup): per block, two v_mfma_i32_32x32x32_i8 give the exact dots of the
+    // Matrix-core form of the block dots (2-bit chunks of at least kMmaMinPairs pairs; the
+    // lane layout of k_gateup's): per block, two v_mfma_i32_32x32x32_i8 give the exact dots of the
     // wave's 64 rows (N: rows 0..31, then 32..63) for the pair slots (M). Every lane holds
     // both code words of its own row; one cross-half swap makes the B operands of the two
     // row halves (word h for the lanes of half h) and another the scale/min words of rows
