@@ -491,15 +491,17 @@ struct Int {
 };
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
 typedef int i32x16_t __attribute__((ext_vector_type(16)));
-// Expert-major down items of at least this many pairs take the int8 matrix-core block
-// dots (k_down), and the host selects that instance when the window averages this many
-// pairs per busy expert.
+// The host selects the matrix-core instance of the expert-major down (k_down) when the
+// window averages at least this many pairs per busy expert.
 constexpr int kMmaMinPairs = 4;
 // 2-bit 32-row gate/up work-list items: chunks of at least kGuMmaFull pairs take the
 // matrix-core block dots on all eight pair slots, chunks of kGuMmaHalf to 4 pairs the
 // half-slot form (k_gateup), smaller chunks the per-chunk-size dot4 variants
 constexpr int kGuMmaFull = 5;
 constexpr int kGuMmaHalf = 3;
+// the same two thresholds in the matrix-core instance of the expert-major down
+constexpr int kDnMmaFull = 5;
+constexpr int kDnMmaHalf = 3;
 template <int BITS, int NPC, int WAVES, int ROWS, bool IDS>
 constexpr bool gu_has_mma() {
   return BITS == 2 && NPC == 8 && WAVES == 4 && ROWS == 32 && !IDS;
@@ -1083,7 +1085,7 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
 
 constexpr int kDnWaves = 4;
 constexpr int kDnThreads = kDnWaves * kWave;
-// MMA: the instance with the matrix-core form for chunks of kMmaMinPairs or more pairs.
+// MMA: the instance with the matrix-core forms (chunks of kDnMmaHalf or more pairs).
 // It needs 144 registers a lane (three waves a SIMD against five without), which costs
 // the dot4 form of small chunks more than the matrix cores save; the host takes it when
 // the window averages kMmaMinPairs or more pairs per busy expert.
@@ -1142,7 +1144,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(
         smw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, rr * 4, b * d * 4, 0);
       }
     };
-    // Matrix-core form of the block dots (2-bit chunks of at least kMmaMinPairs pairs; the
+    // Matrix-core form of the block dots (2-bit chunks of at least kDnMmaFull pairs; the
     // lane layout of k_gateup's): per block, two v_mfma_i32_32x32x32_i8 give the exact dots of the
     // wave's 64 rows (N: rows 0..31, then 32..63) for the pair slots (M). Every lane holds
     // both code words of its own row; one cross-half swap makes the B operands of the two
@@ -1198,10 +1200,62 @@ __global__ __launch_bounds__(kDnThreads) void k_down(
         }
       }
     };
+    // The half-slot form for chunks of at most 4 pairs: result registers 0..3 of lanes
+    // 0..31 (pair slots 0..3) are the only ones holding pairs, so one cross-half swap per
+    // register moves those of the second row half into lanes 32..63. Lane l then holds
+    // pair slots 0..3 of row l of the tile (the dot4 form's layout) and its own loaded
+    // scale/min word, and computes half as many block terms.
+    auto compute_mma_half = [&](int g0, int s0) {
+      const int h = lane >> 5;
+      const int am = min(lane & 31, NPC - 1);
+      const i32x16_t zero = {};
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int b = g0 + wave + kDnWaves * u;  // wave-uniform
+        const int bb = b - s0;
+        if (b < nbf) {
+          const auto cw = __builtin_amdgcn_permlane32_swap(dw[u][0], dw[u][1], false, false);
+          const int4 av = s_act[am][bb][h];
+          const i32x4_t aop = {av.x, av.y, av.z, av.w};
+          i32x16_t dots[2];
+#pragma unroll
+          for (int q = 0; q < 2; ++q) {
+            const uint32_t word = q ? cw[1] : cw[0];
+            const i32x4_t bop = {(int)(word & 0x03030303u), (int)((word >> 2) & 0x03030303u),
+                                 (int)((word >> 4) & 0x03030303u),
+                                 (int)((word >> 6) & 0x03030303u)};
+            dots[q] = __builtin_amdgcn_mfma_i32_32x32x32_i8(aop, bop, zero, 0, 0, 0);
+          }
+          const double s = half_bits_to_double(smw[u] & 0xffffu);
+          const double m = half_bits_to_double(smw[u] >> 16);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int dd = (int)__builtin_amdgcn_permlane32_swap((uint32_t)dots[0][i],
+                                                                 (uint32_t)dots[1][i], false,
+                                                                 false)[0];
+            const int4 scv = s_act[i][bb][2];
+            double2 sc;
+            __builtin_memcpy(&sc, &scv, 16);
+            ay[i] = __builtin_fma(s * sc.x, (double)dd, ay[i]);
+            ay[i] = __builtin_fma(m, sc.y, ay[i]);
+            if (DBG && rvalid && dbg.down_dots && i < np) {
+              int pj = pid[0];
+#pragma unroll
+              for (int j2 = 1; j2 < 4; ++j2) pj = i == j2 ? pid[j2] : pj;
+              dbg.down_dots[((size_t)pj * d + r) * nbf + b] = dd;
+            }
+          }
+        }
+      }
+    };
     auto compute = [&](int g0, int s0) {
       if constexpr (dn_has_mma<BITS, NPC, MMA>()) {
-        if (np >= kMmaMinPairs) {
+        if (np >= kDnMmaFull) {
           compute_mma(g0, s0);
+          return;
+        }
+        if (np >= kDnMmaHalf) {
+          compute_mma_half(g0, s0);
           return;
         }
       }
@@ -1244,7 +1298,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(
       }
     }
     __syncthreads();
-    if (dn_has_mma<BITS, NPC, MMA>() && np >= kMmaMinPairs) {
+    if (dn_has_mma<BITS, NPC, MMA>() && np >= kDnMmaFull) {
       // matrix-core form: slot 4 * (lane / 32) + i of rows lane % 32 and 32 + lane % 32
 #pragma unroll
       for (int q = 0; q < 2; ++q)
