@@ -366,6 +366,38 @@ def test_decode_config3_2bit_batched(T):
     _decode_parity(w, host, lg, x, layer=layer, dots=False)
 
 
+@pytest.mark.parametrize("E", [16, 64])
+def test_decode_2bit_chunk_sizes_planted(E):
+    # Planted top-1 routing that gives 16 experts 1..13, 16, 17 and 3 pairs: with 8-pair
+    # chunks every chunk size 1..8 occurs (9 = 8 + 1, ..., 17 = 8 + 8 + 1), so the 2-bit
+    # work-list kernels run their dot4 variants (1-2 pairs), the half-slot matrix-core form
+    # (3-4 pairs) and the full form (5-8 pairs). At E = 16 the window averages about 8
+    # pairs per busy expert and the host takes the matrix-core instance of the expert-major
+    # down; at E = 64 (the same 16 experts busy) it takes the dot4 instance. d = 352 gives
+    # a partial last group of blocks whose last matrix-core pair straddles the end, f = 96
+    # an odd down reduction length. Dots bit-exact through the debug trace; both the
+    # debug and the timed instances against the oracle.
+    counts = list(range(1, 14)) + [16, 17, 3]
+    assign = np.repeat(np.arange(len(counts)), counts)
+    n = assign.size
+    rng = np.random.default_rng(7)
+    rng.shuffle(assign)
+    w = synth.Workload("planted", 352, 96, E, 1, n, 2, "normal", seed=11)
+    host = synth.host_layer(w, 0)
+    _, x = synth.layer_inputs(w, 0)
+    lg = rng.standard_normal((n, E)).astype(np.float32)
+    lg[np.arange(n), assign] += 20.0
+    ids, _ = O.route(lg, 1)
+    assert np.array_equal(ids[:, 0], assign)
+    _decode_parity(w, host, lg, x, dots=True)
+    layer = workloads.layer_from_host(*host, 1)
+    routing, out, _ = run_decode(layer, lg, x, 1)
+    ids, wt = check_routing(lg, 1, routing)
+    out_o, _ = O.ffn_decode(*(omat(h) for h in host), E, x, ids, wt, x)
+    assert_output_tolerance(out, out_o, what="timed instance residual")
+    assert_output_tolerance(out - x, out_o - x, what="timed instance delta")
+
+
 # ------------------------------------------------------------------ fused layer entry point
 
 def _layer_vs_two_calls(w, host_or_layer, lg, x, logits_kind=None):
