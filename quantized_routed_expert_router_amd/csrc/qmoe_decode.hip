@@ -1700,7 +1700,9 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   const long long max_chunks = std::min<long long>(
       std::min<long long>(P, (long long)E * ((n + NPC - 1) / NPC)),
       (P + NPC - 1) / NPC + std::min<long long>(E, P));
-  const int cap = a.num_cus * 8;
+  // grid cap of the expert-major down, whose workgroups loop over the items past it
+  // (16 a CU measured best against 4, 8 and 64 on the 64-sequence batches)
+  const int cap = a.num_cus * 16;
   // The token-major down (down and combine in one kernel) takes windows of up to 16 tokens
   // and 16 slots a token, d_ff up to 1024, and as many slots as its lanes hold. It reads h
   // in fp32 and quantizes it itself; the expert-major down reads the codes.
