@@ -238,9 +238,9 @@ moe_status moe_layer_decode_stages(const moe_layer* L, const float* logits, cons
 /* moe_layer_decode without a workspace argument, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that forbid
  * allocation). The workspace is the library's static per-GPU array of
- * MOE_NOALLOC_SCRATCH_BYTES bytes (enough for windows of 64 tokens at d_model = 2048,
- * d_ff = 768, top-10 with a shared expert and router weights); nothing is allocated or
- * freed by the call. Arguments, results and errors as moe_layer_decode (dbg = NULL),
+ * MOE_NOALLOC_SCRATCH_BYTES bytes (enough for windows of 128 tokens at d_model = 2048,
+ * d_ff = 768, top-10 with router weights, and for every window a shared expert allows);
+ * nothing is allocated or freed by the call. Arguments, results and errors as moe_layer_decode (dbg = NULL),
  * plus MOE_ERR_WORKSPACE_TOO_SMALL when the sizes need more workspace than the array
  * holds (nothing is enqueued), and MOE_ERR_HIP if the array's device address cannot be
  * resolved. Every call on one GPU uses that GPU's one array, which keeps the last call's

@@ -27,8 +27,9 @@
 //                    projection by token, and the routing-weighted combine into the
 //                    residual (no pair outputs leave the workgroup).
 //   k_hquant         the h quantization alone, when a small window's down runs by expert.
-//   k_down, k_combine  larger windows: the down projection by expert chunk, then the
-//                    slot-order combine in a launch of its own. Folding the combine into
+//   k_down, k_combine  larger windows: the down projection by expert chunk (fp32 pair
+//                    outputs, each a binary64 row sum rounded once), then the slot-order
+//                    binary64 combine in a launch of its own. Folding the combine into
 //                    k_down through a last-arriver counter needs the pair outputs to cross
 //                    XCDs, through device-scope fences (an L2 writeback per workgroup) or
 //                    write-through stores and loads, and both put a chain of memory round
@@ -1098,7 +1099,7 @@ template <int BITS, int NPC, bool DBG, bool MMA>
 __global__ __launch_bounds__(kDnThreads) void k_down(
     const uint32_t* __restrict__ dcodes, const uint32_t* __restrict__ dsm, int d, int f,
     const int* __restrict__ chunks, const int* __restrict__ nchunks, const int8_t* __restrict__ hq,
-    const double2* __restrict__ hsc, double* __restrict__ y, DecodeDebug dbg) {
+    const double2* __restrict__ hsc, float* __restrict__ y, DecodeDebug dbg) {
   constexpr int kUnroll = 8;
   constexpr int kDnGroup = kDnWaves * kUnroll;  // blocks per weight-load group
   constexpr int kDnStage = 2 * kDnGroup;        // blocks per activation staging
@@ -1318,7 +1319,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(
       for (int j = 0; j < NPC; ++j) {
         if (j < np && rvalid) {
           const double v = reduce_waves<NPC, kDnWaves>(red, j, lane);
-          y[(size_t)pid[j] * d + r] = v;
+          y[(size_t)pid[j] * d + r] = (float)v;  // the pair output, rounded once
           if (DBG && dbg.y) dbg.y[(size_t)pid[j] * d + r] = (float)v;
         }
       }
@@ -1328,7 +1329,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(
 
 // ---------------------------------------------------------------- combine
 
-__global__ __launch_bounds__(kThreads) void k_combine(const double* __restrict__ y,
+__global__ __launch_bounds__(kThreads) void k_combine(const float* __restrict__ y,
                                                       const float* __restrict__ w, int n, int d,
                                                       int k, float* residual) {
   const int gid = blockIdx.x * kThreads + threadIdx.x;
@@ -1336,7 +1337,7 @@ __global__ __launch_bounds__(kThreads) void k_combine(const double* __restrict__
   const int t = gid / d, c = gid % d;
   double acc = 0.0;
   for (int j = 0; j < k; ++j)
-    acc += (double)w[(size_t)t * k + j] * y[((size_t)t * k + j) * d + c];
+    acc += (double)w[(size_t)t * k + j] * (double)y[((size_t)t * k + j) * d + c];
   residual[gid] = (float)((double)residual[gid] + acc);
 }
 
@@ -1636,7 +1637,7 @@ hipError_t launch_ffn(const DecodeArgs& a) {
   double2* xsc = reinterpret_cast<double2*>(a.ws + W.xsc);
   int8_t* hq = reinterpret_cast<int8_t*>(a.ws + W.hq);
   double2* hsc = reinterpret_cast<double2*>(a.ws + W.hsc);
-  double* y = reinterpret_cast<double*>(a.ws + W.y);
+  float* y = reinterpret_cast<float*>(a.ws + W.y);
   float* hf = reinterpret_cast<float*>(a.ws + W.hf);
   DecodeDebug dbg{};
   if (DBG) dbg = *a.dbg;
@@ -1681,8 +1682,9 @@ hipError_t launch_ffn(const DecodeArgs& a) {
     } else {
       if (logits) {
         // the histograms of a multi-workgroup grouping live in the pair-output region,
-        // which is only written later (it holds at least 256 bytes per pair, the
-        // histograms at most 2 bytes per pair plus 4 KB)
+        // which is only written later (fp32 rows of d >= 32: at least 128 bytes per pair;
+        // this path runs past 4096 pairs, and the histograms need at most 2 bytes per pair
+        // plus 4 KB)
         err = launch_route(logits, n, E, k, a.r, a.ws + W.y, a.stream);
         if (err != hipSuccess) return err;
       }

@@ -160,7 +160,7 @@ inline DecodeWs decode_ws_layout(int n, int k, int d, int f, bool shared, int ro
   L.hf = o;
   o = align256(o + 4 * P * f);
   L.y = o;
-  o = align256(o + 8 * P * d);
+  o = align256(o + 4 * P * d);
   L.logits = o;
   o = align256(o + 4 * (size_t)n * (size_t)router_E);
   L.total = o;

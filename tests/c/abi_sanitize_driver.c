@@ -169,7 +169,7 @@ int main(void) {
          moe_layer_decode(&ok, (const float*)FAKE(2), x, 4, &r, res, ws, wsb, NULL, NULL),
          MOE_ERR_INVALID_ARGUMENT);
   expect("no-alloc beyond its workspace",
-         moe_layer_decode_noalloc(&ok, (const float*)FAKE(0), x, 128, &r, res, NULL),
+         moe_layer_decode_noalloc(&ok, (const float*)FAKE(0), x, 256, &r, res, NULL),
          MOE_ERR_WORKSPACE_TOO_SMALL);
   expect("no-alloc null layer",
          moe_layer_decode_noalloc(NULL, (const float*)FAKE(0), x, 4, &r, res, NULL),

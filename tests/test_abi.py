@@ -229,7 +229,7 @@ def test_shared_expert_argument_checks():
     a = qmoe.lib.moe_ffn_workspace_bytes(ctypes.byref(_layer(d=2048, f=768, E=512, k=10)), 4, 0)
     b = qmoe.lib.moe_ffn_workspace_bytes(
         ctypes.byref(_with_shared(_layer(d=2048, f=768, E=512, k=10))), 4, 0)
-    assert b >= a + 4 * (768 + 8 * 2048)
+    assert b >= a + 4 * (768 + 4 * 2048)  # per pair: h codes, fp32 pair outputs
     need = b
     assert _decode(_with_shared(_layer(d=2048, f=768, E=512, k=10)), ws_bytes=need - 1) == WS_SMALL
 

@@ -47,10 +47,12 @@ def test_noalloc_matches_layer_decode_two_calls():
 
 
 def test_noalloc_larger_batch_then_small_window():
-    # a 64-token batch (work-list path, grouping in the routing kernel), then one token
-    w = synth.Workload("b64", 2048, 768, 512, 10, 64, 2, "uniform")
+    # a 128-token batch (work-list path, grouping in the routing kernel; 15.7 MiB of
+    # workspace at this shape, the largest window the array holds), then one token
+    w = synth.Workload("b128", 2048, 768, 512, 10, 128, 2, "uniform")
     layer = workloads.device_layer(w, 2)
-    for n in (64, 1):
+    assert qmoe.ffn_workspace_bytes(layer, 128) <= qmoe.NOALLOC_SCRATCH_BYTES
+    for n in (128, 1):
         ww = synth.Workload(w.name, w.d, w.f, w.E, w.k, n, w.bits, w.logits)
         lg, x = synth.layer_inputs(ww, 3 + n)
         res_a, r_a, res_b, r_b = _pair(layer, ww, lg, x)
@@ -61,7 +63,7 @@ def test_noalloc_larger_batch_then_small_window():
 def test_noalloc_rejects_windows_beyond_its_workspace():
     w = synth.config(2)
     layer = workloads.device_layer(w, 0)
-    n = 128  # 25.7 MB of workspace at this shape: more than the array holds
+    n = 256  # 31.4 MiB of workspace at this shape: more than the array holds
     assert qmoe.ffn_workspace_bytes(layer, n) > qmoe.NOALLOC_SCRATCH_BYTES
     lg = torch.zeros((n, w.E), device="cuda")
     x = torch.zeros((n, w.d), device="cuda")
