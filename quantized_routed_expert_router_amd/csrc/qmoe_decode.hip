@@ -829,9 +829,10 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
       };
       // The int8 matrix-core form of the block dots (2-bit work-list items of at least
       // kGuMmaFull pairs; chunks of kGuMmaHalf to 4 pairs take the half-slot form below).
-      // One v_mfma_i32_32x32x32_i8 computes the exact int32 dots of one block for the 32 rows of the wave's matrix (N) and up to 32 pair slots (M;
-      // slots past the chunk read a valid slot and are discarded), K = the block's 32
-      // codes. Operand lanes: row (B) or pair (A) lane % 32, codes 16 * (lane / 32) + 0..15;
+      // One v_mfma_i32_32x32x32_i8 computes the exact int32 dots of one block for the 32
+      // rows of the wave's matrix (N) and up to 32 pair slots (M; slots past the chunk
+      // read a valid slot and are discarded), K = the block's 32 codes. Operand lanes:
+      // row (B) or pair (A) lane % 32, codes 16 * (lane / 32) + 0..15;
       // result register i (< 4) of lane l holds pair 4 * (l / 32) + i of row l % 32. The
       // lanes' loads hold the two 16-code words of their own block, lanes 0..31 block b0
       // and lanes 32..63 block b0 + 1; one cross-half swap turns them into the B operands
@@ -1146,8 +1147,8 @@ __global__ __launch_bounds__(kDnThreads) void k_down(
       }
     };
     // Matrix-core form of the block dots (2-bit chunks of at least kDnMmaFull pairs; the
-    // lane layout of k_gateup's): per block, two v_mfma_i32_32x32x32_i8 give the exact dots of the
-    // wave's 64 rows (N: rows 0..31, then 32..63) for the pair slots (M). Every lane holds
+    // lane layout of k_gateup's): per block, two v_mfma_i32_32x32x32_i8 give the exact
+    // dots of the wave's 64 rows (N: rows 0..31, then 32..63) for the pair slots (M). Every lane holds
     // both code words of its own row; one cross-half swap makes the B operands of the two
     // row halves (word h for the lanes of half h) and another the scale/min words of rows
     // lane % 32 and 32 + lane % 32. Lane l then carries pair slots 4 * (l / 32) + i of
