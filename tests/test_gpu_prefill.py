@@ -116,6 +116,31 @@ def test_prefill_deterministic():
     assert all(np.array_equal(outs[0], o) for o in outs[1:])
 
 
+@pytest.mark.parametrize("bits", [4, 2])
+def test_prefill_stages_match_single_call(bits):
+    # moe_expert_ffn_prefill_stages with each stage in a call of its own (the benchmark's
+    # instrumented pass issues them so) reproduces moe_expert_ffn_prefill bit for bit on a
+    # shared workspace, and stays within the tolerance of the oracle; ragged shape
+    w = synth.Workload("staged", 352, 160, 33, 3, 517, bits, "zipf", seed=5)
+    host = synth.host_layer(w, 0)
+    lg, x = synth.layer_inputs(w, 0)
+    dev = workloads.layer_from_host(*host, w.k)
+    xb = synth.to_bf16_bits(x)
+    xb_d = to_dev(xb.view(np.int16))
+    routing = qmoe.route(to_dev(lg), w.k)
+    res_a = to_dev(x)
+    qmoe.ffn_prefill(dev, xb_d, routing, res_a)
+    res_b = to_dev(x)
+    ws = qmoe.workspace(dev, w.n, prefill=True, device=xb_d.device)
+    for st in (qmoe.PREFILL_PREP, qmoe.PREFILL_GATE_UP, qmoe.PREFILL_DOWN, qmoe.PREFILL_COMBINE):
+        qmoe.ffn_prefill(dev, xb_d, routing, res_b, ws=ws, stages=st)
+    torch.cuda.synchronize()
+    assert torch.equal(res_a, res_b), "staged prefill differs from the single call"
+    ids, wt = check_routing(lg, w.k, routing)
+    out_o, _ = O.ffn_prefill(*(omat(h) for h in host), w.E, xb, ids, wt, x)
+    _check(res_b.cpu().numpy(), out_o, x)
+
+
 @pytest.fixture(scope="module")
 def cfg5():
     w = synth.config(5)
