@@ -396,13 +396,17 @@ __global__ __launch_bounds__(kRtThreads) void k_router_logits(
 // ---------------------------------------------------------------- streaming block loads
 
 // One packed block (16 B at 4 bits, 8 B at 2 bits) through a buffer resource.
+// Expert weights and their scale/min words are read once per call: their loads carry the
+// non-temporal cache policy (kNt). On the T=4 window this measured 0.5-0.8 us faster in
+// the gate/up kernel and about 1 us faster a step.
+constexpr int kNt = 2;
 template <int BITS>
 struct BlockLoad;
 template <>
 struct BlockLoad<4> {
   __device__ static __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int voff, int soff,
                                               uint32_t (&w)[4]) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b128(rs, voff, soff, kNt);
     w[0] = v[0];
     w[1] = v[1];
     w[2] = v[2];
@@ -413,7 +417,7 @@ template <>
 struct BlockLoad<2> {
   __device__ static __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, int voff, int soff,
                                               uint32_t (&w)[2]) {
-    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, 0);
+    const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, voff, soff, kNt);
     w[0] = v[0];
     w[1] = v[1];
   }
@@ -793,7 +797,7 @@ __global__ __launch_bounds__((GuShape<WAVES, ROWS>::kThreads)) __attribute__((
         // per-lane offset (a lane-varying scalar offset would split every load in two)
         const int b = min(g0 + ke + S::kSplit * u, nbd - 1);
         BlockLoad<BITS>::load(rs_c, (b * f + r) * BITS * 4, 0, w[u]);
-        smw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, (b * f + r) * 4, 0, 0);
+        smw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, (b * f + r) * 4, 0, kNt);
       }
       __builtin_amdgcn_sched_barrier(0);
       wait_vmcnt<2 * S::kUnroll>();  // this wave's staging loads have landed
@@ -1143,7 +1147,7 @@ __global__ __launch_bounds__(kDnThreads) void k_down(
       for (int u = 0; u < kUnroll; ++u) {
         const int b = min(g0 + wave + kDnWaves * u, nbf - 1);  // see k_gateup
         BlockLoad<BITS>::load(rs_c, rr * BITS * 4, b * d * BITS * 4, dw[u]);
-        smw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, rr * 4, b * d * 4, 0);
+        smw[u] = __builtin_amdgcn_raw_buffer_load_b32(rs_s, rr * 4, b * d * 4, kNt);
       }
     };
     // Matrix-core form of the block dots (2-bit chunks of at least kDnMmaFull pairs; the
@@ -1479,17 +1483,19 @@ __global__ __launch_bounds__(kDtThreads) void k_down_tok(
       const int b = min(wave + 8 * u, nbf - 1);
       const size_t blk = ((size_t)(SH && e < 0 ? 0 : e) * nbf + b) * d + row;
       if (BITS == 4) {
-        const uint4 v = *reinterpret_cast<const uint4*>(cb + blk * 4);
+        typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+        const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(cb + blk * 4));
         w[i][u][0] = v.x;
         w[i][u][1] = v.y;
         w[i][u][2 % BITS] = v.z;
         w[i][u][3 % BITS] = v.w;
       } else {
-        const uint2 v = *reinterpret_cast<const uint2*>(cb + blk * 2);
+        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+        const u32x2 v = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(cb + blk * 2));
         w[i][u][0] = v.x;
         w[i][u][1] = v.y;
       }
-      smw[i][u] = sb[blk];
+      smw[i][u] = __builtin_nontemporal_load(sb + blk);  // read once: see BlockLoad
     }
   }
   __builtin_amdgcn_sched_barrier(0);
