@@ -129,3 +129,24 @@ def device_layer_matches_host(dev: qmoe.Layer, host, experts, E: int):
             sm = dm.scale_min[e * sw:(e + 1) * sw].cpu().numpy().view(np.uint16)
             assert np.array_equal(codes, hm.codes[e].reshape(-1)), f"codes of expert {e}"
             assert np.array_equal(sm, hm.scale_min[e].reshape(-1)), f"scale/min of expert {e}"
+
+
+SPIN_CYCLES = 50_000_000  # about 20 ms of the spin kernel
+
+
+def on_side_stream(srcs, call):
+    """Zero-filled copies of the device tensors `srcs`, filled on a side stream after a
+    spin; `call(*copies)` is made on that stream and its result returned once it is done."""
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        dst = [torch.zeros_like(t) for t in srcs]
+        torch.cuda._sleep(SPIN_CYCLES)
+        for a, b in zip(dst, srcs):
+            a.copy_(b)
+        out = call(*dst)
+    # every call was enqueued while the spin still ran: a stage on another stream would
+    # have found zeros, and the binding waited on nothing
+    assert not s.query(), "the side stream finished before the calls were enqueued"
+    s.synchronize()
+    return dst, out

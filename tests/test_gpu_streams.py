@@ -11,29 +11,9 @@ import torch
 
 from quantized_routed_expert_router_amd import qmoe, synth, workloads
 
-from gpu_common import to_dev
+from gpu_common import on_side_stream, to_dev
 
 pytestmark = pytest.mark.gpu
-
-SPIN_CYCLES = 50_000_000  # about 20 ms of the spin kernel
-
-
-def _on_side_stream(srcs, call):
-    """Zero-filled copies of the device tensors `srcs`, filled on a side stream after a
-    spin; `call(*copies)` is made on that stream and its result returned once it is done."""
-    torch.cuda.synchronize()
-    s = torch.cuda.Stream()
-    with torch.cuda.stream(s):
-        dst = [torch.zeros_like(t) for t in srcs]
-        torch.cuda._sleep(SPIN_CYCLES)
-        for a, b in zip(dst, srcs):
-            a.copy_(b)
-        out = call(*dst)
-    # every call was enqueued while the spin still ran: a stage on another stream would
-    # have found zeros, and the binding waited on nothing
-    assert not s.query(), "the side stream finished before the calls were enqueued"
-    s.synchronize()
-    return dst, out
 
 
 def _same_routing(a: qmoe.Routing, b: qmoe.Routing, pairs: int):
@@ -53,7 +33,7 @@ def _layer_decode_case(layer, lg, x, k):
     def call(xs, res, lgs=None):
         return qmoe.layer_decode(layer, lgs, xs, res)
 
-    (xs, res, *_), r = _on_side_stream(srcs, call)
+    (xs, res, *_), r = on_side_stream(srcs, call)
     assert torch.equal(res, res_ref), "residual differs from the default-stream call"
     _same_routing(r, r_ref, x.shape[0] * k)
 
@@ -98,7 +78,7 @@ def test_route_then_ffn_decode_on_caller_stream():
         qmoe.ffn_decode(layer, xs, r, res)
         return r
 
-    (_, _, res), r = _on_side_stream([lg_d, x_d, x_d], call)
+    (_, _, res), r = on_side_stream([lg_d, x_d, x_d], call)
     assert torch.equal(res, res_ref)
     _same_routing(r, r_ref, w.n * w.k)
 
@@ -120,6 +100,6 @@ def test_prefill_on_caller_stream(bits):
         qmoe.ffn_prefill(layer, xbs, r, res)
         return r
 
-    (_, _, res), r = _on_side_stream([lg_d, xb, x_d], call)
+    (_, _, res), r = on_side_stream([lg_d, xb, x_d], call)
     assert torch.equal(res, res_ref)
     _same_routing(r, r_ref, w.n * w.k)

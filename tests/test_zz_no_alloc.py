@@ -12,7 +12,7 @@ import torch
 from oracle import oracle as O
 from quantized_routed_expert_router_amd import qmoe, synth, workloads
 
-from gpu_common import assert_output_tolerance, check_routing, omat, to_dev
+from gpu_common import assert_output_tolerance, check_routing, omat, on_side_stream, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -74,3 +74,24 @@ def test_noalloc_rejects_windows_beyond_its_workspace():
     assert ei.value.status == 3  # MOE_ERR_WORKSPACE_TOO_SMALL, nothing enqueued
     torch.cuda.synchronize()
     assert bool((res == 3.0).all())
+
+
+def test_noalloc_on_caller_stream():
+    # the library's own workspace serves a call on a side stream whose inputs arrive behind
+    # a spin: every stage on that stream, the result equal to moe_layer_decode's
+    w = synth.config(2)
+    layer = workloads.device_layer(w, 1)
+    lg, x = synth.layer_inputs(w, 5)
+    res_a = to_dev(x)
+    r_a = qmoe.layer_decode(layer, to_dev(lg), to_dev(x), res_a)
+    torch.cuda.synchronize()
+
+    def call(lgs, xs, res):
+        r = qmoe.Routing.empty(w.n, w.E, w.k)
+        qmoe.layer_decode_noalloc(layer, lgs, xs, res, r)
+        return r
+
+    (_, _, res_b), r_b = on_side_stream([to_dev(lg), to_dev(x), to_dev(x)], call)
+    assert torch.equal(res_a, res_b)
+    for name in ("topk_ids", "topk_w", "expert_offsets"):
+        assert torch.equal(getattr(r_a, name), getattr(r_b, name)), name
