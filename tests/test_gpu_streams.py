@@ -11,7 +11,7 @@ import torch
 
 from quantized_routed_expert_router_amd import qmoe, synth, workloads
 
-from gpu_common import on_side_stream, to_dev
+from gpu_common import SPIN_CYCLES, on_side_stream, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -103,3 +103,49 @@ def test_prefill_on_caller_stream(bits):
     (_, _, res), r = on_side_stream([lg_d, xb, x_d], call)
     assert torch.equal(res, res_ref)
     _same_routing(r, r_ref, w.n * w.k)
+
+
+def test_two_streams_at_once():
+    # a T=4 decode layer and a prefill chunk, each on its own stream behind a spin of the
+    # same length, so their kernels run at the same time; each call has its own
+    # workspace, and the results equal the same calls made one after the other
+    wd = synth.config(2)
+    dlayer = workloads.device_layer(wd, 2)
+    dlg, dx = synth.layer_inputs(wd, 2)
+    wp = synth.Workload("streams", 2048, 768, 16, 4, 517, 4, "zipf", seed=81)
+    player = workloads.layer_from_host(*synth.host_layer(wp, 0), wp.k)
+    plg, px = synth.layer_inputs(wp, 0)
+    pxb = to_dev(synth.to_bf16_bits(px).view(np.int16))
+    dsrc = [to_dev(dlg), to_dev(dx), to_dev(dx)]
+    psrc = [to_dev(plg), pxb, to_dev(px)]
+
+    def dcall(lgs, xs, res):
+        return qmoe.layer_decode(dlayer, lgs, xs, res)
+
+    def pcall(lgs, xbs, res):
+        r = qmoe.route(lgs, wp.k)
+        qmoe.ffn_prefill(player, xbs, r, res)
+        return r
+
+    ref_d = [t.clone() for t in dsrc]
+    rd_ref = dcall(*ref_d)
+    ref_p = [t.clone() for t in psrc]
+    rp_ref = pcall(*ref_p)
+    torch.cuda.synchronize()
+    streams = (torch.cuda.Stream(), torch.cuda.Stream())
+    outs = []
+    for s, src, call in zip(streams, (dsrc, psrc), (dcall, pcall)):
+        with torch.cuda.stream(s):
+            dst = [torch.zeros_like(t) for t in src]
+            torch.cuda._sleep(SPIN_CYCLES)
+            for a, b in zip(dst, src):
+                a.copy_(b)
+            outs.append((dst, call(*dst)))
+    assert not any(s.query() for s in streams)
+    for s in streams:
+        s.synchronize()
+    (dd, rd), (pd, rp) = outs
+    assert torch.equal(dd[2], ref_d[2]), "decode residual"
+    assert torch.equal(pd[2], ref_p[2]), "prefill residual"
+    _same_routing(rd, rd_ref, wd.n * wd.k)
+    _same_routing(rp, rp_ref, wp.n * wp.k)
