@@ -95,3 +95,45 @@ def test_noalloc_on_caller_stream():
     assert torch.equal(res_a, res_b)
     for name in ("topk_ids", "topk_w", "expert_offsets"):
         assert torch.equal(getattr(r_a, name), getattr(r_b, name)), name
+
+
+def test_noalloc_graph_replays_between_eager_calls():
+    # the call captured in a HIP graph and replayed three times; before each replay an
+    # eager call on a 40-token window leaves its own contents in the shared array, so every
+    # replay also shows that a call sets up whatever it needs cleared
+    w = synth.config(2)
+    layer = workloads.device_layer(w, 0)
+    lg, x = synth.layer_inputs(w, 9)
+    lg_d, x_d = to_dev(lg), to_dev(x)
+    res_e = x_d.clone()
+    r_e = qmoe.layer_decode(layer, lg_d, x_d, res_e)
+    wo = synth.Workload(w.name, w.d, w.f, w.E, w.k, 40, w.bits, w.logits)
+    lg_o, x_o = (to_dev(a) for a in synth.layer_inputs(wo, 4))
+    r_o = qmoe.Routing.empty(wo.n, w.E, w.k)
+
+    def other_window():
+        res_o = x_o.clone()
+        qmoe.layer_decode_noalloc(layer, lg_o, x_o, res_o, r_o)
+        return res_o
+
+    other_ref = other_window()  # also resolves the array's address before the capture
+    res_g = x_d.clone()
+    r_g = qmoe.Routing.empty(w.n, w.E, w.k)
+    torch.cuda.synchronize()
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        qmoe.layer_decode_noalloc(layer, lg_d, x_d, res_g, r_g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        assert torch.equal(other_window(), other_ref), f"eager call before replay {rep}"
+        res_g.copy_(x_d)
+        r_g.topk_ids.fill_(-1)
+        r_g.expert_offsets.fill_(-1)
+        r_g.pair_index.fill_(-1)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(res_g, res_e), f"replay {rep}: residual"
+        for name in ("topk_ids", "topk_w", "expert_offsets"):
+            assert torch.equal(getattr(r_g, name), getattr(r_e, name)), f"replay {rep}: {name}"
+        assert torch.equal(r_g.pair_index[: w.n * w.k], r_e.pair_index[: w.n * w.k])
