@@ -1,4 +1,5 @@
-"""A decode chain captured as a HIP graph replays exactly like the eager launches.
+"""A decode chain, and a prefill chunk, captured as a HIP graph replay exactly like the
+eager launches.
 
 Several layers of the routed-expert layer (moe_layer_decode, residual chained: x aliases
 the residual) are captured once into a graph. The graph is then replayed several times,
@@ -124,3 +125,46 @@ def test_graph_replay_matches_oracle_chain(shape):
             check_routing(lg, w.k, r)
         assert_output_tolerance(out, chain, what=f"replay {rep} residual")
         assert_output_tolerance(out - x0, chain - x0, what=f"replay {rep} moe delta")
+
+
+@pytest.mark.parametrize("n,bits", [(517, 4), (5000, 2)])
+def test_prefill_graph_replays_match_eager(n, bits):
+    # routing and a prefill chunk captured once (5000 tokens: 30,000 pairs, past the
+    # single-workgroup grouping, so the counting and scatter launches with their
+    # workspace), replayed three times with eager work between; each replay equals the
+    # eager calls bit for bit
+    w = synth.Workload("small", 512, 256, 64, 6, n, bits, "zipf", seed=12)
+    layer = workloads.layer_from_host(*synth.host_layer(w, 0), w.k)
+    lg, x = synth.layer_inputs(w, 0)
+    lg_d, x_d = to_dev(lg), to_dev(x)
+    xb = to_dev(synth.to_bf16_bits(x).view(np.int16))
+    rws = qmoe.route_workspace(n, w.E, w.k, lg_d.device)
+    pws = qmoe.workspace(layer, n, prefill=True)
+
+    def run(res, r):
+        qmoe.route(lg_d, w.k, out=r, ws=rws)
+        qmoe.ffn_prefill(layer, xb, r, res, ws=pws)
+
+    res_e = x_d.clone()
+    r_e = qmoe.Routing.empty(n, w.E, w.k)
+    run(res_e, r_e)
+    torch.cuda.synchronize()
+    res_g = x_d.clone()
+    r_g = qmoe.Routing.empty(n, w.E, w.k)
+    stream = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=stream):
+        run(res_g, r_g)
+    torch.cuda.synchronize()
+    for rep in range(3):
+        res_g.copy_(x_d)
+        r_g.topk_ids.fill_(-1)
+        r_g.expert_offsets.fill_(-1)
+        r_g.pair_index.fill_(-1)
+        scratch = torch.randn(1 << 16, device="cuda")  # eager work between replays
+        (scratch * 2).sum().item()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(res_g, res_e), f"replay {rep}: residual differs"
+        for name in ("topk_ids", "topk_w", "expert_offsets", "pair_index"):
+            assert torch.equal(getattr(r_g, name), getattr(r_e, name)), f"replay {rep}: {name}"
